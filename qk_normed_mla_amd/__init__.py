@@ -1,0 +1,237 @@
+"""Python binding of libqknmla.so (QK-Normed MLA absorbed-latent decode on MI355X).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels of
+the shared library.  Tensors supply device pointers; the current torch stream
+supplies the HIP stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+The functions carry the names of the C entry points (include/qkn_mla.h):
+
+    qkn_mla_absorb_query, qkn_mla_append, qkn_mla_decode, qkn_mla_combine
+
+and check on the host that every tensor is a contiguous device tensor of the
+dtype and element count the kernels and their grids assume before launching.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqknmla.so")
+
+QKN_OK = 0
+QKN_F32 = 0
+QKN_BF16 = 1
+QKN_DECODE_NO_ALPHA = 1
+QKN_DECODE_FORCE_GENERIC = 2
+PAGE_SIZE = 64
+
+_c_int32 = ctypes.c_int32
+_c_float = ctypes.c_float
+
+
+class Dims(ctypes.Structure):
+    """qkn_mla_dims."""
+    _fields_ = [
+        ("batch", _c_int32), ("s_q", _c_int32), ("heads", _c_int32), ("groups", _c_int32),
+        ("rank", _c_int32), ("head_dim", _c_int32), ("rope_dim", _c_int32),
+        ("page_size", _c_int32), ("max_pages_per_seq", _c_int32), ("num_pages", _c_int32),
+        ("eps", _c_float), ("softmax_scale", _c_float), ("rope_theta", _c_float),
+        ("cache_dtype", _c_int32),
+    ]
+
+    def __repr__(self):
+        return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class QknError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libqknmla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m qk_normed_mla_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        D = ctypes.POINTER(Dims)
+        lib.qkn_mla_abi_version.restype = ctypes.c_int
+        lib.qkn_mla_abi_version.argtypes = []
+        lib.qkn_status_string.restype = ctypes.c_char_p
+        lib.qkn_status_string.argtypes = [ctypes.c_int]
+        lib.qkn_mla_check_dims.restype = ctypes.c_int
+        lib.qkn_mla_check_dims.argtypes = [D]
+        lib.qkn_mla_decode_kernel_kind.restype = ctypes.c_int
+        lib.qkn_mla_decode_kernel_kind.argtypes = [D, _c_int32, ctypes.c_uint32]
+        lib.qkn_mla_absorb_query.restype = ctypes.c_int
+        lib.qkn_mla_absorb_query.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
+        lib.qkn_mla_append.restype = ctypes.c_int
+        lib.qkn_mla_append.argtypes = [D, _c_int32, P, P, P, P, P, P, P, P, P, P, P]
+        lib.qkn_mla_decode.restype = ctypes.c_int
+        lib.qkn_mla_decode.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
+                                       P, P, P, P]
+        lib.qkn_mla_combine.restype = ctypes.c_int
+        lib.qkn_mla_combine.argtypes = [D, _c_int32, P, P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+EXPORTED_SYMBOLS = (
+    "qkn_mla_abi_version", "qkn_status_string", "qkn_mla_check_dims",
+    "qkn_mla_decode_kernel_kind", "qkn_mla_absorb_query", "qkn_mla_append",
+    "qkn_mla_decode", "qkn_mla_combine",
+)
+
+
+def status_string(status: int) -> str:
+    return library().qkn_status_string(int(status)).decode()
+
+
+def make_dims(*, batch, s_q, heads, groups, rank, head_dim, rope_dim, max_pages_per_seq,
+              num_pages, eps, softmax_scale, rope_theta, cache_dtype) -> Dims:
+    dt = {"f32": QKN_F32, "bf16": QKN_BF16}.get(cache_dtype, cache_dtype)
+    return Dims(batch, s_q, heads, groups, rank, head_dim, rope_dim, PAGE_SIZE,
+                max_pages_per_seq, num_pages, eps, softmax_scale, rope_theta, dt)
+
+
+def dims_for(wl, num_pages: int) -> Dims:
+    """Dims of a workloads.Workload with a pool of ``num_pages`` pages."""
+    return make_dims(batch=wl.batch, s_q=wl.s_q, heads=wl.heads, groups=wl.groups,
+                     rank=wl.rank, head_dim=wl.head_dim, rope_dim=wl.rope_dim,
+                     max_pages_per_seq=wl.max_pages_per_seq, num_pages=num_pages, eps=wl.eps,
+                     softmax_scale=wl.softmax_scale, rope_theta=wl.rope_theta,
+                     cache_dtype=wl.cache_dtype)
+
+
+def cache_torch_dtype(dims: Dims) -> torch.dtype:
+    return torch.bfloat16 if dims.cache_dtype == QKN_BF16 else torch.float32
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: int, allow_none=False):
+    if t is None:
+        if allow_none or numel == 0:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()} {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, status: int):
+    if status != QKN_OK:
+        raise QknError(fn, status)
+
+
+def decode_kernel_kind(dims: Dims, num_splits: int, flags: int = 0) -> int:
+    return library().qkn_mla_decode_kernel_kind(ctypes.byref(dims), int(num_splits), int(flags))
+
+
+def qkn_mla_absorb_query(dims: Dims, q, q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr,
+                         q_tilde, alpha_q, q_rope_normed, stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    st = library().qkn_mla_absorb_query(
+        ctypes.byref(d),
+        _ptr(q, "q", f32, rows * d.head_dim),
+        _ptr(q_rope, "q_rope", f32, rows * d.rope_dim),
+        _ptr(q_pos, "q_pos", i32, d.batch * d.s_q),
+        _ptr(w_k, "w_k", f32, d.groups * d.rank * d.head_dim),
+        _ptr(gamma_q, "gamma_q", f32, d.head_dim),
+        _ptr(gamma_k, "gamma_k", f32, d.groups * d.head_dim),
+        _ptr(gamma_qr, "gamma_qr", f32, d.rope_dim),
+        _ptr(q_tilde, "q_tilde", ct, rows * d.rank),
+        _ptr(alpha_q, "alpha_q", f32, rows),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_absorb_query", st)
+
+
+def qkn_mla_append(dims: Dims, c_new, k_rope_new, seq_idx, pos, block_table, w_k, gamma_kr,
+                   kv_cache, alpha_k_cache, err_flag=None, stream=None):
+    d = dims
+    n = int(seq_idx.numel()) if seq_idx is not None else 0
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    st = library().qkn_mla_append(
+        ctypes.byref(d), n,
+        _ptr(c_new, "c_new", f32, n * d.rank),
+        _ptr(k_rope_new, "k_rope_new", f32, n * d.rope_dim),
+        _ptr(seq_idx, "seq_idx", i32, n),
+        _ptr(pos, "pos", i32, n),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(w_k, "w_k", f32, d.groups * d.rank * d.head_dim),
+        _ptr(gamma_kr, "gamma_kr", f32, d.rope_dim),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(alpha_k_cache, "alpha_k_cache", f32, d.num_pages * PAGE_SIZE * d.groups),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_append", st)
+
+
+def qkn_mla_decode(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,
+                   block_table, seq_lens, num_splits: int, flags: int, o_partial, lse_partial,
+                   err_flag=None, stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    P = int(num_splits)
+    st = library().qkn_mla_decode(
+        ctypes.byref(d),
+        _ptr(q_tilde, "q_tilde", ct, rows * d.rank),
+        _ptr(alpha_q, "alpha_q", f32, rows),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(alpha_k_cache, "alpha_k_cache", f32, d.num_pages * PAGE_SIZE * d.groups),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", i32, d.batch),
+        P, int(flags),
+        _ptr(o_partial, "o_partial", f32, rows * P * d.rank),
+        _ptr(lse_partial, "lse_partial", f32, rows * P),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_decode", st)
+
+
+def qkn_mla_combine(dims: Dims, num_splits: int, o_partial, lse_partial, o_latent, lse,
+                    stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    f32 = torch.float32
+    P = int(num_splits)
+    st = library().qkn_mla_combine(
+        ctypes.byref(d), P,
+        _ptr(o_partial, "o_partial", f32, rows * P * d.rank),
+        _ptr(lse_partial, "lse_partial", f32, rows * P),
+        _ptr(o_latent, "o_latent", f32, rows * d.rank),
+        _ptr(lse, "lse", f32, rows),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_combine", st)

@@ -1,0 +1,62 @@
+"""Shared pieces of the GPU parity tests (inputs, uploads, comparisons)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import qk_normed_mla_amd as Q
+from qk_normed_mla_amd.runner import DecodeRunner
+
+# Tolerances.  Floating point: row-normwise max relative error
+# max |gpu - ref| / max |ref| over each latent row (b, i, h), and absolute error
+# on lse.  Float32 cache: 1e-4; bf16 cache with float32 accumulation: 1e-2
+# end to end (from the float32 inputs against the float64 explicit path).  The
+# decode kernel alone, run on the oracle's own stored state, is held to 3e-3
+# (bf16 probabilities feed the matrix cores) or 1e-5 (float32 vector path).
+TOL_E2E = {"f32": 1e-4, "bf16": 1e-2}
+TOL_KERNEL = {"f32": 1e-5, "bf16": 3e-3}
+TOL_KERNEL_GENERIC = 1e-5
+
+
+def announce(msg: str):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    Q.library()  # raises when the HIP library is missing
+
+
+def row_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.max(np.abs(got - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return float(np.max(num / den))
+
+
+def ulp_distance_bf16(a_words, b_words):
+    """Distance in representable bf16 steps between two arrays of words."""
+    def ordered(w):
+        w = np.asarray(w, dtype=np.uint16).astype(np.int32)
+        return np.where(w & 0x8000, -(w & 0x7FFF), w)
+    return np.abs(ordered(a_words) - ordered(b_words))
+
+
+def upload_words(words, like: torch.Tensor) -> torch.Tensor:
+    """Host storage words -> a device tensor of ``like``'s dtype and shape."""
+    if like.dtype == torch.bfloat16:
+        t = torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).to(like.device)
+        return t.view(torch.bfloat16).reshape(like.shape)
+    return torch.from_numpy(np.ascontiguousarray(words, dtype=np.float32)).to(like.device).reshape(like.shape)
+
+
+def run_e2e(wl, inp, num_splits=None, flags=0, kv_fill_word=None):
+    r = DecodeRunner(wl, inp, num_splits=num_splits, kv_fill_word=kv_fill_word)
+    r.fill_history()
+    r.step(flags)
+    torch.cuda.synchronize()
+    return r

@@ -1,0 +1,340 @@
+"""GPU parity: every library call against the CPU oracle, element by element.
+
+Sizes keep the float64 oracle to seconds while spanning several 64-token tiles
+and a ragged tail.  Every GPU step is announced (case name, seed, shape) on
+stdout before it runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins as P
+import qk_normed_mla_amd as Q
+import workloads as W
+from gpu_helpers import (TOL_E2E, TOL_KERNEL, TOL_KERNEL_GENERIC, announce, require_gpu,
+                         row_err, ulp_distance_bf16, upload_words, run_e2e)
+from oracle import qkn_oracle as O
+from qk_normed_mla_amd.runner import DecodeRunner
+
+pytestmark = pytest.mark.gpu
+NAMES = ["tiny", "dsv3", "grouped", "long", "mtp"]
+SENTINEL_BF16 = 0x7FC1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _oracle_decode_all(wl, inp, qi, img, num_splits, use_alpha=True):
+    return O.decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                             inp["seq_lens"], num_splits, use_alpha=use_alpha)
+
+
+# ---------------------------------------------------------------------------
+# append: the cache image
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", NAMES)
+def test_append_cache_image(name):
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=21, extra_pages=2)
+    announce(f"append {name} B={wl.batch} T={list(inp['seq_lens'])[:4]} pages={inp['num_pages']}")
+    fill = SENTINEL_BF16 if wl.cache_dtype == "bf16" else float("nan")
+    r = DecodeRunner(wl, inp, kv_fill_word=fill)
+    r.fill_history()
+    r.append_new()
+    torch.cuda.synchronize()
+    assert int(r.err_flag.item()) == 0
+    got = r.kv_words()
+    ak = r.alpha_k.cpu().numpy()
+    kv0, ak0 = O.empty_images(wl, inp["num_pages"])
+    img = O.full_cache_image(wl, inp, kv0, ak0)
+    rk = wl.rank
+    written = np.zeros(got.shape[:2], bool)
+    bt = inp["block_table"]
+    for b, T in enumerate(inp["seq_lens"]):
+        t = np.arange(int(T))
+        written[bt[b, t // 64], t % 64] = True
+    # latent and slot indexing: bit-exact; untouched slots keep the sentinel
+    if wl.cache_dtype == "bf16":
+        assert np.array_equal(got[..., :rk], img["kv"][..., :rk])
+        assert np.all(got[~written] == SENTINEL_BF16)
+        d = ulp_distance_bf16(got[written][:, rk:], img["kv"][written][:, rk:])
+        assert d.max() <= 1, f"RoPE key off by {d.max()} bf16 steps"
+    else:
+        assert np.array_equal(got[..., :rk][written], img["kv"][..., :rk][written])
+        assert np.all(np.isnan(got[~written]))
+        assert np.allclose(got[written][:, rk:], img["kv"][written][:, rk:], rtol=1e-5, atol=1e-6)
+    assert np.all(np.isnan(ak[~written]))
+    rel = np.abs(ak[written] / img["alpha_k"][written] - 1.0)
+    assert rel.max() < 1e-5, rel.max()
+
+
+def test_append_rejects_bad_slots():
+    """Out-of-range sequence, position or page entries are skipped and flagged."""
+    wl = P.small("dsv3", batch=2, seq_len=130)
+    inp = W.make_inputs(wl, seed=22)
+    inp["block_table"] = inp["block_table"].copy()
+    inp["block_table"][1, 1] = -1            # page entry out of range
+    announce("append bad slots dsv3")
+    r = DecodeRunner(wl, inp, kv_fill_word=SENTINEL_BF16)
+    before = r.kv_words().copy()
+    # tokens: one valid, one in the bad page, one past max pages, one bad sequence
+    seq = torch.tensor([0, 1, 0, 5], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([3, 70, 64 * wl.max_pages_per_seq + 1, 0], dtype=torch.int32, device="cuda")
+    c = torch.randn(4, wl.rank, device="cuda")
+    kr = torch.randn(4, wl.rope_dim, device="cuda")
+    r.err_flag.zero_()
+    Q.qkn_mla_append(r.dims, c, kr, seq, pos, r.block_table, r.w_k, r.gamma_kr, r.kv, r.alpha_k,
+                     r.err_flag)
+    torch.cuda.synchronize()
+    assert int(r.err_flag.item()) == 1
+    after = r.kv_words()
+    changed = np.any(after != before, axis=-1)
+    pg = inp["block_table"][0, 0]
+    assert changed[pg, 3] and changed.sum() == 1
+
+
+# ---------------------------------------------------------------------------
+# absorb_query
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", NAMES)
+def test_absorb_query(name):
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=23)
+    announce(f"absorb {name}")
+    r = DecodeRunner(wl, inp)
+    r.absorb()
+    torch.cuda.synchronize()
+    ref = O.query_image(wl, inp)
+    aq = r.alpha_q.cpu().numpy()
+    assert np.max(np.abs(aq / ref["alpha_q"] - 1)) < 1e-5
+    qt, qr = r.words(r.q_tilde), r.words(r.q_rope_normed)
+    if wl.cache_dtype == "bf16":
+        # q~ is a dot product of length d that can cancel, so a per-element ulp
+        # bound is wrong near zero: hold each row to half a bf16 step of its
+        # largest entry (the storage rounding, 2^-8 relative) against the exact
+        # float64 value, and require almost every word to be bit-equal.
+        exact = O.absorb_query(wl, inp["q"], inp["q_rope"], inp["w_k"], inp["gamma_q"],
+                               inp["gamma_k"], inp["gamma_qr"], r.q_pos.cpu().numpy())
+        got = O.bf16_bits_to_f32(qt).astype(np.float64)
+        assert row_err(got, exact["q_tilde"]) <= 2.0 ** -8 * 1.01
+        assert np.mean(qt == ref["q_tilde"]) > 0.99
+        d = ulp_distance_bf16(qr, ref["qr_hat"])
+        assert d.max() <= 1
+    else:
+        assert row_err(qt, ref["q_tilde"]) < 1e-5
+        assert row_err(qr, ref["qr_hat"]) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# decode + combine on the oracle's own stored state
+# ---------------------------------------------------------------------------
+
+def _decode_on_image(wl, inp, num_splits, flags=0):
+    img = O.full_cache_image(wl, inp)
+    qi = O.query_image(wl, inp)
+    r = DecodeRunner(wl, inp, num_splits=num_splits)
+    r.kv.copy_(upload_words(img["kv"], r.kv))
+    r.alpha_k.copy_(torch.from_numpy(img["alpha_k"]).to("cuda"))
+    r.q_tilde.copy_(upload_words(qi["q_tilde"], r.q_tilde))
+    r.alpha_q.copy_(torch.from_numpy(qi["alpha_q"]).to("cuda"))
+    r.q_rope_normed.copy_(upload_words(qi["qr_hat"], r.q_rope_normed))
+    r.decode(flags)
+    r.combine()
+    torch.cuda.synchronize()
+    ref = _oracle_decode_all(wl, inp, qi, img, num_splits,
+                             use_alpha=not (flags & Q.QKN_DECODE_NO_ALPHA))
+    return r, ref
+
+
+def _compare_decode(wl, r, ref, tol):
+    o_part = r.o_partial.cpu().numpy()
+    lse_part = r.lse_partial.cpu().numpy()
+    o_lat = r.o_latent.cpu().numpy()
+    lse = r.lse.cpu().numpy()
+    worst = 0.0
+    for (b, i, h), v in ref.items():
+        empty = np.isneginf(v["lse_part"])
+        assert np.all(np.isneginf(lse_part[b, i, h][empty]))
+        assert not np.any(o_part[b, i, h][empty])
+        if np.any(~empty):
+            worst = max(worst, row_err(o_part[b, i, h][~empty], v["o_part"][~empty]))
+            assert np.max(np.abs(lse_part[b, i, h][~empty] - v["lse_part"][~empty])) < 10 * tol
+        worst = max(worst, row_err(o_lat[b, i, h], v["o_lat"]))
+        assert abs(lse[b, i, h] - v["lse"]) < 10 * tol
+    assert worst <= tol, worst
+    return worst
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_decode_on_oracle_state(name):
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=24)
+    kind = Q.decode_kernel_kind(Q.dims_for(wl, inp["num_pages"]), wl.num_splits)
+    announce(f"decode {name} kind={kind} splits={wl.num_splits}")
+    r, ref = _decode_on_image(wl, inp, wl.num_splits)
+    tol = TOL_KERNEL[wl.cache_dtype] if kind == 1 else TOL_KERNEL_GENERIC
+    print(f"  row err {_compare_decode(wl, r, ref, tol):.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "grouped", "mtp"])
+def test_decode_generic_kernel(name):
+    """The vector-ALU kernel on the bf16 shapes (an independent GPU path)."""
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=25)
+    announce(f"decode generic {name}")
+    r, ref = _decode_on_image(wl, inp, 3, flags=Q.QKN_DECODE_FORCE_GENERIC)
+    _compare_decode(wl, r, ref, TOL_KERNEL_GENERIC)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "grouped"])
+def test_decode_without_alpha(name):
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=26)
+    kind = Q.decode_kernel_kind(Q.dims_for(wl, inp["num_pages"]), 2)
+    announce(f"decode no-alpha {name} kind={kind}")
+    r, ref = _decode_on_image(wl, inp, 2, flags=Q.QKN_DECODE_NO_ALPHA)
+    tol = TOL_KERNEL[wl.cache_dtype] if kind == 1 else TOL_KERNEL_GENERIC
+    _compare_decode(wl, r, ref, tol)
+
+
+# ---------------------------------------------------------------------------
+# end to end: float32 inputs through all four calls vs the explicit float64 path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", NAMES)
+def test_end_to_end(name):
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=27)
+    announce(f"e2e {name} splits={wl.num_splits}")
+    r = run_e2e(wl, inp)
+    assert int(r.err_flag.item()) == 0
+    o_lat = r.o_latent.cpu().numpy()
+    lse = r.lse.cpu().numpy()
+    tol = TOL_E2E[wl.cache_dtype]
+    worst = 0.0
+    for b in range(wl.batch):
+        for i in range(wl.s_q):
+            e = O.explicit_rows(wl, inp, b, i)
+            worst = max(worst, row_err(o_lat[b, i], e["o_lat"]))
+            assert np.max(np.abs(lse[b, i] - e["lse"])) < tol
+            # the caller's value up-projection of the GPU latent output
+            o = O.value_up_projection(wl, o_lat[b, i], inp["w_v"], np.arange(wl.heads))
+            assert row_err(o, e["o"]) < 2 * tol
+    print(f"  e2e row err {worst:.2e}", flush=True)
+    assert worst <= tol
+
+
+# ---------------------------------------------------------------------------
+# invariants and edge cases
+# ---------------------------------------------------------------------------
+
+def test_split_invariance_and_empty_splits():
+    wl = P.small("long", seq_len=700)   # 11 pages
+    inp = W.make_inputs(wl, seed=28)
+    outs = {}
+    for splits in (1, 3, 11, 40):       # 40 leaves empty partitions
+        announce(f"split invariance P={splits}")
+        r = run_e2e(wl, inp, num_splits=splits)
+        outs[splits] = (r.o_latent.cpu().numpy(), r.lse.cpu().numpy())
+        if splits == 40:
+            lp = r.lse_partial.cpu().numpy()
+            assert np.all(np.isneginf(lp[..., 11:]))
+    for splits in (3, 11, 40):
+        assert row_err(outs[splits][0][0, 0], outs[1][0][0, 0]) < 1e-5
+        assert np.max(np.abs(outs[splits][1] - outs[1][1])) < 1e-5
+
+
+def test_page_permutation_bitwise():
+    wl = P.small("mtp", batch=3)
+    inp = W.make_inputs(wl, seed=29)
+    inp2 = W.permute_pages(inp, seed=30)
+    announce("page permutation")
+    a = run_e2e(wl, inp)
+    b = run_e2e(wl, inp2)
+    assert torch.equal(a.o_latent, b.o_latent) and torch.equal(a.lse, b.lse)
+
+
+def test_deterministic():
+    wl = P.small("grouped")
+    inp = W.make_inputs(wl, seed=31)
+    announce("determinism")
+    r = run_e2e(wl, inp)
+    first = r.o_latent.clone()
+    for _ in range(3):
+        r.step()
+    torch.cuda.synchronize()
+    assert torch.equal(first, r.o_latent)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "mtp"])
+def test_rows_sum_to_one(name):
+    """Latent dimension 0 set to 1.0 (exact in bf16): o_latent[..., 0] = sum_t p_t = 1."""
+    wl = P.small(name)
+    inp = W.make_inputs(wl, seed=32)
+    inp["c"][:, 0] = 1.0
+    announce(f"rows sum to one {name}")
+    r = run_e2e(wl, inp)
+    o0 = r.o_latent[..., 0].cpu().numpy()
+    assert np.max(np.abs(o0 - 1.0)) < 1e-5, np.max(np.abs(o0 - 1.0))
+
+
+def test_single_token_and_minimal_lengths():
+    """T_b = s_q (each query sees a prefix of the new tokens) and T_b = 1."""
+    wl = W.WORKLOADS["mtp"].replace(batch=3, seq_len=64, seq_len_range=(4, 6))
+    inp = W.make_inputs(wl, seed=33)
+    inp["seq_lens"] = inp["seq_lens"].copy()
+    announce(f"minimal lengths {list(inp['seq_lens'])}")
+    r = run_e2e(wl, inp)
+    o_lat = r.o_latent.cpu().numpy()
+    for b in range(wl.batch):
+        for i in range(wl.s_q):
+            e = O.explicit_rows(wl, inp, b, i)
+            assert row_err(o_lat[b, i], e["o_lat"]) < TOL_E2E["bf16"]
+    wl1 = P.small("dsv3", batch=1, seq_len=1)
+    inp1 = W.make_inputs(wl1, seed=34)
+    announce("T = 1")
+    r1 = run_e2e(wl1, inp1)
+    c0 = O.stored_value(inp1["c"][0], "bf16")
+    assert np.array_equal(r1.o_latent[0, 0].cpu().numpy(), np.broadcast_to(c0, (wl1.heads, wl1.rank)))
+
+
+def test_zero_vectors_stay_finite():
+    """c_t = 0 gives alpha^k = 1/sqrt(eps) and a zero content logit; q = 0 likewise."""
+    wl = P.small("dsv3", batch=1, seq_len=100)
+    inp = W.make_inputs(wl, seed=35)
+    inp["c"][10:20] = 0.0
+    inp["q"][0, 0, :5] = 0.0
+    announce("zero vectors")
+    r = run_e2e(wl, inp)
+    o_lat = r.o_latent.cpu().numpy()
+    assert np.all(np.isfinite(o_lat))
+    e = O.explicit_rows(wl, inp, 0, 0)
+    assert row_err(o_lat[0, 0], e["o_lat"]) < TOL_E2E["bf16"]
+    ak = r.alpha_k.cpu().numpy()
+    pg = inp["block_table"][0, 0]
+    assert np.allclose(ak[pg, 10:20, 0], 1.0 / np.sqrt(np.float32(wl.eps)), rtol=1e-6)
+
+
+def test_decode_flags_bad_lengths():
+    """A sequence length past the block table is clamped and flagged; a page
+    entry out of range skips its tokens and is flagged."""
+    wl = P.small("dsv3", batch=2, seq_len=128)
+    inp = W.make_inputs(wl, seed=36)
+    announce("decode bad lengths")
+    r = run_e2e(wl, inp)
+    r.err_flag.zero_()
+    r.seq_lens[1] = 64 * wl.max_pages_per_seq + 5
+    r.decode()
+    torch.cuda.synchronize()
+    assert int(r.err_flag.item()) == 1
+    assert np.all(np.isfinite(r.o_partial.cpu().numpy()[1][r.lse_partial.cpu().numpy()[1] > -np.inf]))
+    r.seq_lens.copy_(torch.from_numpy(inp["seq_lens"]).cuda())
+    r.err_flag.zero_()
+    r.block_table[0, 1] = inp["num_pages"] + 7
+    r.decode()
+    torch.cuda.synchronize()
+    assert int(r.err_flag.item()) == 1
