@@ -12,12 +12,24 @@ from qk_normed_mla_amd.runner import DecodeRunner
 # Tolerances.  Floating point: row-normwise max relative error
 # max |gpu - ref| / max |ref| over each latent row (b, i, h), and absolute error
 # on lse.  Float32 cache: 1e-4; bf16 cache with float32 accumulation: 1e-2
-# end to end (from the float32 inputs against the float64 explicit path).  The
-# decode kernel alone, run on the oracle's own stored state, is held to 3e-3
-# (bf16 probabilities feed the matrix cores) or 1e-5 (float32 vector path).
+# end to end (from the float32 inputs against the float64 explicit path).
+#
+# The decode kernel alone, run on the oracle's own stored state:
+#  * vector-ALU kernel (float32 throughout): 1e-5 row-relative.
+#  * matrix-core kernel: each probability enters the P.C product rounded to
+#    bf16, p~_t = p_t (1 + e_t) with |e_t| <= 2^-9, and the row is normalised by
+#    the sum of the same rounded values, so o = sum_t w_t c_t stays a convex
+#    combination whose weights moved by w_t (e_t - e_mean) / (1 + e_mean), i.e.
+#    by at most ~2^-8 relative.  Hence |delta o_m| <= 2^-8 sum_t w_t |c_tm - o_m|
+#    <= 2^-8 * 2 max_t |c_tm| = 2^-7 max_t |c_tm|.  The split-KV combine keeps
+#    one rounding per token, so the bound holds for the merged result too.  It
+#    is absolute, per row, in units of the largest latent entry the row can
+#    see (KERNEL_P_ROUND), plus 1e-5 relative for float32 accumulation; lse
+#    moves by <= 2^-9 + 1e-5.
 TOL_E2E = {"f32": 1e-4, "bf16": 1e-2}
-TOL_KERNEL = {"f32": 1e-5, "bf16": 3e-3}
 TOL_KERNEL_GENERIC = 1e-5
+KERNEL_P_ROUND = 2.0 ** -7
+KERNEL_LSE = 2.0 ** -9 + 1e-5
 
 
 def announce(msg: str):
