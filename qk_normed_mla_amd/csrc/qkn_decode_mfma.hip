@@ -13,37 +13,35 @@
 // the 4 bytes per token and group of the scalar cache.
 //
 // Work decomposition
-//   one workgroup (8 waves, 2 per SIMD) per (sequence b, split p, block of 128
-//   query rows); wave w owns 16 query rows = 16 heads of one query token, all
+//   one workgroup (4 waves, 1 per SIMD) per (sequence b, split p, block of 128
+//   query rows); wave w owns 32 query rows = 32 heads of one query token, all
 //   in one KV group.  Every 64-token page of the split is read from HBM once
-//   and shared by the 8 waves through LDS.  A wave keeps its 16 x 512 latent
-//   accumulator (128 registers) and its q~ (64 registers) in registers, so two
-//   waves fit on a SIMD and one wave's softmax overlaps the other's MFMAs.
+//   and shared by the 4 waves through LDS.  A wave keeps q~ (128 registers) in
+//   VGPRs and its 32 x 512 latent accumulator (256 registers) in the AGPR file.
 //
-// Per page (one pipeline stage):
+// Per page (one pipeline stage), in two 32-token halves:
 //   HBM -> LDS   73 LDS-DMA loads of 16 B per lane (buffer_load ... lds), issued
 //                two pages ahead into a double buffer.  The buffer descriptor of
 //                a page ends at the last valid token, so a partial page reads
 //                zeros beyond it; an invalid page entry reads zeros throughout.
-//   QK           S^T[16 tok x 16 heads] = C[16 x 512] . q~^T  (v_mfma_f32_16x16x32_bf16,
-//                A = latent rows from LDS, B = q~ held in registers for the whole
+//   QK           S^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
+//                A = latent rows from LDS, B = q~ in registers for the whole
 //                kernel), then S *= alpha^q alpha^k, then += K^R . q^R^T.
-//   softmax      online, base 2, once per page, with the running maximum raised
-//                only when a row's maximum grows by more than 8 (in log2
-//                units): the probabilities stay <= 2^8 and the rescale factor
-//                of the running sums is 1 almost always.  A head's tokens sit
-//                in lanes l, l^16, l^32, l^48.
-//   PV           O^T[512 x 16 heads] += C^T . P^T over 32-token steps, the C^T
-//                operand read with ds_read_b64_tr_b16 straight from the
-//                row-major page in LDS; the token order inside a step follows
-//                the register layout of two S^T tiles (both operands use the
-//                same permutation of the reduction index, which leaves the sum
-//                unchanged).
+//   softmax      base 2 against a per-head reference fixed at the first
+//                visible tokens of the split, so the accumulator is never
+//                rescaled inside the loop.  QK-norm bounds the logits, so the
+//                probabilities stay far below the 2^96 headroom allowed; should
+//                a later logit exceed it, the workgroup restarts the split with
+//                the larger reference (exact; never seen with normalised
+//                logits).  A head's tokens sit in lanes l and l^32.
+//   PV           O^T[512 x 32 heads] += C^T . P^T, the C^T operand read with
+//                ds_read_b64_tr_b16 straight from the row-major page in LDS; the
+//                token order inside each 16-token step follows the register
+//                layout of S^T (both operands use the same permutation of the
+//                reduction index, which leaves the sum unchanged).
 // LDS layout of a staged page (bytes): content [64][1024] with the 16-byte
 // chunk c of token t stored at chunk position c ^ f(t) (f below), RoPE keys
 // [64][128] with chunk c of token t at c ^ ((t >> 1) & 7), then alpha^k [64][G].
-// The swizzles make both the row reads of QK and the transposed reads of PV
-// free of bank conflicts.
 #include <math.h>
 
 #include "qkn_internal.h"
@@ -54,6 +52,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -66,11 +65,13 @@ constexpr int ROPE_BYTES = PAGE * DR * 2;         // 8192
 constexpr int ALPHA_BYTES = PAGE * 16 * 4;        // room for G <= 16
 constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 77824
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // 155648
-constexpr int WAVES = 8;
-constexpr int HEADS_PER_WAVE = 16;
+constexpr int WAVES = 4;
+constexpr int HEADS_PER_WAVE = 32;
 constexpr int ROWS_PER_WG = WAVES * HEADS_PER_WAVE;  // 128
 constexpr int kMaxGroups = 16;
-constexpr float kRescaleThreshold = 8.0f;         // log2 units
+constexpr int QK_AHEAD = 3;                      // LDS reads in flight ahead of the MFMAs
+constexpr int PV_AHEAD = 3;
+constexpr float kMaxExp2 = 96.0f;                 // headroom of p = 2^(y - ref), log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -109,19 +110,37 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const LDS_AS uint8_t* p) {
       reinterpret_cast<LDS_AS bf16x4*>(const_cast<LDS_AS uint8_t*>(p)));
 }
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// The lane index, re-materialised where it is used: the empty volatile asm
+// keeps per-lane offsets derived from it from being hoisted out of the page
+// loop and held in registers for the whole kernel.
+__device__ __forceinline__ int fresh_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
 }
 
-// max / sum over the four lanes l, l^16, l^32, l^48 that hold one head
-__device__ __forceinline__ float head_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float head_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+
+// PV product into an accumulator tile kept in the AGPR file (the 512-wide
+// accumulator of a wave fills it exactly).  Issued through asm so that the
+// compiler never parks another MFMA result in an AGPR and spills a tile to
+// make room.  Hazards the compiler cannot see through asm: 2 wait states
+// before the MFMA reads operands written by the vector ALU (s_nop 1), and
+// wait_acc_results() before anything reads the accumulator back.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc) : "v"(a), "v"(b));
 }
+// wait states between an MFMA writing registers and a vector instruction
+// reading them (covers the longest MFMA; 3 x 8)
+__device__ __forceinline__ void wait_acc_results() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 template <bool USE_ALPHA>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
@@ -146,8 +165,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int l16 = lane & 15;
-  const int q4 = lane >> 4;   // which 8-wide slice of a 32-long reduction step
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;   // which 8-wide half of a 16-long reduction step
   int err = 0;
 
   int T = seq_lens[b];
@@ -161,7 +180,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int first_page = lo / PAGE;
   const int n_st = hi > lo ? (hi - lo + PAGE - 1) / PAGE : 0;
 
-  // this wave's 16 query rows: query token i, heads h0 .. h0 + 15, group g
+  // this wave's 32 query rows: query token i, heads h0 .. h0 + 31, group g
   const int rows_total = s_q * heads;
   const int row0 = rb * ROWS_PER_WG + w * HEADS_PER_WAVE;
   const bool wave_active = row0 < rows_total;
@@ -170,24 +189,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int g = h0 / (heads / groups);
   const int hi_w = min(hi, T - s_q + i + 1);  // visible end for this query token
   // row of this lane's head (an idle wave uses row 0 and discards its results)
-  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l16;
+  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l32;
 
-  // q~ as the B operand of QK: lane holds q~[head l16][32 kk + 8 q4 .. +8]
-  bf16x8 qb[R / 32];
-  bf16x8 qrb[DR / 32];
+  // q~ as the B operand of QK: lane holds q~[head l32][16 kk + 8 hh .. +8]
+  bf16x8 qb[R / 16];
+  bf16x8 qrb[DR / 16];
   {
-    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + q4;
+    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + hh;
 #pragma unroll
-    for (int kk = 0; kk < R / 32; ++kk) qb[kk] = qt[4 * kk];
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + q4;
+    for (int kk = 0; kk < R / 16; ++kk) qb[kk] = qt[2 * kk];
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + hh;
 #pragma unroll
-    for (int kk = 0; kk < DR / 32; ++kk) qrb[kk] = qr[4 * kk];
+    for (int kk = 0; kk < DR / 16; ++kk) qrb[kk] = qr[2 * kk];
   }
   const float aq = USE_ALPHA ? alpha_q[my_row] : 1.f;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query operands are in registers
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS uint8_t*)smem));
-  const int alpha_bytes_per_wave = PAGE * groups * 4 / WAVES;  // 32 G
+  const int alpha_bytes_per_wave = PAGE * groups * 4 / WAVES;  // 64 G
 
   // page index of stage s (-1 when the entry is out of range)
   auto page_of = [&](int s) -> int {
@@ -195,19 +214,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     return (pg >= 0 && pg < num_pages) ? pg : -1;
   };
 
-  // DMA source offsets inside a page.  Content token t = w + 8k starts at
-  // t * ROW_BYTES; the per-lane chunk depends on t only through t mod 16 (w or
-  // w + 8) in the swizzle.
-  const uint32_t dma_content0 = (lane ^ swz(w)) << 4;
-  const uint32_t dma_content1 = (lane ^ swz(w + 8)) << 4;
-  // RoPE rows of tokens 8w .. 8w + 7: token 8 w + lane / 8, chunk (lane % 8) ^ f_R(token)
-  const uint32_t dma_rope = (8 * w + (lane >> 3)) * ROW_BYTES + R * 2 +
-                            (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-  const uint32_t dma_alpha = w * (PAGE * groups * 4 / WAVES) + lane * 16;
-
-  // issue the 10 loads of this wave for stage s into buffer (s & 1):
-  // 8 content rows, 1 RoPE block, 1 slice of alpha^k
+  // issue the 19 loads of this wave for stage s into buffer (s & 1):
+  // 16 content rows, 2 RoPE blocks, 1 slice of alpha^k
   auto issue = [&](int s) {
+    const int ln = fresh_lane();
     const int pg = page_of(s);
     const int tok0 = lo + s * PAGE;
     const int nv = pg >= 0 ? min(PAGE, T - tok0) : 0;   // valid rows of the page
@@ -216,169 +226,201 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const i32x4 rs = buffer_rsrc(page_ptr, nv * ROW_BYTES);
     const uint32_t buf = lds_base + (s & 1) * STAGE_BYTES;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {  // content: token t = w + 8k, lane -> chunk lane ^ f(t)
-      const int t = w + 8 * k;
-      dma16(buf + t * 1024, ((k & 1) ? dma_content1 : dma_content0) + t * ROW_BYTES, rs);
+    for (int k = 0; k < 16; ++k) {  // content: token t = w + 4k, lane -> chunk lane ^ f(t)
+      const int t = w + 4 * k;
+      dma16(buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t & 15)) << 4), rs);
     }
-    // RoPE keys of tokens 8w .. 8w + 7
-    dma16(buf + CONTENT_BYTES + w * 1024, dma_rope, rs);
-    {  // alpha^k of the page: 64 * G floats, an eighth per wave
+    // RoPE keys of tokens 8r .. 8r + 7 for r = w, w + 4: token 8 r + lane / 8,
+    // chunk (lane % 8) ^ f_R(token), and f_R = (4 r + lane / 16) mod 8 is the same for both
+    const uint32_t rope_lane = (ln >> 3) * ROW_BYTES + R * 2 +
+                               (((ln & 7) ^ ((4 * w + (ln >> 4)) & 7)) << 4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = w + 4 * k;
+      dma16(buf + CONTENT_BYTES + r * 1024, r * 8 * ROW_BYTES + rope_lane, rs);
+    }
+    {  // alpha^k of the page: 64 * G floats, a quarter per wave
       const float* ap = alpha_k + (size_t)(pg >= 0 ? pg : 0) * PAGE * groups;
       const i32x4 ra = buffer_rsrc(ap, nv * groups * 4);
-      if (lane * 16 < alpha_bytes_per_wave)
-        dma16(buf + CONTENT_BYTES + ROPE_BYTES + w * alpha_bytes_per_wave, dma_alpha, ra);
+      if (ln * 16 < alpha_bytes_per_wave)
+        dma16(buf + CONTENT_BYTES + ROPE_BYTES + w * alpha_bytes_per_wave,
+              w * alpha_bytes_per_wave + ln * 16, ra);
     }
   };
 
-  // Per-lane LDS byte offsets inside a staged page.  The XOR swizzle only
-  // touches the low bits of a chunk index, and a chunk index splits into
-  // disjoint bit fields, so every read is  (per-lane base) XOR (compile-time
-  // constant)  plus a compile-time offset above those bits:
-  //   QK row read, token 32 tb + 16 tt + l16, chunk 4 kk + q4:
-  //     [l16 * 1024 + ((q4 ^ f(l16)) << 4)] ^ (64 (kk % 4)) + 256 (kk / 4) + 1024 (32 tb + 16 tt)
-  //   RoPE row read, chunk 4 kk + q4 (kk < 2):
-  //     [l16 * 128 + ((q4 ^ f_R(l16)) << 4)] ^ (64 kk) + 128 (32 tb + 16 tt)
-  //   PV transposed read of latents 16 om .. +15, tokens 32 tb + 4 q4 + (0..3)
-  //   and + 16: row t = 4 q4 + l16 / 4, chunk 2 om + c1 with c1 = (l16 % 4) / 2,
-  //   byte (l16 % 2) * 8 of the chunk:
-  //     [t * 1024 + (l16 % 2) * 8 + ((c1 ^ f(t)) << 4)] ^ (32 (om % 8)) + 256 (om / 8) + 1024 (32 tb [+ 16])
-  // A stage base is a multiple of 1024 and so commutes with the XORs.
-  const uint32_t qk_base = l16 * 1024 + ((q4 ^ swz(l16)) << 4);
-  const uint32_t rp_base = l16 * 128 + ((q4 ^ swz_rope(l16)) << 4);
-  uint32_t pv_base;
-  {
-    const int t = 4 * q4 + (l16 >> 2);
-    pv_base = t * 1024 + (l16 & 1) * 8 + (((((l16 & 3) >> 1)) ^ swz(t)) << 4);
-  }
-
-  f32x4 acc[R / 16];
-#pragma unroll
-  for (int om = 0; om < R / 16; ++om) acc[om] = f32x4{};
-  float m_run = -INFINITY;  // running max of the unscaled logits of this lane's head
-  float l_run = 0.f;        // this lane's share of the softmax denominator
+  f32x16 acc[R / 32];
+  float m_ref = -INFINITY;   // reference of the exponent for this lane's head (logit units)
+  float m_seen = -INFINITY;  // largest logit of this head seen so far
+  float l_run = 0.f;         // this lane's share of the softmax denominator
   const float c2 = scale * kLog2e;  // logits -> log2 units
 
-  if (n_st > 0) issue(0);
-  if (n_st > 1) issue(1);
+  bool again;
+  do {
+    again = false;
+#pragma unroll
+    for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
+    l_run = 0.f;
+    if (n_st > 0) issue(0);
+    if (n_st > 1) issue(1);
 
-  for (int s = 0; s < n_st; ++s) {
-    if (s + 1 < n_st) {
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // the next page's 10 loads may fly
-    } else {
+    for (int s = 0; s < n_st; ++s) {
+      if (s + 1 < n_st) {
+        asm volatile("s_waitcnt vmcnt(19)" ::: "memory");  // the next page's 19 loads may fly
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      const uint32_t stage_off = (s & 1) * STAGE_BYTES;
+      const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
+      const LDS_AS float* st_alpha = (const LDS_AS float*)(lds0 + stage_off + CONTENT_BYTES + ROPE_BYTES);
+      const int tok0 = lo + s * PAGE;
+      const bool page_ok = page_of(s) >= 0;
+      if (!page_ok) err = 1;
+      // rows r of this page with r < lim are visible to this wave
+      const int lim = page_ok ? hi_w - tok0 : 0;
+      int overflow = 0;
+
+      if (wave_active) {
+        // Per-lane LDS byte offsets inside the staged page.  The XOR swizzle only
+        // touches the low 4 bits of a chunk index, and a chunk index splits into
+        // disjoint bit fields, so every read is (per-lane base) XOR (constant)
+        // plus a compile-time offset above those bits (stage bases are multiples
+        // of 1024 and commute with the XORs):
+        //  QK row read, token 32 mt + l32, chunk 2 kk + hh:
+        //    [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8) + 32768 mt
+        //  RoPE row read, chunk 2 kk + hh (kk < 4):
+        //    [l32*128 + ((hh ^ f_R(l32)) << 4)] ^ (32 kk) + 4096 mt
+        //  PV transposed read: 16-lane group G = lane / 16 reads 4 rows
+        //  t0 = 4 (G / 2) + (lane % 16) / 4 of the step (and t0 + 8), latents
+        //  32 om + 16 (G % 2) + 4 (lane % 4) .. +3, i.e. chunk 4 om + c0 with
+        //  c0 = 2 (G % 2) + (lane % 4) / 2, byte 8 (lane % 2) of the chunk:
+        //    [t*1024 + 8 (lane % 2) + ((c0 ^ f(t)) << 4)] ^ (64 (om % 4)) + 256 (om / 4) + 1024 (16 ks + 32 mt)
+        uint32_t qk_b, rp_b, pv_a, pv_bb;
+        {
+          const int ln = fresh_lane();
+          const int lt = ln & 31, lh = ln >> 5;
+          qk_b = lt * 1024 + ((lh ^ swz(lt & 15)) << 4) + stage_off;
+          rp_b = lt * 128 + ((lh ^ swz_rope(lt)) << 4) + stage_off + CONTENT_BYTES;
+          const int G = ln >> 4, k16 = ln & 15;
+          const int t0 = 4 * (G >> 1) + (k16 >> 2);
+          const int c0 = 2 * (G & 1) + ((k16 & 3) >> 1);
+          const int inner = 8 * (k16 & 1);
+          pv_a = t0 * 1024 + inner + ((c0 ^ swz(t0)) << 4) + stage_off;
+          pv_bb = (t0 + 8) * 1024 + inner + ((c0 ^ swz(t0 + 8)) << 4) + stage_off;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          // ---- QK for 32 tokens: content, alpha scaling, RoPE ----
+          // 32 reduction steps kk = 8 kh + k8, operands read QK_AHEAD steps ahead
+          f32x16 sc = f32x16{};
+          {
+            constexpr int NK = R / 16;
+            bf16x8 abuf[QK_AHEAD];
+            auto rd = [&](int n) {  // step n in issue order: k8 = n / 4, kh = n % 4
+              const int k8 = n >> 2, kh = n & 3;
+              return lds_read16(lds0 + (qk_b ^ (32u * k8)) + 256 * kh + 32768 * mt);
+            };
+#pragma unroll
+            for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
+#pragma unroll
+            for (int n = 0; n < NK; ++n) {
+              const bf16x8 a = abuf[n % QK_AHEAD];
+              if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
+              sc = mfma(a, qb[8 * (n & 3) + (n >> 2)], sc);
+            }
+          }
+          if (USE_ALPHA) {
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg) {
+              const int t = 32 * mt + 8 * jg + 4 * hh;  // rows of registers 4 jg .. 4 jg + 3
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sc[4 * jg + e] *= aq * st_alpha[(t + e) * groups + g];
+            }
+          }
+#pragma unroll
+          for (int kk = 0; kk < DR / 16; ++kk) {
+            const bf16x8 a = lds_read16(lds0 + (rp_b ^ (32u * kk)) + 4096 * mt);
+            sc = mfma(a, qrb[kk], sc);
+          }
+          // ---- mask rows past the visible end (tail page, causal window, bad page)
+          if (lim < 32 * mt + 32) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (32 * mt + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[j] = -INFINITY;
+          }
+          // ---- probabilities against the fixed reference ----
+          float mx = sc[0];
+#pragma unroll
+          for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
+          mx = pair_max(mx);
+          m_seen = fmaxf(m_seen, mx);
+          if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
+          if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
+          const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+          bf16x8 pb[2];  // P^T of the two 16-token steps
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const __bf16 pr = static_cast<__bf16>(exp2f(fmaf(sc[j], c2, -mc)));
+            pb[j >> 3][j & 7] = pr;
+            l_run += static_cast<float>(pr);
+          }
+          // ---- PV: O^T[512 x 32] += C^T[512 x 32 tok] . P^T ----
+          // 32 products (o4, ks, oh) in that order, operands read PV_AHEAD ahead
+          {
+            constexpr int NP = 4 * 2 * (R / 128);
+            bf16x8 abuf[PV_AHEAD];
+            auto rd = [&](int n) {
+              const int o4 = n >> 3, ks = (n >> 2) & 1, oh = n & 3;
+              const int imm = 256 * oh + 1024 * (16 * ks + 32 * mt);
+              const bf16x4 lo4 = lds_read_tr(lds0 + (pv_a ^ (64u * o4)) + imm);
+              const bf16x4 hi4 = lds_read_tr(lds0 + (pv_bb ^ (64u * o4)) + imm);
+              return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+#pragma unroll
+            for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
+#pragma unroll
+            for (int n = 0; n < NP; ++n) {
+              const bf16x8 a = abuf[n % PV_AHEAD];
+              if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
+              mfma_acc(acc[4 * (n & 3) + (n >> 3)], a, pb[(n >> 2) & 1]);
+            }
+          }
+        }
+      }
+      // all waves done with this buffer; did any head outgrow its reference?
+      if (__syncthreads_or(overflow)) {
+        again = true;
+        break;
+      }
+      if (s + 2 < n_st) issue(s + 2);
+    }
+    if (again) {
+      // restart the split with the largest logit seen as the reference
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      m_ref = m_seen;
     }
-    __syncthreads();
-    const uint32_t stage_off = (s & 1) * STAGE_BYTES;
-    const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
-    const LDS_AS float* st_alpha = (const LDS_AS float*)(lds0 + stage_off + CONTENT_BYTES + ROPE_BYTES);
-    const uint32_t qk_b = qk_base + stage_off;
-    const uint32_t rp_b = rp_base + stage_off + CONTENT_BYTES;
-    const uint32_t pv_b = pv_base + stage_off;
-    const int tok0 = lo + s * PAGE;
-    const bool page_ok = page_of(s) >= 0;
-    if (!page_ok) err = 1;
-    // rows r of this page with r < lim are visible to this wave
-    const int lim = page_ok ? hi_w - tok0 : 0;
+  } while (again);
 
-    if (wave_active) {
-      // ---- QK for the 64 tokens of the page: four 16-token tiles ----
-      f32x4 sc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-#pragma unroll
-      for (int kk = 0; kk < R / 32; ++kk) {
-        const uint32_t a_off = (qk_b ^ (64u * (kk & 3))) + 256 * (kk >> 2);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const bf16x8 a = lds_read16(lds0 + a_off + 1024 * 16 * tt);
-          sc[tt] = mfma(a, qb[kk], sc[tt]);
-        }
-      }
-      if (USE_ALPHA) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int t = 16 * tt + 4 * q4;  // rows of the four registers
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sc[tt][j] *= aq * st_alpha[(t + j) * groups + g];
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < DR / 32; ++kk) {
-        const uint32_t a_off = rp_b ^ (64u * kk);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const bf16x8 a = lds_read16(lds0 + a_off + 128 * 16 * tt);
-          sc[tt] = mfma(a, qrb[kk], sc[tt]);
-        }
-      }
-      // ---- mask rows past the visible end (tail page, causal window, bad page)
-      if (lim < PAGE) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (16 * tt + 4 * q4 + j >= lim) sc[tt][j] = -INFINITY;
-      }
-      // ---- online softmax over the page; the running sums are rescaled by a
-      // per-head factor (1 unless the maximum grew by more than the threshold)
-      float mx = sc[0][0];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[tt][j]);
-      mx = head_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_new - m_run) * c2 > kRescaleThreshold;  // false when both -inf
-      float f = 1.f;
-      if (grow) {
-        f = (m_new == -INFINITY) ? 1.f : exp2f((m_run - m_new) * c2);
-        m_run = m_new;
-      }
-#pragma unroll
-      for (int om = 0; om < R / 16; ++om)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[om][j] *= f;
-      l_run *= f;
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c2;
-      bf16x8 pb[2];  // P^T of tokens 32 tb .. +31: elements 0-3 tile 2 tb, 4-7 tile 2 tb + 1
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const __bf16 pr = static_cast<__bf16>(exp2f(fmaf(sc[tt][j], c2, -mc)));
-          pb[tt >> 1][4 * (tt & 1) + j] = pr;
-          l_run += static_cast<float>(pr);
-        }
-      // ---- PV: O^T[512 x 16] += C^T[512 x 64 tok] . P^T, two 32-token steps ----
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int om = 0; om < R / 16; ++om) {
-          const uint32_t a_off = (pv_b ^ (32u * (om & 7))) + 256 * (om >> 3) + 1024 * 32 * tb;
-          const bf16x4 lo4 = lds_read_tr(lds0 + a_off);
-          const bf16x4 hi4 = lds_read_tr(lds0 + a_off + 16 * 1024);
-          const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[om] = mfma(a, pb[tb], acc[om]);
-        }
-      }
-    }
-    __syncthreads();
-    if (s + 2 < n_st) issue(s + 2);
-  }
-
-  // ---- epilogue: o_p = acc / l, lse_p = scale * m + ln l ----
+  // ---- epilogue: o_p = acc / l, lse_p = scale * m_ref + ln l ----
+  wait_acc_results();
   if (wave_active) {
-    const float l_tot = head_sum(l_run);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* out = o_part + (my_row * num_splits + p) * R;
 #pragma unroll
-    for (int om = 0; om < R / 16; ++om) {
-      f32x4 v;
+    for (int om = 0; om < R / 32; ++om) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[om][j] * inv;
-      *reinterpret_cast<f32x4*>(out + om * 16 + q4 * 4) = v;
+      for (int jg = 0; jg < 4; ++jg) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[om][4 * jg + e] * inv;
+        *reinterpret_cast<f32x4*>(out + 32 * om + 8 * jg + 4 * hh) = v;
+      }
     }
-    if (q4 == 0) {
+    if (hh == 0) {
       lse_part[my_row * num_splits + p] =
-          l_tot > 0.f ? m_run * scale + log2f(l_tot) * kLn2 : -INFINITY;
+          l_tot > 0.f ? m_ref * scale + log2f(l_tot) * kLn2 : -INFINITY;
     }
   }
   if (err && err_flag && lane == 0) atomicOr(err_flag, 1);
