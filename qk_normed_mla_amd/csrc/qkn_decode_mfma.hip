@@ -13,18 +13,22 @@
 // the 4 bytes per token and group of the scalar cache.
 //
 // Work decomposition
-//   one workgroup (4 waves, 1 per SIMD) per (sequence b, split p, block of 128
-//   query rows); wave w owns 32 query rows = 32 heads of one query token, all
-//   in one KV group.  Every 64-token page of the split is read from HBM once
-//   and shared by the 4 waves through LDS.  A wave keeps q~ (128 registers) in
-//   VGPRs and its 32 x 512 latent accumulator (256 registers) in the AGPR file.
+//   one workgroup (8 waves, 2 per SIMD) per (sequence b, split p, block of 128
+//   query rows); wave w owns 16 query rows = 16 heads of one query token, all
+//   in one KV group.  Every token of the split is read from HBM once and
+//   shared by the 8 waves through LDS.  A wave keeps q~ (72 registers) and its
+//   16 x 512 latent accumulator (128 registers) for the whole kernel, within
+//   the 256 registers that let two waves share a SIMD, so one wave's softmax
+//   overlaps the other's MFMAs.
 //
-// Per page (one pipeline stage), in two 32-token halves:
-//   HBM -> LDS   73 LDS-DMA loads of 16 B per lane (buffer_load ... lds), issued
-//                two pages ahead into a double buffer.  The buffer descriptor of
-//                a page ends at the last valid token, so a partial page reads
-//                zeros beyond it; an invalid page entry reads zeros throughout.
-//   QK           S^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
+// Per 32-token stage (half a page):
+//   HBM -> LDS   LDS-DMA loads of 16 B per lane (buffer_load ... lds) into a
+//                ring of 4 stage buffers, 3 stages in flight, so that about
+//                115 KB per CU is always on its way from HBM.  The buffer
+//                descriptor of a stage ends at its last valid token, so a
+//                partial page reads zeros beyond it; an invalid page entry
+//                reads zeros throughout.
+//   QK           S^T[16 tok x 16 heads] = C[16 x 512] . q~^T  (v_mfma_f32_16x16x32_bf16,
 //                A = latent rows from LDS, B = q~ in registers for the whole
 //                kernel), then S *= alpha^q alpha^k, then += K^R . q^R^T.
 //   softmax      base 2 against a per-head reference fixed at the first
@@ -33,15 +37,18 @@
 //                probabilities stay far below the 2^96 headroom allowed; should
 //                a later logit exceed it, the workgroup restarts the split with
 //                the larger reference (exact; never seen with normalised
-//                logits).  A head's tokens sit in lanes l and l^32.
-//   PV           O^T[512 x 32 heads] += C^T . P^T, the C^T operand read with
-//                ds_read_b64_tr_b16 straight from the row-major page in LDS; the
-//                token order inside each 16-token step follows the register
-//                layout of S^T (both operands use the same permutation of the
-//                reduction index, which leaves the sum unchanged).
-// LDS layout of a staged page (bytes): content [64][1024] with the 16-byte
-// chunk c of token t stored at chunk position c ^ f(t) (f below), RoPE keys
-// [64][128] with chunk c of token t at c ^ ((t >> 1) & 7), then alpha^k [64][G].
+//                logits).  A head's tokens sit in lanes l, l^16, l^32, l^48.
+//   PV           O^T[512 x 16 heads] += C^T . P^T over the 32 tokens, the C^T
+//                operand read with ds_read_b64_tr_b16 straight from the
+//                row-major stage in LDS; the token order inside the step
+//                follows the register layout of two S^T tiles (both operands
+//                use the same permutation of the reduction index, which leaves
+//                the sum unchanged).
+// LDS layout of a stage (bytes): content [32][1024] with the 16-byte chunk c of
+// token t stored at chunk position c ^ f(t) (f below), RoPE keys [32][128] with
+// chunk c of token t at c ^ ((t >> 1) & 7), then alpha^k [32][G].  The
+// swizzles spread the row reads of QK and the transposed reads of PV over
+// the LDS banks.
 #include <math.h>
 
 #include "qkn_internal.h"
@@ -52,21 +59,23 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int R = 512;                    // latent rank
 constexpr int DR = 64;                    // RoPE dim
-constexpr int PAGE = QKN_MLA_PAGE_SIZE;   // 64 tokens per page = per stage
+constexpr int PAGE = QKN_MLA_PAGE_SIZE;   // 64 tokens per page
+constexpr int ST = 32;                    // tokens per pipeline stage
+constexpr int NSTAGE = 4;                 // stage buffers in LDS
 constexpr int ROW_BYTES = (R + DR) * 2;   // 1152
-constexpr int CONTENT_BYTES = PAGE * R * 2;       // 65536
-constexpr int ROPE_BYTES = PAGE * DR * 2;         // 8192
-constexpr int ALPHA_BYTES = PAGE * 16 * 4;        // room for G <= 16
-constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 77824
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // 155648
-constexpr int WAVES = 4;
-constexpr int HEADS_PER_WAVE = 32;
+constexpr int CONTENT_BYTES = ST * R * 2;         // 32768
+constexpr int ROPE_BYTES = ST * DR * 2;           // 4096
+constexpr int ALPHA_BYTES = ST * 16 * 4;          // room for G <= 16
+constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 38912
+constexpr int FLAG_OFFSET = NSTAGE * STAGE_BYTES; // the workgroup's restart flag
+constexpr int LDS_BYTES = FLAG_OFFSET + 16;       // 155664
+constexpr int WAVES = 8;
+constexpr int HEADS_PER_WAVE = 16;
 constexpr int ROWS_PER_WG = WAVES * HEADS_PER_WAVE;  // 128
 constexpr int kMaxGroups = 16;
 constexpr int QK_AHEAD = 3;                      // LDS reads in flight ahead of the MFMAs
@@ -75,8 +84,17 @@ constexpr float kMaxExp2 = 96.0f;                 // headroom of p = 2^(y - ref)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// content chunk position of chunk c of token t: c ^ f(t mod 16)
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+// content chunk position of chunk c of token t: c ^ f(t mod 16), f the
+// linear map over GF(2)^4 with f(1) = 2, f(2) = 15, f(4) = 8, f(8) = 9.
+// Measured on gfx950: LDS b128 reads run at full rate when lanes 0-7 of a
+// 16-lane group stay in one 128-byte half of the 64 banks and lanes 8-15 in
+// the other, which the QK row read (16 tokens x one chunk) meets when f's top
+// bit follows t's top bit; among such maps this one also keeps the
+// transposed 8-byte reads of PV (4 tokens x 2 chunks per 16 lanes) near
+// their best rate.  A search over all invertible maps picked it.
+__device__ __forceinline__ int swz(int t) {
+  return static_cast<int>((0xce3146b957a8df20ull >> (4 * (t & 15))) & 15);
+}
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
 
 // raw buffer descriptor: base, byte size (reads at or past it return 0)
@@ -119,28 +137,35 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// the value, hidden from the optimiser so that it recomputes what derives from it
+// instead of keeping those results live in registers
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-// PV product into an accumulator tile kept in the AGPR file (the 512-wide
-// accumulator of a wave fills it exactly).  Issued through asm so that the
-// compiler never parks another MFMA result in an AGPR and spills a tile to
-// make room.  Hazards the compiler cannot see through asm: 2 wait states
-// before the MFMA reads operands written by the vector ALU (s_nop 1), and
-// wait_acc_results() before anything reads the accumulator back.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-               : "+a"(acc) : "v"(a), "v"(b));
-}
-// wait states between an MFMA writing registers and a vector instruction
-// reading them (covers the longest MFMA; 3 x 8)
-__device__ __forceinline__ void wait_acc_results() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
-__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+// max / sum over the four lanes l, l^16, l^32, l^48 that hold one head.
+// v_permlane16_swap / v_permlane32_swap with both operands v return the two
+// halves that pair lane l with lane l^16 (l^32) in every lane.
+__device__ __forceinline__ float xor16_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float head_max(float v) { return xor32_pair_max(xor16_pair_max(v)); }
+__device__ __forceinline__ float head_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <bool USE_ALPHA>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
@@ -165,8 +190,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;   // which 8-wide half of a 16-long reduction step
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;   // which 8-wide slice of a 32-long reduction step
   int err = 0;
 
   int T = seq_lens[b];
@@ -177,10 +202,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int L = split_len(max(T, 1), num_splits);
   const int lo = p * L;
   const int hi = min(lo + L, T);
-  const int first_page = lo / PAGE;
-  const int n_st = hi > lo ? (hi - lo + PAGE - 1) / PAGE : 0;
+  const int first_page = lo / PAGE;  // lo is a multiple of the page size
+  const int n_st = hi > lo ? (hi - lo + ST - 1) / ST : 0;
 
-  // this wave's 32 query rows: query token i, heads h0 .. h0 + 31, group g
+  // this wave's 16 query rows: query token i, heads h0 .. h0 + 15, group g
   const int rows_total = s_q * heads;
   const int row0 = rb * ROWS_PER_WG + w * HEADS_PER_WAVE;
   const bool wave_active = row0 < rows_total;
@@ -189,237 +214,294 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int g = h0 / (heads / groups);
   const int hi_w = min(hi, T - s_q + i + 1);  // visible end for this query token
   // row of this lane's head (an idle wave uses row 0 and discards its results)
-  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l32;
+  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l16;
 
-  // q~ as the B operand of QK: lane holds q~[head l32][16 kk + 8 hh .. +8]
-  bf16x8 qb[R / 16];
-  bf16x8 qrb[DR / 16];
+  // Page-table window: lane j of every wave holds the entry of split page
+  // wbase + j (64 pages, 4096 tokens), so a stage finds its page with one
+  // v_readlane instead of a memory round trip inside the loop.
+  int wbase = 0;
+  int pwin;
+  auto load_window = [&](int base) {
+    const int j = first_page + base + fresh_lane();
+    pwin = j < max_pages ? block_table[(size_t)b * max_pages + j] : -1;
+  };
+  load_window(0);
+
+  // q~ as the B operand of QK: lane holds q~[head l16][32 kk + 8 q4 .. +8]
+  bf16x8 qb[R / 32];
+  bf16x8 qrb[DR / 32];
   {
-    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + hh;
+    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + q4;
 #pragma unroll
-    for (int kk = 0; kk < R / 16; ++kk) qb[kk] = qt[2 * kk];
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + hh;
+    for (int kk = 0; kk < R / 32; ++kk) qb[kk] = qt[4 * kk];
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + q4;
 #pragma unroll
-    for (int kk = 0; kk < DR / 16; ++kk) qrb[kk] = qr[2 * kk];
+    for (int kk = 0; kk < DR / 32; ++kk) qrb[kk] = qr[4 * kk];
   }
   const float aq = USE_ALPHA ? alpha_q[my_row] : 1.f;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query operands are in registers
+  // query operands and page window in registers before any page load is
+  // issued (the page loads are not visible to the compiler's own waits)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS uint8_t*)smem));
-  const int alpha_bytes_per_wave = PAGE * groups * 4 / WAVES;  // 64 G
 
-  // page index of stage s (-1 when the entry is out of range)
-  auto page_of = [&](int s) -> int {
-    int pg = block_table[(size_t)b * max_pages + first_page + s];
-    return (pg >= 0 && pg < num_pages) ? pg : -1;
+  // validity of the pages of the stages in flight, bit s mod 4 (uniform)
+  uint32_t vmask = 0;
+
+  // The 6 loads of this wave for stage s (tokens lo + 32 s ..) into buffer
+  // s mod 4: 4 content rows, a quarter of the RoPE block on lanes 0-31, and an
+  // eighth of alpha^k on lanes 0 .. G-1 (lane 0 always takes part, so every
+  // wave issues all 6 and the vmcnt bookkeeping holds).  plan() looks the page
+  // up and builds the descriptors; load(k) issues load k.  Inside the page
+  // loop the loads are spread over the QK products, so the address units work
+  // through them while the matrix cores run.
+  struct StagePlan {
+    i32x4 rs, ra;  // KV rows of the stage, alpha^k rows of the stage
+    uint32_t buf;  // LDS address of the stage buffer
   };
-
-  // issue the 19 loads of this wave for stage s into buffer (s & 1):
-  // 16 content rows, 2 RoPE blocks, 1 slice of alpha^k
-  auto issue = [&](int s) {
+  auto plan = [&](int s) {
+    const int rel = s >> 1;  // page of the split
+    if (rel < wbase || rel >= wbase + 64) {  // uniform; once per 64 pages
+      wbase = rel & ~63;
+      load_window(wbase);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    int pg = __builtin_amdgcn_readlane(pwin, rel - wbase);
+    pg = (pg >= 0 && pg < num_pages) ? pg : -1;
+    vmask = (vmask & ~(1u << (s & 3))) | ((pg >= 0 ? 1u : 0u) << (s & 3));
+    const int tok0 = lo + s * ST;
+    const int nv = pg >= 0 ? min(ST, T - tok0) : 0;   // valid rows of the stage
+    const size_t row0 = (size_t)(pg >= 0 ? pg : 0) * PAGE + (s & 1) * ST;  // cache row
+    StagePlan pl;
+    pl.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0 * ROW_BYTES, nv * ROW_BYTES);
+    pl.ra = buffer_rsrc(alpha_k + row0 * groups, nv * groups * 4);
+    pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
+    asm volatile("" : "+s"(pl.buf));  // keep the per-load LDS addresses out of loop-invariant registers
+    return pl;
+  };
+  auto load = [&](const StagePlan& pl, int k) {
     const int ln = fresh_lane();
-    const int pg = page_of(s);
-    const int tok0 = lo + s * PAGE;
-    const int nv = pg >= 0 ? min(PAGE, T - tok0) : 0;   // valid rows of the page
-    const uint8_t* page_ptr = reinterpret_cast<const uint8_t*>(kv) +
-                              (size_t)(pg >= 0 ? pg : 0) * PAGE * ROW_BYTES;
-    const i32x4 rs = buffer_rsrc(page_ptr, nv * ROW_BYTES);
-    const uint32_t buf = lds_base + (s & 1) * STAGE_BYTES;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {  // content: token t = w + 4k, lane -> chunk lane ^ f(t)
-      const int t = w + 4 * k;
-      dma16(buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t & 15)) << 4), rs);
-    }
-    // RoPE keys of tokens 8r .. 8r + 7 for r = w, w + 4: token 8 r + lane / 8,
-    // chunk (lane % 8) ^ f_R(token), and f_R = (4 r + lane / 16) mod 8 is the same for both
-    const uint32_t rope_lane = (ln >> 3) * ROW_BYTES + R * 2 +
-                               (((ln & 7) ^ ((4 * w + (ln >> 4)) & 7)) << 4);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int r = w + 4 * k;
-      dma16(buf + CONTENT_BYTES + r * 1024, r * 8 * ROW_BYTES + rope_lane, rs);
-    }
-    {  // alpha^k of the page: 64 * G floats, a quarter per wave
-      const float* ap = alpha_k + (size_t)(pg >= 0 ? pg : 0) * PAGE * groups;
-      const i32x4 ra = buffer_rsrc(ap, nv * groups * 4);
-      if (ln * 16 < alpha_bytes_per_wave)
-        dma16(buf + CONTENT_BYTES + ROPE_BYTES + w * alpha_bytes_per_wave,
-              w * alpha_bytes_per_wave + ln * 16, ra);
+    if (k < ST / 8) {
+      // content token t = w + 8k at t * ROW_BYTES; the lane's chunk is lane ^ f(t)
+      const int t = w + 8 * k;
+      dma16(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
+    } else if (k == ST / 8) {
+      // RoPE keys of tokens 4w .. 4w + 3: token 4 w + lane / 8, chunk (lane % 8) ^ f_R(token)
+      if (ln < 32) {
+        const int t = 4 * w + (ln >> 3);
+        dma16(pl.buf + CONTENT_BYTES + w * 512, t * ROW_BYTES + R * 2 + (((ln & 7) ^ swz_rope(t)) << 4), pl.rs);
+      }
+    } else {
+      // alpha^k of the stage: 32 * G floats, 16 G bytes per wave
+      if (ln < groups)
+        dma16(pl.buf + CONTENT_BYTES + ROPE_BYTES + 16 * groups * w, 16 * groups * w + ln * 16, pl.ra);
     }
   };
+  constexpr int LOADS = ST / 8 + 2;
+  auto issue = [&](int s) {
+    const StagePlan pl = plan(s);
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) load(pl, k);
+  };
 
-  f32x16 acc[R / 32];
+  f32x4 acc[R / 16];
   float m_ref = -INFINITY;   // reference of the exponent for this lane's head (logit units)
   float m_seen = -INFINITY;  // largest logit of this head seen so far
   float l_run = 0.f;         // this lane's share of the softmax denominator
   const float c2 = scale * kLog2e;  // logits -> log2 units
 
+  // restart flag: set by any wave whose logits outgrew the reference, read by
+  // all after the next barrier
+  volatile LDS_AS int* flag = (volatile LDS_AS int*)((LDS_AS uint8_t*)smem + FLAG_OFFSET);
+  if (tid == 0) *flag = 0;
+
   bool again;
   do {
     again = false;
 #pragma unroll
-    for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
+    for (int om = 0; om < R / 16; ++om) acc[om] = f32x4{};
     l_run = 0.f;
+    static_assert(NSTAGE == 4, "the prologue issues three stages");
     if (n_st > 0) issue(0);
     if (n_st > 1) issue(1);
+    if (n_st > 2) issue(2);
 
     for (int s = 0; s < n_st; ++s) {
-      if (s + 1 < n_st) {
-        asm volatile("s_waitcnt vmcnt(19)" ::: "memory");  // the next page's 19 loads may fly
+      // stage s has landed (its successors may still be in flight) and every
+      // wave is done with stage s - 1
+      const int ahead = min(n_st - 1 - s, NSTAGE - 2);
+      if (ahead >= 2) {
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      } else if (ahead == 1) {
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       __syncthreads();
-      const uint32_t stage_off = (s & 1) * STAGE_BYTES;
+      // the loads of stage s + 3 go into the buffer of stage s - 1
+      const bool ahead3 = s + NSTAGE - 1 < n_st;
+      StagePlan pl{};
+      if (ahead3) pl = plan(s + NSTAGE - 1);
+      const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
       const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
       const LDS_AS float* st_alpha = (const LDS_AS float*)(lds0 + stage_off + CONTENT_BYTES + ROPE_BYTES);
-      const int tok0 = lo + s * PAGE;
-      const bool page_ok = page_of(s) >= 0;
+      const int tok0 = lo + s * ST;
+      const bool page_ok = (vmask >> (s & 3)) & 1u;
       if (!page_ok) err = 1;
-      // rows r of this page with r < lim are visible to this wave
+      // rows r of this stage with r < lim are visible to this wave
       const int lim = page_ok ? hi_w - tok0 : 0;
       int overflow = 0;
 
+      if (!wave_active && ahead3) {
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k) load(pl, k);
+      }
       if (wave_active) {
-        // Per-lane LDS byte offsets inside the staged page.  The XOR swizzle only
-        // touches the low 4 bits of a chunk index, and a chunk index splits into
-        // disjoint bit fields, so every read is (per-lane base) XOR (constant)
-        // plus a compile-time offset above those bits (stage bases are multiples
-        // of 1024 and commute with the XORs):
-        //  QK row read, token 32 mt + l32, chunk 2 kk + hh:
-        //    [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8) + 32768 mt
-        //  RoPE row read, chunk 2 kk + hh (kk < 4):
-        //    [l32*128 + ((hh ^ f_R(l32)) << 4)] ^ (32 kk) + 4096 mt
-        //  PV transposed read: 16-lane group G = lane / 16 reads 4 rows
-        //  t0 = 4 (G / 2) + (lane % 16) / 4 of the step (and t0 + 8), latents
-        //  32 om + 16 (G % 2) + 4 (lane % 4) .. +3, i.e. chunk 4 om + c0 with
-        //  c0 = 2 (G % 2) + (lane % 4) / 2, byte 8 (lane % 2) of the chunk:
-        //    [t*1024 + 8 (lane % 2) + ((c0 ^ f(t)) << 4)] ^ (64 (om % 4)) + 256 (om / 4) + 1024 (16 ks + 32 mt)
-        uint32_t qk_b, rp_b, pv_a, pv_bb;
+        // Per-lane LDS byte offsets inside the stage.  The XOR swizzle only
+        // touches the low 4 bits of a chunk index, and a chunk index splits
+        // into disjoint bit fields, so every read is (per-lane base) XOR
+        // (constant) plus a compile-time offset above those bits (stage bases
+        // are multiples of 1024 and commute with the XORs):
+        //  QK row read, token 16 tt + l16, chunk 4 kk + q4:
+        //    [l16*1024 + ((q4 ^ f(l16)) << 4)] ^ (64 (kk % 4)) + 256 (kk / 4) + 1024 * 16 tt
+        //  RoPE row read, chunk 4 kk + q4 (kk < 2):
+        //    [l16*128 + ((q4 ^ f_R(l16)) << 4)] ^ (64 kk) + 128 * 16 tt
+        //  PV transposed read of latents 16 om .. +15, tokens 4 q4 + (0..3) and
+        //  + 16: row t = 4 q4 + l16 / 4, chunk 2 om + c1 with c1 = (l16 % 4) / 2,
+        //  byte 8 (l16 % 2) of the chunk:
+        //    [t*1024 + 8 (l16 % 2) + ((c1 ^ f(t)) << 4)] ^ (32 (om % 8)) + 256 (om / 8) [+ 1024 * 16]
+        uint32_t qk_b, rp_b, pv_b;
         {
           const int ln = fresh_lane();
-          const int lt = ln & 31, lh = ln >> 5;
-          qk_b = lt * 1024 + ((lh ^ swz(lt & 15)) << 4) + stage_off;
-          rp_b = lt * 128 + ((lh ^ swz_rope(lt)) << 4) + stage_off + CONTENT_BYTES;
-          const int G = ln >> 4, k16 = ln & 15;
-          const int t0 = 4 * (G >> 1) + (k16 >> 2);
-          const int c0 = 2 * (G & 1) + ((k16 & 3) >> 1);
-          const int inner = 8 * (k16 & 1);
-          pv_a = t0 * 1024 + inner + ((c0 ^ swz(t0)) << 4) + stage_off;
-          pv_bb = (t0 + 8) * 1024 + inner + ((c0 ^ swz(t0 + 8)) << 4) + stage_off;
+          const int lt = ln & 15, lq = ln >> 4;
+          const int t = 4 * lq + (lt >> 2);
+          qk_b = lt * 1024 + ((lq ^ swz(lt)) << 4) + stage_off;
+          rp_b = lt * 128 + ((lq ^ swz_rope(lt)) << 4) + stage_off + CONTENT_BYTES;
+          pv_b = t * 1024 + 8 * (lt & 1) + ((((lt & 3) >> 1) ^ swz(t)) << 4) + stage_off;
         }
+        // ---- QK for the 32 tokens (two 16-token tiles): content, alpha, RoPE ----
+        f32x4 sc[2] = {f32x4{}, f32x4{}};
+        {
+          // steps n = (k4, kh, tt) in that order; kk = 4 kh + k4
+          constexpr int NK = 4 * (R / 128) * 2;
+          bf16x8 abuf[QK_AHEAD];
+          const uint32_t base = opaque(qk_b);
+          auto rd = [&](int n) {
+            const int k4 = n >> 3, kh = (n >> 1) & 3, tt = n & 1;
+            return lds_read16(lds0 + (base ^ (64u * k4)) + 256 * kh + 1024 * 16 * tt);
+          };
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          // ---- QK for 32 tokens: content, alpha scaling, RoPE ----
-          // 32 reduction steps kk = 8 kh + k8, operands read QK_AHEAD steps ahead
-          f32x16 sc = f32x16{};
-          {
-            constexpr int NK = R / 16;
-            bf16x8 abuf[QK_AHEAD];
-            auto rd = [&](int n) {  // step n in issue order: k8 = n / 4, kh = n % 4
-              const int k8 = n >> 2, kh = n & 3;
-              return lds_read16(lds0 + (qk_b ^ (32u * k8)) + 256 * kh + 32768 * mt);
-            };
+          for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
 #pragma unroll
-            for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
+          for (int n = 0; n < NK; ++n) {
+            const bf16x8 a = abuf[n % QK_AHEAD];
+            if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
+            const int k4 = n >> 3, kh = (n >> 1) & 3, tt = n & 1;
+            sc[tt] = mfma(a, qb[4 * kh + k4], sc[tt]);
+            if (n % 5 == 2 && n / 5 < LOADS && ahead3) load(pl, n / 5);
+          }
+        }
+        if (USE_ALPHA) {
 #pragma unroll
-            for (int n = 0; n < NK; ++n) {
-              const bf16x8 a = abuf[n % QK_AHEAD];
-              if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
-              sc = mfma(a, qb[8 * (n & 3) + (n >> 2)], sc);
+          for (int tt = 0; tt < 2; ++tt) {
+            const int t = 16 * tt + 4 * q4;  // rows of the four registers
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[tt][j] *= aq * st_alpha[(t + j) * groups + g];
+          }
+        }
+        {
+          const uint32_t base = opaque(rp_b);
+#pragma unroll
+          for (int kk = 0; kk < DR / 32; ++kk) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const bf16x8 a = lds_read16(lds0 + (base ^ (64u * kk)) + 128 * 16 * tt);
+              sc[tt] = mfma(a, qrb[kk], sc[tt]);
             }
           }
-          if (USE_ALPHA) {
+        }
+        // ---- mask rows past the visible end (tail page, causal window, bad page)
+        if (lim < ST) {
 #pragma unroll
-            for (int jg = 0; jg < 4; ++jg) {
-              const int t = 32 * mt + 8 * jg + 4 * hh;  // rows of registers 4 jg .. 4 jg + 3
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) sc[4 * jg + e] *= aq * st_alpha[(t + e) * groups + g];
-            }
-          }
+            for (int j = 0; j < 4; ++j)
+              if (16 * tt + 4 * q4 + j >= lim) sc[tt][j] = -INFINITY;
+        }
+        // ---- probabilities against the fixed reference ----
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = head_max(mx);
+        m_seen = fmaxf(m_seen, mx);
+        if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
+        if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
+        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+        bf16x8 pb;  // P^T as the B operand: elements 0-3 tile 0, 4-7 tile 1
 #pragma unroll
-          for (int kk = 0; kk < DR / 16; ++kk) {
-            const bf16x8 a = lds_read16(lds0 + (rp_b ^ (32u * kk)) + 4096 * mt);
-            sc = mfma(a, qrb[kk], sc);
-          }
-          // ---- mask rows past the visible end (tail page, causal window, bad page)
-          if (lim < 32 * mt + 32) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (32 * mt + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[j] = -INFINITY;
-          }
-          // ---- probabilities against the fixed reference ----
-          float mx = sc[0];
-#pragma unroll
-          for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
-          mx = pair_max(mx);
-          m_seen = fmaxf(m_seen, mx);
-          if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
-          if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
-          const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-          bf16x8 pb[2];  // P^T of the two 16-token steps
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const __bf16 pr = static_cast<__bf16>(exp2f(fmaf(sc[j], c2, -mc)));
-            pb[j >> 3][j & 7] = pr;
+          for (int j = 0; j < 4; ++j) {
+            const __bf16 pr = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[tt][j], c2, -mc)));
+            pb[4 * tt + j] = pr;
             l_run += static_cast<float>(pr);
           }
-          // ---- PV: O^T[512 x 32] += C^T[512 x 32 tok] . P^T ----
-          // 32 products (o4, ks, oh) in that order, operands read PV_AHEAD ahead
-          {
-            constexpr int NP = 4 * 2 * (R / 128);
-            bf16x8 abuf[PV_AHEAD];
-            auto rd = [&](int n) {
-              const int o4 = n >> 3, ks = (n >> 2) & 1, oh = n & 3;
-              const int imm = 256 * oh + 1024 * (16 * ks + 32 * mt);
-              const bf16x4 lo4 = lds_read_tr(lds0 + (pv_a ^ (64u * o4)) + imm);
-              const bf16x4 hi4 = lds_read_tr(lds0 + (pv_bb ^ (64u * o4)) + imm);
-              return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
+        // ---- PV: O^T[512 x 16] += C^T[512 x 32 tok] . P^T ----
+        {
+          // products n = (o8, oh) in that order; om = 8 oh + o8
+          constexpr int NP = 8 * (R / 128);
+          bf16x8 abuf[PV_AHEAD];
+          const uint32_t base = opaque(pv_b);
+          auto rd = [&](int n) {
+            const int o8 = n >> 2, oh = n & 3;
+            const uint32_t a_off = (base ^ (32u * o8)) + 256 * oh;
+            const bf16x4 lo4 = lds_read_tr(lds0 + a_off);
+            const bf16x4 hi4 = lds_read_tr(lds0 + a_off + 16 * 1024);
+            return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          };
 #pragma unroll
-            for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
+          for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
 #pragma unroll
-            for (int n = 0; n < NP; ++n) {
-              const bf16x8 a = abuf[n % PV_AHEAD];
-              if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
-              mfma_acc(acc[4 * (n & 3) + (n >> 3)], a, pb[(n >> 2) & 1]);
-            }
+          for (int n = 0; n < NP; ++n) {
+            const bf16x8 a = abuf[n % PV_AHEAD];
+            if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
+            acc[8 * (n & 3) + (n >> 2)] = mfma(a, pb, acc[8 * (n & 3) + (n >> 2)]);
           }
         }
       }
-      // all waves done with this buffer; did any head outgrow its reference?
-      if (__syncthreads_or(overflow)) {
+      // did any head outgrow its reference?
+      if (__builtin_amdgcn_ballot_w64(overflow != 0)) *flag = 1;
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(*flag)) {
         again = true;
         break;
       }
-      if (s + 2 < n_st) issue(s + 2);
     }
     if (again) {
-      // restart the split with the largest logit seen as the reference
+      // restart the split with the largest logit seen as the reference; every
+      // wave has read the flag before it is cleared
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (tid == 0) *flag = 0;
       m_ref = m_seen;
     }
   } while (again);
 
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // an empty split never waited for its loads
   // ---- epilogue: o_p = acc / l, lse_p = scale * m_ref + ln l ----
-  wait_acc_results();
   if (wave_active) {
-    const float l_tot = pair_sum(l_run);
+    const float l_tot = head_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* out = o_part + (my_row * num_splits + p) * R;
+    const size_t row_e = ((size_t)b * s_q + i) * heads + h0 + (fresh_lane() & 15);
+    float* out = o_part + (row_e * num_splits + p) * R;
 #pragma unroll
-    for (int om = 0; om < R / 32; ++om) {
+    for (int om = 0; om < R / 16; ++om) {
+      f32x4 v;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[om][4 * jg + e] * inv;
-        *reinterpret_cast<f32x4*>(out + 32 * om + 8 * jg + 4 * hh) = v;
-      }
+      for (int j = 0; j < 4; ++j) v[j] = acc[om][j] * inv;
+      *reinterpret_cast<f32x4*>(out + 16 * om + 4 * q4) = v;
     }
-    if (hh == 0) {
-      lse_part[my_row * num_splits + p] =
+    if (q4 == 0) {
+      lse_part[row_e * num_splits + p] =
           l_tot > 0.f ? m_ref * scale + log2f(l_tot) * kLn2 : -INFINITY;
     }
   }
