@@ -95,7 +95,10 @@ QKN_API const char* qkn_status_string(int status);
 QKN_API int qkn_mla_check_dims(const qkn_mla_dims* dims);
 
 /* Which decode kernel qkn_mla_decode would launch for these sizes and flags:
- * 1 = matrix-core (MFMA) kernel, 0 = generic kernel, < 0 = a qkn_status error. */
+ * 1 = matrix-core (MFMA) kernel, 0 = generic kernel, < 0 = a qkn_status error.
+ * The matrix-core kernel takes a bfloat16 cache with r = 512, d_R = 64, at most
+ * 8 KV groups and a multiple of 32 heads per group; every other valid size
+ * runs on the generic kernel. */
 QKN_API int qkn_mla_decode_kernel_kind(const qkn_mla_dims* dims, int32_t num_splits, uint32_t flags);
 
 /*

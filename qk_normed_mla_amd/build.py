@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
+    # MFMAs the compiler emits write VGPRs; the decode kernel's latent
+    # accumulator is placed in the AGPR file explicitly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

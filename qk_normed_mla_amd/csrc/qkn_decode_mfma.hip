@@ -1,5 +1,5 @@
 // Matrix-core split-KV decode for gfx950 (MI355X): bf16 latent cache, r = 512,
-// d_R = 64, heads per KV group a multiple of 16.
+// d_R = 64, heads per KV group a multiple of 32.
 //
 // What it computes (QK-Normed MLA summary, "Metodologia", decode-logit
 // equation; the RoPE dot of the shared RoPE key from the MQA-absorbed path of
@@ -13,42 +13,46 @@
 // the 4 bytes per token and group of the scalar cache.
 //
 // Work decomposition
-//   one workgroup (8 waves, 2 per SIMD) per (sequence b, split p, block of 128
-//   query rows); wave w owns 16 query rows = 16 heads of one query token, all
-//   in one KV group.  Every token of the split is read from HBM once and
-//   shared by the 8 waves through LDS.  A wave keeps q~ (72 registers) and its
-//   16 x 512 latent accumulator (128 registers) for the whole kernel, within
-//   the 256 registers that let two waves share a SIMD, so one wave's softmax
-//   overlaps the other's MFMAs.
+//   one workgroup (4 waves, one per SIMD) per (sequence b, split p, block of
+//   128 query rows); wave w owns 32 query rows = 32 heads of one query token,
+//   all in one KV group.  Every token of the split is read from HBM once and
+//   shared by the 4 waves through LDS.  With 32 heads per wave every latent
+//   row read from LDS feeds 32 heads, which keeps the LDS traffic of a stage
+//   (272 KB per CU) below what the matrix cores need in time.  A wave keeps
+//   q~ and q^R (144 VGPRs) for the whole kernel and its 32 x 512 latent
+//   accumulator in the 256 AGPRs.
 //
 // Per 32-token stage (half a page):
 //   HBM -> LDS   LDS-DMA loads of 16 B per lane (buffer_load ... lds) into a
-//                ring of 4 stage buffers, 3 stages in flight, so that about
-//                115 KB per CU is always on its way from HBM.  The buffer
-//                descriptor of a stage ends at its last valid token, so a
-//                partial page reads zeros beyond it; an invalid page entry
-//                reads zeros throughout.
-//   QK           S^T[16 tok x 16 heads] = C[16 x 512] . q~^T  (v_mfma_f32_16x16x32_bf16,
-//                A = latent rows from LDS, B = q~ in registers for the whole
-//                kernel), then S *= alpha^q alpha^k, then += K^R . q^R^T.
+//                ring of 4 stage buffers: while stage s is multiplied, stage
+//                s - 1 is still read by PV and stages s + 1, s + 2 are on their
+//                way.  The buffer descriptor of a stage ends at its last valid
+//                token, so a partial page reads zeros beyond it; an invalid
+//                page entry reads zeros throughout.  The loads are spread over
+//                the QK products.
+//   QK           S^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
+//                A = latent rows from LDS, B = q~ in registers), then
+//                S *= alpha^q alpha^k, then += K^R . q^R^T.
 //   softmax      base 2 against a per-head reference fixed at the first
 //                visible tokens of the split, so the accumulator is never
 //                rescaled inside the loop.  QK-norm bounds the logits, so the
 //                probabilities stay far below the 2^96 headroom allowed; should
 //                a later logit exceed it, the workgroup restarts the split with
 //                the larger reference (exact; never seen with normalised
-//                logits).  A head's tokens sit in lanes l, l^16, l^32, l^48.
-//   PV           O^T[512 x 16 heads] += C^T . P^T over the 32 tokens, the C^T
-//                operand read with ds_read_b64_tr_b16 straight from the
-//                row-major stage in LDS; the token order inside the step
-//                follows the register layout of two S^T tiles (both operands
-//                use the same permutation of the reduction index, which leaves
-//                the sum unchanged).
+//                logits).  A head's 32 tokens sit in lanes l and l ^ 32.
+//   PV           O^T[512 x 32 heads] += C^T . P^T, the C^T operand read with
+//                ds_read_b64_tr_b16 straight from the row-major stage in LDS;
+//                the token order inside a 16-token step follows the register
+//                layout of the S^T tile (both operands use the same
+//                permutation of the reduction index, which leaves the sum
+//                unchanged).  PV of stage s - 1 is issued together with the
+//                softmax of stage s, so the vector ALU work of one stage runs
+//                under the matrix products of the previous one.
 // LDS layout of a stage (bytes): content [32][1024] with the 16-byte chunk c of
 // token t stored at chunk position c ^ f(t) (f below), RoPE keys [32][128] with
-// chunk c of token t at c ^ ((t >> 1) & 7), then alpha^k [32][G].  The
-// swizzles spread the row reads of QK and the transposed reads of PV over
-// the LDS banks.
+// chunk c of token t at c ^ ((t >> 1) & 7), then alpha^k [G][32].  The
+// swizzles spread the row reads of QK and the transposed reads of PV over the
+// LDS banks.
 #include <math.h>
 
 #include "qkn_internal.h"
@@ -58,7 +62,10 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -70,14 +77,15 @@ constexpr int NSTAGE = 4;                 // stage buffers in LDS
 constexpr int ROW_BYTES = (R + DR) * 2;   // 1152
 constexpr int CONTENT_BYTES = ST * R * 2;         // 32768
 constexpr int ROPE_BYTES = ST * DR * 2;           // 4096
-constexpr int ALPHA_BYTES = ST * 16 * 4;          // room for G <= 16
-constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 38912
+constexpr int kMaxGroups = 8;
+constexpr int ALPHA_BYTES = ST * kMaxGroups * 4;  // 1024
+constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 37888
 constexpr int FLAG_OFFSET = NSTAGE * STAGE_BYTES; // the workgroup's restart flag
-constexpr int LDS_BYTES = FLAG_OFFSET + 16;       // 155664
-constexpr int WAVES = 8;
-constexpr int HEADS_PER_WAVE = 16;
+constexpr int LDS_BYTES = FLAG_OFFSET + 16;       // 151568
+constexpr int WAVES = 4;
+constexpr int HEADS_PER_WAVE = 32;
 constexpr int ROWS_PER_WG = WAVES * HEADS_PER_WAVE;  // 128
-constexpr int kMaxGroups = 16;
+constexpr int LOADS = ST / WAVES + 2;             // per wave and stage: 8 content, RoPE, alpha
 constexpr int QK_AHEAD = 3;                      // LDS reads in flight ahead of the MFMAs
 constexpr int PV_AHEAD = 3;
 constexpr float kMaxExp2 = 96.0f;                 // headroom of p = 2^(y - ref), log2 units
@@ -85,15 +93,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // content chunk position of chunk c of token t: c ^ f(t mod 16), f the
-// linear map over GF(2)^4 with f(1) = 2, f(2) = 15, f(4) = 8, f(8) = 9.
-// Measured on gfx950: LDS b128 reads run at full rate when lanes 0-7 of a
-// 16-lane group stay in one 128-byte half of the 64 banks and lanes 8-15 in
-// the other, which the QK row read (16 tokens x one chunk) meets when f's top
-// bit follows t's top bit; among such maps this one also keeps the
-// transposed 8-byte reads of PV (4 tokens x 2 chunks per 16 lanes) near
-// their best rate.  A search over all invertible maps picked it.
+// linear map over GF(2)^4 with f(1) = 9, f(2) = 5, f(4) = 2, f(8) = 6.  Chosen
+// by measuring, on gfx950, every invertible map for the two read patterns of
+// this kernel (32 rows x one chunk for QK, 8 rows x 4 chunks of transposed
+// 8-byte reads for PV); this one runs both near the best rate seen.
 __device__ __forceinline__ int swz(int t) {
-  return static_cast<int>((0xce3146b957a8df20ull >> (4 * (t & 15))) & 15);
+  return static_cast<int>((0x81d4a3f6e7b2c590ull >> (4 * (t & 15))) & 15);
 }
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
 
@@ -113,10 +118,24 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // range check covers (reads at or past the descriptor size return zeros).
 // Issued through asm so that the compiler does not hold every LDS read until
 // all DMA in flight has landed; completion is awaited explicitly (vmcnt)
-// before the barrier that publishes a page.  The s_nop covers the wait states
-// the hardware needs after M0 and descriptor SGPRs are written.
+// before the barrier that publishes a stage.  Wait states: one after the
+// scalar write of M0 (s_nop 0); the first load through a descriptor also
+// covers the five a vector memory instruction needs after a vector
+// instruction (v_readfirstlane) wrote one of its SGPRs (s_nop 4).
+template <bool FIRST_USE>
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  if (FIRST_USE) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+  } else {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+  }
+}
+
+// 4 bytes per lane from rsrc + voff to LDS (M0 + 4 * lane); wait states as above
+__device__ __forceinline__ void dma4_first(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
@@ -137,33 +156,35 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
-// the value, hidden from the optimiser so that it recomputes what derives from it
-// instead of keeping those results live in registers
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// PV product into an accumulator tile kept in the AGPR file.  Issued through
+// asm so that the compiler keeps the 256 accumulator registers of a wave there
+// and the VGPRs free for the operands.  Hazards the compiler cannot see
+// through asm: 2 wait states before the MFMA reads operands written by the
+// vector ALU (s_nop 1), and wait_acc_results() before anything reads the
+// accumulator back.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states between an MFMA writing registers and a vector instruction
+// reading them (covers the longest MFMA; 3 x 8)
+__device__ __forceinline__ void wait_acc_results() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-// max / sum over the four lanes l, l^16, l^32, l^48 that hold one head.
-// v_permlane16_swap / v_permlane32_swap with both operands v return the two
-// halves that pair lane l with lane l^16 (l^32) in every lane.
-__device__ __forceinline__ float xor16_pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_pair_max(float v) {
+// max / sum over the two lanes l, l ^ 32 that hold one head.  With both
+// operands v, v_permlane32_swap returns the two halves of the wave, which pair
+// lane l with lane l ^ 32 in every lane.
+__device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float head_max(float v) { return xor32_pair_max(xor16_pair_max(v)); }
-__device__ __forceinline__ float head_sum(float v) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -190,8 +211,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int l16 = lane & 15;
-  const int q4 = lane >> 4;   // which 8-wide slice of a 32-long reduction step
+  const int l32 = lane & 31;  // head within the wave
+  const int hh = lane >> 5;   // which 8-wide half of a 16-long reduction step
   int err = 0;
 
   int T = seq_lens[b];
@@ -205,7 +226,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int first_page = lo / PAGE;  // lo is a multiple of the page size
   const int n_st = hi > lo ? (hi - lo + ST - 1) / ST : 0;
 
-  // this wave's 16 query rows: query token i, heads h0 .. h0 + 15, group g
+  // this wave's 32 query rows: query token i, heads h0 .. h0 + 31, group g
   const int rows_total = s_q * heads;
   const int row0 = rb * ROWS_PER_WG + w * HEADS_PER_WAVE;
   const bool wave_active = row0 < rows_total;
@@ -214,7 +235,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int g = h0 / (heads / groups);
   const int hi_w = min(hi, T - s_q + i + 1);  // visible end for this query token
   // row of this lane's head (an idle wave uses row 0 and discards its results)
-  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l16;
+  const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l32;
 
   // Page-table window: lane j of every wave holds the entry of split page
   // wbase + j (64 pages, 4096 tokens), so a stage finds its page with one
@@ -227,16 +248,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   };
   load_window(0);
 
-  // q~ as the B operand of QK: lane holds q~[head l16][32 kk + 8 q4 .. +8]
-  bf16x8 qb[R / 32];
-  bf16x8 qrb[DR / 32];
+  // q~ and q^R as the B operand of QK: lane holds q[head l32][16 kk + 8 hh .. +8]
+  bf16x8 qb[R / 16];
+  bf16x8 qrb[DR / 16];
   {
-    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + q4;
+    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + hh;
 #pragma unroll
-    for (int kk = 0; kk < R / 32; ++kk) qb[kk] = qt[4 * kk];
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + q4;
+    for (int kk = 0; kk < R / 16; ++kk) qb[kk] = qt[2 * kk];
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + hh;
 #pragma unroll
-    for (int kk = 0; kk < DR / 32; ++kk) qrb[kk] = qr[4 * kk];
+    for (int kk = 0; kk < DR / 16; ++kk) qrb[kk] = qr[2 * kk];
   }
   const float aq = USE_ALPHA ? alpha_q[my_row] : 1.f;
   // query operands and page window in registers before any page load is
@@ -244,67 +265,82 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS uint8_t*)smem));
-
-  // validity of the pages of the stages in flight, bit s mod 4 (uniform)
+  // validity of the pages of the stages in the ring, bit s mod 4 (uniform)
   uint32_t vmask = 0;
 
-  // The 6 loads of this wave for stage s (tokens lo + 32 s ..) into buffer
-  // s mod 4: 4 content rows, a quarter of the RoPE block on lanes 0-31, and an
-  // eighth of alpha^k on lanes 0 .. G-1 (lane 0 always takes part, so every
-  // wave issues all 6 and the vmcnt bookkeeping holds).  plan() looks the page
-  // up and builds the descriptors; load(k) issues load k.  Inside the page
-  // loop the loads are spread over the QK products, so the address units work
-  // through them while the matrix cores run.
+  // The 10 loads of this wave for stage s (tokens lo + 32 s ..) into buffer
+  // s mod 4: 8 content rows, a quarter of the RoPE block, and a quarter of
+  // alpha^k on lanes 0 .. 8G-1 (lane 0 always takes part, so every wave
+  // issues all 10 and the vmcnt bookkeeping holds).  plan() looks the page up
+  // and builds the descriptors; load(k) issues load k.
   struct StagePlan {
     i32x4 rs, ra;  // KV rows of the stage, alpha^k rows of the stage
     uint32_t buf;  // LDS address of the stage buffer
   };
   auto plan = [&](int s) {
     const int rel = s >> 1;  // page of the split
+    if (s >= n_st) {
+      // no such stage: its loads read nothing (size 0) and write zeros into
+      // a buffer nobody reads, which keeps the load count of every stage the same
+      StagePlan pl;
+      pl.rs = buffer_rsrc(kv, 0);
+      pl.ra = buffer_rsrc(alpha_k, 0);
+      pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
+      asm volatile("" : "+s"(pl.buf));
+      return pl;
+    }
     if (rel < wbase || rel >= wbase + 64) {  // uniform; once per 64 pages
       wbase = rel & ~63;
       load_window(wbase);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // a wait the compiler sees, so that it adds none of its own at every
+      // later use of the window (which would also wait for the page loads)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
     int pg = __builtin_amdgcn_readlane(pwin, rel - wbase);
     pg = (pg >= 0 && pg < num_pages) ? pg : -1;
     vmask = (vmask & ~(1u << (s & 3))) | ((pg >= 0 ? 1u : 0u) << (s & 3));
     const int tok0 = lo + s * ST;
     const int nv = pg >= 0 ? min(ST, T - tok0) : 0;   // valid rows of the stage
-    const size_t row0 = (size_t)(pg >= 0 ? pg : 0) * PAGE + (s & 1) * ST;  // cache row
+    const size_t row0s = (size_t)(pg >= 0 ? pg : 0) * PAGE + (s & 1) * ST;  // cache row
     StagePlan pl;
-    pl.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0 * ROW_BYTES, nv * ROW_BYTES);
-    pl.ra = buffer_rsrc(alpha_k + row0 * groups, nv * groups * 4);
+    pl.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0s * ROW_BYTES, nv * ROW_BYTES);
+    pl.ra = buffer_rsrc(alpha_k + row0s * groups, nv * groups * 4);
     pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
     asm volatile("" : "+s"(pl.buf));  // keep the per-load LDS addresses out of loop-invariant registers
     return pl;
   };
   auto load = [&](const StagePlan& pl, int k) {
     const int ln = fresh_lane();
-    if (k < ST / 8) {
-      // content token t = w + 8k at t * ROW_BYTES; the lane's chunk is lane ^ f(t)
-      const int t = w + 8 * k;
-      dma16(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
-    } else if (k == ST / 8) {
-      // RoPE keys of tokens 4w .. 4w + 3: token 4 w + lane / 8, chunk (lane % 8) ^ f_R(token)
-      if (ln < 32) {
-        const int t = 4 * w + (ln >> 3);
-        dma16(pl.buf + CONTENT_BYTES + w * 512, t * ROW_BYTES + R * 2 + (((ln & 7) ^ swz_rope(t)) << 4), pl.rs);
+    if (k < ST / WAVES) {
+      // content token t = w + 4k at t * ROW_BYTES; the lane's chunk is lane ^ f(t)
+      const int t = w + WAVES * k;
+      if (k == 0) {
+        dma16<true>(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
+      } else {
+        dma16<false>(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
       }
+    } else if (k == ST / WAVES) {
+      // RoPE keys of tokens 8w .. 8w + 7: token 8 w + lane / 8, chunk (lane % 8) ^ f_R(token)
+      const int t = 8 * w + (ln >> 3);
+      dma16<false>(pl.buf + CONTENT_BYTES + w * 1024, t * ROW_BYTES + R * 2 + (((ln & 7) ^ swz_rope(t)) << 4), pl.rs);
     } else {
-      // alpha^k of the stage: 32 * G floats, 16 G bytes per wave
-      if (ln < groups)
-        dma16(pl.buf + CONTENT_BYTES + ROPE_BYTES + 16 * groups * w, 16 * groups * w + ln * 16, pl.ra);
+      // alpha^k of the stage, transposed to [G][32 tokens] on the way: slot
+      // i = g * 32 + t of the 32 G floats takes element (t, g) of the rows;
+      // wave w fills slots 8 G w .. 8 G w + 8 G - 1, one per lane
+      if (ln < 8 * groups) {
+        const int i = 8 * groups * w + ln;
+        dma4_first(pl.buf + CONTENT_BYTES + ROPE_BYTES + 32 * groups * w,
+                   ((i & 31) * groups + (i >> 5)) * 4, pl.ra);
+      }
     }
   };
-  constexpr int LOADS = ST / 8 + 2;
   auto issue = [&](int s) {
     const StagePlan pl = plan(s);
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) load(pl, k);
   };
 
-  f32x4 acc[R / 16];
+  f32x16 acc[R / 32];
   float m_ref = -INFINITY;   // reference of the exponent for this lane's head (logit units)
   float m_seen = -INFINITY;  // largest logit of this head seen so far
   float l_run = 0.f;         // this lane's share of the softmax denominator
@@ -315,161 +351,193 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   volatile LDS_AS int* flag = (volatile LDS_AS int*)((LDS_AS uint8_t*)smem + FLAG_OFFSET);
   if (tid == 0) *flag = 0;
 
+  const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
+
+  // PV of stage s with the probabilities pb (token order of the S^T tile):
+  // O^T[512 x 32] += C^T[512 x 32 tok] . P^T over two 16-token steps.
+  // Transposed read of latents 32 om .. +31, tokens 16 ks + 4 hh + (0..3)
+  // [+ 8]: within a 16-lane group G, row t = 4 hh + l16 / 4, chunk 4 om + 2 G +
+  // (l16 % 4) / 2, byte 8 (l16 % 2):
+  //   [t*1024 + 8 (l16 % 2) + ((c_lo ^ f(t)) << 4)] ^ (64 (om % 4)) + 256 (om / 4) + 16384 ks
+  // with c_lo = 2 G + (l16 % 4) / 2; the + 8 rows use their own base.
+  // fill(n) runs after the n-th product: vector ALU work that needs no matrix
+  // result of this PV step, issued while the matrix core works on it
+  auto pv_stage = [&](int s, const bf16x8 (&pb)[2], auto&& fill) {
+    const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
+    // the four XOR variants of both bases, so that every read below is a
+    // register plus an immediate (stage offsets leave bits 5-9 alone)
+    uint32_t xb0[4], xb1[4];
+    {
+      const int ln = fresh_lane();
+      const int l16 = ln & 15, G = (ln >> 4) & 1, h = ln >> 5;
+      const int t = 4 * h + (l16 >> 2);
+      const int c_lo = 2 * G + ((l16 & 3) >> 1);
+      const uint32_t b0 = t * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t)) << 4) + stage_off;
+      const uint32_t b1 = (t + 8) * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t + 8)) << 4) + stage_off;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xb0[j] = b0 ^ (64u * j);
+        xb1[j] = b1 ^ (64u * j);
+      }
+    }
+    // products n = (ks, om) in that order
+    constexpr int NP = 2 * (R / 32);
+    bf16x8 abuf[PV_AHEAD];
+    auto rd = [&](int n) {
+      const int ks = n / (R / 32), om = n % (R / 32);
+      const uint32_t off = 256 * (om >> 2) + 16384 * ks;
+      const bf16x4 lo4 = lds_read_tr(lds0 + xb0[om & 3] + off);
+      const bf16x4 hi4 = lds_read_tr(lds0 + xb1[om & 3] + off);
+      return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+#pragma unroll
+    for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      const bf16x8 a = abuf[n % PV_AHEAD];
+      if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
+      mfma_acc(acc[n % (R / 32)], a, pb[n / (R / 32)]);
+      fill(n);
+    }
+  };
+
+  // PV of "stage -1" reads buffer 3 with zero probabilities: clear that
+  // buffer once so that it holds finite values (later it only ever holds
+  // cache rows or zeros)
+  {
+    const f32x4 z = {};
+    for (int e = tid; e < CONTENT_BYTES / 16; e += 64 * WAVES)
+      *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)smem + 3 * STAGE_BYTES + 16 * e) = z;
+  }
+
   bool again;
   do {
     again = false;
 #pragma unroll
-    for (int om = 0; om < R / 16; ++om) acc[om] = f32x4{};
+    for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
     l_run = 0.f;
-    static_assert(NSTAGE == 4, "the prologue issues three stages");
-    if (n_st > 0) issue(0);
-    if (n_st > 1) issue(1);
-    if (n_st > 2) issue(2);
+    issue(0);
+    issue(1);
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage 0 has landed
+    __syncthreads();
+    bf16x8 pprev[2] = {};  // probabilities of the previous stage
 
-    for (int s = 0; s < n_st; ++s) {
-      // stage s has landed (its successors may still be in flight) and every
-      // wave is done with stage s - 1
-      const int ahead = min(n_st - 1 - s, NSTAGE - 2);
-      if (ahead >= 2) {
-        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      } else if (ahead == 1) {
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();
-      // the loads of stage s + 3 go into the buffer of stage s - 1
-      const bool ahead3 = s + NSTAGE - 1 < n_st;
-      StagePlan pl{};
-      if (ahead3) pl = plan(s + NSTAGE - 1);
+    // iteration s: QK and softmax of stage s (s < n_st) and PV of stage s - 1;
+    // it ends with the one barrier of the iteration, after which stage s + 1
+    // is in LDS, every wave is done with stage s - 1, and the restart flag
+    // of stage s is visible
+    for (int s = 0; s <= n_st; ++s) {
+      const bool has_qk = s < n_st;
+      // the loads of stage s + 2 go into the buffer of stage s - 2
+      const StagePlan pl = plan(s + 2);
       const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
-      const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
       const LDS_AS float* st_alpha = (const LDS_AS float*)(lds0 + stage_off + CONTENT_BYTES + ROPE_BYTES);
       const int tok0 = lo + s * ST;
       const bool page_ok = (vmask >> (s & 3)) & 1u;
-      if (!page_ok) err = 1;
+      if (has_qk && !page_ok) err = 1;
       // rows r of this stage with r < lim are visible to this wave
-      const int lim = page_ok ? hi_w - tok0 : 0;
+      const int lim = (has_qk && page_ok) ? hi_w - tok0 : 0;
       int overflow = 0;
 
-      if (!wave_active && ahead3) {
+      if (!wave_active) {
 #pragma unroll
         for (int k = 0; k < LOADS; ++k) load(pl, k);
       }
       if (wave_active) {
-        // Per-lane LDS byte offsets inside the stage.  The XOR swizzle only
-        // touches the low 4 bits of a chunk index, and a chunk index splits
-        // into disjoint bit fields, so every read is (per-lane base) XOR
-        // (constant) plus a compile-time offset above those bits (stage bases
-        // are multiples of 1024 and commute with the XORs):
-        //  QK row read, token 16 tt + l16, chunk 4 kk + q4:
-        //    [l16*1024 + ((q4 ^ f(l16)) << 4)] ^ (64 (kk % 4)) + 256 (kk / 4) + 1024 * 16 tt
-        //  RoPE row read, chunk 4 kk + q4 (kk < 2):
-        //    [l16*128 + ((q4 ^ f_R(l16)) << 4)] ^ (64 kk) + 128 * 16 tt
-        //  PV transposed read of latents 16 om .. +15, tokens 4 q4 + (0..3) and
-        //  + 16: row t = 4 q4 + l16 / 4, chunk 2 om + c1 with c1 = (l16 % 4) / 2,
-        //  byte 8 (l16 % 2) of the chunk:
-        //    [t*1024 + 8 (l16 % 2) + ((c1 ^ f(t)) << 4)] ^ (32 (om % 8)) + 256 (om / 8) [+ 1024 * 16]
-        uint32_t qk_b, rp_b, pv_b;
-        {
-          const int ln = fresh_lane();
-          const int lt = ln & 15, lq = ln >> 4;
-          const int t = 4 * lq + (lt >> 2);
-          qk_b = lt * 1024 + ((lq ^ swz(lt)) << 4) + stage_off;
-          rp_b = lt * 128 + ((lq ^ swz_rope(lt)) << 4) + stage_off + CONTENT_BYTES;
-          pv_b = t * 1024 + 8 * (lt & 1) + ((((lt & 3) >> 1) ^ swz(t)) << 4) + stage_off;
-        }
-        // ---- QK for the 32 tokens (two 16-token tiles): content, alpha, RoPE ----
-        f32x4 sc[2] = {f32x4{}, f32x4{}};
-        {
-          // steps n = (k4, kh, tt) in that order; kk = 4 kh + k4
-          constexpr int NK = 4 * (R / 128) * 2;
-          bf16x8 abuf[QK_AHEAD];
-          const uint32_t base = opaque(qk_b);
-          auto rd = [&](int n) {
-            const int k4 = n >> 3, kh = (n >> 1) & 3, tt = n & 1;
-            return lds_read16(lds0 + (base ^ (64u * k4)) + 256 * kh + 1024 * 16 * tt);
-          };
+        f32x16 sc = {};
+        if (has_qk) {
+          // ---- QK: S^T[32 tok x 32 heads] over the 512 latents, then alpha, then RoPE ----
+          // Row read of token l32, chunk 2 kk + hh:
+          //   [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8)
+          // RoPE row read, chunk 2 kk + hh (kk < 4):
+          //   [l32*128 + ((hh ^ f_R(l32)) << 4)] ^ (32 kk)
+          uint32_t qx[8], rx[DR / 16];
+          {
+            const int ln = fresh_lane();
+            const int t = ln & 31, h = ln >> 5;
+            const uint32_t qk_b = t * 1024 + ((h ^ swz(t)) << 4) + stage_off;
+            const uint32_t rp_b = t * 128 + ((h ^ swz_rope(t)) << 4) + stage_off + CONTENT_BYTES;
 #pragma unroll
-          for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
+            for (int j = 0; j < 8; ++j) qx[j] = qk_b ^ (32u * j);
 #pragma unroll
-          for (int n = 0; n < NK; ++n) {
-            const bf16x8 a = abuf[n % QK_AHEAD];
-            if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
-            const int k4 = n >> 3, kh = (n >> 1) & 3, tt = n & 1;
-            sc[tt] = mfma(a, qb[4 * kh + k4], sc[tt]);
-            if (n % 5 == 2 && n / 5 < LOADS && ahead3) load(pl, n / 5);
+            for (int j = 0; j < DR / 16; ++j) rx[j] = rp_b ^ (32u * j);
           }
-        }
-        if (USE_ALPHA) {
+          // alpha^k of this lane's 16 tokens (4 runs of 4): prefetched with the
+          // RoPE rows ahead of the content products
+          f32x4 ak[4];
+          bf16x8 rope_a[DR / 16];
+          if (USE_ALPHA) {
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int t = 16 * tt + 4 * q4;  // rows of the four registers
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[tt][j] *= aq * st_alpha[(t + j) * groups + g];
+            for (int j = 0; j < 4; ++j) ak[j] = *(const LDS_AS f32x4*)(st_alpha + g * ST + 8 * j + 4 * hh);
           }
-        }
-        {
-          const uint32_t base = opaque(rp_b);
 #pragma unroll
-          for (int kk = 0; kk < DR / 32; ++kk) {
+          for (int kk = 0; kk < DR / 16; ++kk) rope_a[kk] = lds_read16(lds0 + rx[kk]);
+          {
+            constexpr int NK = R / 16;
+            bf16x8 abuf[QK_AHEAD];
+            auto rd = [&](int n) { return lds_read16(lds0 + qx[n & 7] + 256 * (n >> 3)); };
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              const bf16x8 a = lds_read16(lds0 + (base ^ (64u * kk)) + 128 * 16 * tt);
-              sc[tt] = mfma(a, qrb[kk], sc[tt]);
+            for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
+#pragma unroll
+            for (int n = 0; n < NK; ++n) {
+              const bf16x8 a = abuf[n % QK_AHEAD];
+              if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
+              sc = mfma(a, qb[n], sc);
+              if (n % 3 == 1 && n / 3 < LOADS) load(pl, n / 3);
             }
           }
-        }
-        // ---- mask rows past the visible end (tail page, causal window, bad page)
-        if (lim < ST) {
+          // S^T tile layout: lane holds head l32 and tokens
+          // r % 4 + 8 (r / 4) + 4 hh for its 16 registers r
+          if (USE_ALPHA) {
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (16 * tt + 4 * q4 + j >= lim) sc[tt][j] = -INFINITY;
-        }
-        // ---- probabilities against the fixed reference ----
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = head_max(mx);
-        m_seen = fmaxf(m_seen, mx);
-        if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
-        if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
-        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-        bf16x8 pb;  // P^T as the B operand: elements 0-3 tile 0, 4-7 tile 1
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const __bf16 pr = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[tt][j], c2, -mc)));
-            pb[4 * tt + j] = pr;
-            l_run += static_cast<float>(pr);
+            for (int r = 0; r < 16; ++r) sc[r] *= aq * ak[r >> 2][r & 3];
           }
-        // ---- PV: O^T[512 x 16] += C^T[512 x 32 tok] . P^T ----
-        {
-          // products n = (o8, oh) in that order; om = 8 oh + o8
-          constexpr int NP = 8 * (R / 128);
-          bf16x8 abuf[PV_AHEAD];
-          const uint32_t base = opaque(pv_b);
-          auto rd = [&](int n) {
-            const int o8 = n >> 2, oh = n & 3;
-            const uint32_t a_off = (base ^ (32u * o8)) + 256 * oh;
-            const bf16x4 lo4 = lds_read_tr(lds0 + a_off);
-            const bf16x4 hi4 = lds_read_tr(lds0 + a_off + 16 * 1024);
-            return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          };
 #pragma unroll
-          for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
-#pragma unroll
-          for (int n = 0; n < NP; ++n) {
-            const bf16x8 a = abuf[n % PV_AHEAD];
-            if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
-            acc[8 * (n & 3) + (n >> 2)] = mfma(a, pb, acc[8 * (n & 3) + (n >> 2)]);
-          }
+          for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
         }
+        // ---- mask rows past the visible end (tail page, causal window, bad
+        // page; past the last stage every row, which makes the softmax steps
+        // below a no-op without branching around them)
+        if (__builtin_expect(lim < ST, 0)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r & 3) + 8 * (r >> 2) + 4 * hh >= lim) sc[r] = -INFINITY;
+        }
+        // ---- PV of the previous stage, with the probabilities of this one
+        // computed between its products ----
+        float mx = -INFINITY, mc = 0.f;
+        bf16x8 pnew[2];
+        auto softmax_step = [&](int n) {
+          if (n == 0) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
+          } else if (n == 1) {
+#pragma unroll
+            for (int r = 8; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+          } else if (n == 2) {
+            mx = pair_max(mx);
+            m_seen = fmaxf(m_seen, mx);
+            if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
+            if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
+            mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+          } else if (n >= 3 && n < 3 + 8) {
+            // P^T as the B operand of the two 16-token steps: registers 8 ks .. 8 ks + 7
+            const int r = 2 * (n - 3);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -mc));
+            const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+            pnew[r >> 3][r & 7] = pr[0];
+            pnew[r >> 3][(r & 7) + 1] = pr[1];
+            l_run += static_cast<float>(pr[0]) + static_cast<float>(pr[1]);
+          }
+        };
+        pv_stage(s - 1, pprev, softmax_step);
+        pprev[0] = pnew[0];
+        pprev[1] = pnew[1];
       }
       // did any head outgrow its reference?
       if (__builtin_amdgcn_ballot_w64(overflow != 0)) *flag = 1;
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage s + 1 has landed
       __syncthreads();
       if (__builtin_amdgcn_readfirstlane(*flag)) {
         again = true;
@@ -488,19 +556,25 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // an empty split never waited for its loads
   // ---- epilogue: o_p = acc / l, lse_p = scale * m_ref + ln l ----
+  wait_acc_results();
   if (wave_active) {
-    const float l_tot = head_sum(l_run);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const size_t row_e = ((size_t)b * s_q + i) * heads + h0 + (fresh_lane() & 15);
+    const int ln = fresh_lane();
+    const size_t row_e = ((size_t)b * s_q + i) * heads + h0 + (ln & 31);
     float* out = o_part + (row_e * num_splits + p) * R;
+    // accumulator tile om: lane holds head l32 and latents 32 om + r % 4 + 8 (r / 4) + 4 hh
 #pragma unroll
-    for (int om = 0; om < R / 16; ++om) {
-      f32x4 v;
+    for (int om = 0; om < R / 32; ++om) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[om][j] * inv;
-      *reinterpret_cast<f32x4*>(out + 16 * om + 4 * q4) = v;
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[om][4 * q + j] * inv;
+        *reinterpret_cast<f32x4*>(out + 32 * om + 8 * q + 4 * (ln >> 5)) = v;
+      }
     }
-    if (q4 == 0) {
+    if ((ln >> 5) == 0) {
       lse_part[row_e * num_splits + p] =
           l_tot > 0.f ? m_ref * scale + log2f(l_tot) * kLn2 : -INFINITY;
     }
