@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-overhead", action="store_true", help="skip the alpha-free timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
@@ -129,6 +132,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 4}), flush=True)
+        return
 
     import qk_normed_mla_amd as Q
     import workloads as W

@@ -221,6 +221,54 @@ def test_decode_on_oracle_state(name):
     print(f"  row err {_compare_decode(wl, r, ref, kind, bounds):.2e}", flush=True)
 
 
+def test_reference_restart_on_rising_logits():
+    """The matrix-core kernel fixes each head's exponent reference at the first
+    visible tokens of a split and restarts the split when a later logit
+    outgrows it by more than its headroom.  Here the stored latents of the
+    second half of every sequence are scaled up 80-fold (alpha^k kept), which
+    lifts those content logits far past the first tokens' maximum; the result
+    must still equal the oracle's softmax over the same stored state."""
+    wl = P.small("dsv3", seq_len=256)
+    inp = W.make_inputs(wl, seed=31)
+    img = O.full_cache_image(wl, inp)
+    qi = O.query_image(wl, inp)
+    rk = wl.rank
+    for b, T in enumerate(inp["seq_lens"]):
+        t = np.arange(int(T) // 2, int(T))
+        pg, sl = inp["block_table"][b, t // 64], t % 64
+        c = O.words_to_f64(img["kv"][pg, sl, :rk], wl.cache_dtype)
+        img["kv"][pg, sl, :rk] = O.stored_bits(80.0 * c, wl.cache_dtype)
+    ref = _oracle_decode_all(wl, inp, qi, img, 1)
+    # precondition: some head's logits rise past the first tile's maximum by
+    # more than the kernel's headroom (2^96, i.e. 96 ln 2 in natural units)
+    rose = False
+    for b, T in enumerate(inp["seq_lens"]):
+        t = np.arange(int(T))
+        pg, sl = inp["block_table"][b, t // 64], t % 64
+        C = O.words_to_f64(img["kv"][pg, sl, :rk], wl.cache_dtype)
+        KR = O.words_to_f64(img["kv"][pg, sl, rk:], wl.cache_dtype)
+        lg = O.absorbed_logits(wl, O.words_to_f64(qi["q_tilde"][b, 0], wl.cache_dtype),
+                               qi["alpha_q"][b, 0].astype(np.float64),
+                               O.words_to_f64(qi["qr_hat"][b, 0], wl.cache_dtype), C,
+                               img["alpha_k"][pg, sl, :].astype(np.float64), KR, 0)
+        rose |= bool(np.any(lg.max(axis=1) - lg[:, :32].max(axis=1) > 96 * np.log(2.0)))
+    assert rose
+    r = DecodeRunner(wl, inp, num_splits=1)
+    kind = Q.decode_kernel_kind(r.dims, 1)
+    announce(f"decode restart dsv3 B={wl.batch} T={list(inp['seq_lens'])} kind={kind}")
+    assert kind == 1
+    r.kv.copy_(upload_words(img["kv"], r.kv))
+    r.alpha_k.copy_(torch.from_numpy(img["alpha_k"]).to("cuda"))
+    r.q_tilde.copy_(upload_words(qi["q_tilde"], r.q_tilde))
+    r.alpha_q.copy_(torch.from_numpy(qi["alpha_q"]).to("cuda"))
+    r.q_rope_normed.copy_(upload_words(qi["qr_hat"], r.q_rope_normed))
+    r.decode(0)
+    r.combine()
+    torch.cuda.synchronize()
+    bounds = _row_bounds(wl, inp, img, qi)
+    print(f"  row err {_compare_decode(wl, r, ref, 1, bounds):.2e}", flush=True)
+
+
 @pytest.mark.parametrize("name", ["dsv3", "grouped", "mtp"])
 def test_decode_generic_kernel(name):
     """The vector-ALU kernel on the bf16 shapes (an independent GPU path)."""
