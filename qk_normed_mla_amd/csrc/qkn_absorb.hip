@@ -6,9 +6,8 @@
 // Two launches:
 //   absorb_gemm   q~[row, m] = sum_j W^K_g[m, j] * (gamma_q[j] gamma_k[g, j] q[row, j])
 //                 a float32 GEMM per KV group, [rows_g x d] . [d x r], on the
-//                 float32 matrix cores (v_mfma_f32_32x32x2_f32): one wave per
-//                 32 x 32 output tile, operands read straight from global memory
-//                 as 16-byte rows of 4 head-dim entries.
+//                 float32 matrix cores (v_mfma_f32_32x32x2_f32), 64 x 128 tiles
+//                 per block with both operands staged through LDS.
 //   absorb_rows   alpha^q and the RoPE query; one wave per query row, four
 //                 heads of one query token per block sharing the rotation
 //                 angles, formed once per block.
@@ -19,30 +18,34 @@ namespace {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int WAVES_GEMM = 4;  // column tiles per block
-constexpr int kMaxHeadDimGemm = 512;  // the host checks head_dim
+constexpr int TM = 64;    // query rows per block (all of one KV group)
+constexpr int TN = 128;   // latent columns per block
+constexpr int KC = 32;    // head-dim entries staged per step
+constexpr int LDA = KC + 4;  // padded LDS row (floats)
 
-// Wave tile: rows n0 .. n0 + 31 of group g, latent columns m0 .. m0 + 31.
-// Lane l holds row / column l % 32; for each chunk of 8 head-dim entries the
-// lanes 0-31 hold entries 0-3 and lanes 32-63 entries 4-7, and the i-th
-// product pairs entry i with entry 4 + i (a fixed split of the reduction
-// index, the same for both operands).
+// Block of 4 waves: a 64-row x 128-column tile of q~ for one group.  Wave
+// (wr, wc) owns rows 32 wr .. +31 and columns 64 wc .. +63, i.e. two 32 x 32
+// tiles of v_mfma_f32_32x32x2_f32.  The folded query rows and the W^K_g rows
+// are staged through LDS 32 head-dim entries at a time (the next step's
+// global loads are issued before the current step's products).  In a step,
+// lane l reads 4 consecutive head-dim entries of its row (lanes 0-31 entries
+// 8j .. 8j+3, lanes 32-63 entries 8j+4 .. 8j+7) and the i-th product pairs
+// entry 8j+i with 8j+4+i: a fixed split of the reduction index, the same for
+// both operands.
 template <typename OutT>
-__global__ __launch_bounds__(64 * WAVES_GEMM) void absorb_gemm(
+__global__ __launch_bounds__(256) void absorb_gemm(
     const float* __restrict__ q, const float* __restrict__ w_k, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, OutT* __restrict__ q_tilde, int rows_per_group,
     int heads, int heads_per_group, int head_dim, int rank) {
-  __shared__ __attribute__((aligned(16))) float gqk[kMaxHeadDimGemm];  // gamma_q * gamma_k[g]
+  __shared__ __attribute__((aligned(16))) float As[TM * LDA];
+  __shared__ __attribute__((aligned(16))) float Bs[TN * LDA];
   const int g = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const float* gk = gamma_k + (size_t)g * head_dim;
-  for (int j = threadIdx.x; j < head_dim; j += 64 * WAVES_GEMM) gqk[j] = gamma_q[j] * gk[j];
-  __syncthreads();
-  const int n0 = blockIdx.x * 32;
-  const int m0 = (blockIdx.y * WAVES_GEMM + wave) * 32;
-  if (m0 >= rank) return;  // uniform per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * TM, m0 = blockIdx.y * TN;
   const float* wg = w_k + (size_t)g * rank * head_dim;
+  const float* gk = gamma_k + (size_t)g * head_dim;
 
   // global row of local row n of group g: n = bi * Hg + hl -> bi * H + g * Hg + hl
   auto global_row = [&](int n) {
@@ -50,47 +53,75 @@ __global__ __launch_bounds__(64 * WAVES_GEMM) void absorb_gemm(
     return (size_t)bi * heads + (size_t)g * heads_per_group + hl;
   };
 
-  const int r = lane & 31, hsel = lane >> 5;
-  const int n = n0 + r, m = m0 + r;
-  const bool row_ok = n < rows_per_group, col_ok = m < rank;
-  // out-of-range rows / columns read row 0 and are zeroed after the load
-  const float* qa = q + (row_ok ? global_row(n) : 0) * head_dim;
-  const float* wb = wg + (size_t)(col_ok ? m : 0) * head_dim;
-
-  f32x16 acc = {};
-  constexpr int CB = 8;  // chunks of 8 head-dim entries whose loads are issued together
-  for (int c0 = 0; c0 < head_dim; c0 += 8 * CB) {
-    float4 a[CB], bv[CB];
+  // staging assignment: A 64 x 32 floats = 512 float4 (2 per thread), B 128 x 32 = 1024 (4)
+  float4 ra[2], rb[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int k = c0 + 8 * u + 4 * hsel;
-      const int kc = min(k, head_dim - 4);  // head_dim is a multiple of 4
-      a[u] = *reinterpret_cast<const float4*>(qa + kc);
-      bv[u] = *reinterpret_cast<const float4*>(wb + kc);
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, r = e >> 3, k = k0 + 4 * (e & 7);
+      const int n = n0 + r;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (n < rows_per_group && k < head_dim) {  // head_dim is a multiple of 4
+        v = *reinterpret_cast<const float4*>(q + global_row(n) * head_dim + k);
+        v.x *= gamma_q[k] * gk[k];
+        v.y *= gamma_q[k + 1] * gk[k + 1];
+        v.z *= gamma_q[k + 2] * gk[k + 2];
+        v.w *= gamma_q[k + 3] * gk[k + 3];
+      }
+      ra[u] = v;
     }
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int k = c0 + 8 * u + 4 * hsel;
-      const bool ok = k < head_dim;
-      const int kc = min(k, head_dim - 4);
-      const float4 gf = *reinterpret_cast<const float4*>(gqk + kc);
-      const bool ra = ok && row_ok, rb = ok && col_ok;
-      const float ax = ra ? a[u].x * gf.x : 0.f, ay = ra ? a[u].y * gf.y : 0.f;
-      const float az = ra ? a[u].z * gf.z : 0.f, aw = ra ? a[u].w * gf.w : 0.f;
-      const float bx = rb ? bv[u].x : 0.f, by = rb ? bv[u].y : 0.f;
-      const float bz = rb ? bv[u].z : 0.f, bw = rb ? bv[u].w : 0.f;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ax, bx, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ay, by, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(az, bz, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aw, bw, acc, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u, r = e >> 3, k = k0 + 4 * (e & 7);
+      const int m = m0 + r;
+      rb[u] = (m < rank && k < head_dim) ? *reinterpret_cast<const float4*>(wg + (size_t)m * head_dim + k)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u;
+      *reinterpret_cast<float4*>(&As[(e >> 3) * LDA + 4 * (e & 7)]) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      *reinterpret_cast<float4*>(&Bs[(e >> 3) * LDA + 4 * (e & 7)]) = rb[u];
+    }
+  };
+
+  f32x16 acc[2] = {};
+  const int r = lane & 31, hsel = lane >> 5;
+  fetch(0);
+  for (int k0 = 0; k0 < head_dim; k0 += KC) {
+    __syncthreads();  // every wave is done with the previous step's tiles
+    stash();
+    __syncthreads();
+    if (k0 + KC < head_dim) fetch(k0 + KC);
+#pragma unroll
+    for (int j = 0; j < KC / 8; ++j) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[(32 * wr + r) * LDA + 8 * j + 4 * hsel]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 bv = *reinterpret_cast<const float4*>(&Bs[(64 * wc + 32 * t + r) * LDA + 8 * j + 4 * hsel]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bv.x, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bv.y, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bv.z, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bv.w, acc[t], 0, 0, 0);
+      }
     }
   }
   // D[i][j]: column j = lane % 32, row i = (reg % 4) + 8 (reg / 4) + 4 (lane / 32)
-  if (!col_ok) return;
 #pragma unroll
-  for (int reg = 0; reg < 16; ++reg) {
-    const int i = (reg & 3) + 8 * (reg >> 2) + 4 * hsel;
-    if (n0 + i < rows_per_group) Elem<OutT>::store(q_tilde, global_row(n0 + i) * rank + m, acc[reg]);
+  for (int t = 0; t < 2; ++t) {
+    const int m = m0 + 64 * wc + 32 * t + r;
+    if (m >= rank) continue;
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) {
+      const int n = n0 + 32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * hsel;
+      if (n < rows_per_group) Elem<OutT>::store(q_tilde, global_row(n) * rank + m, acc[t][reg]);
+    }
   }
 }
 
@@ -148,8 +179,8 @@ hipError_t launch_typed(const qkn_mla_dims& d, const float* q, const float* q_ro
                         float* alpha_q, void* q_rope_normed, hipStream_t s) {
   const int hpg = d.heads / d.groups;
   const int rows_per_group = d.batch * d.s_q * hpg;
-  dim3 grid(cdiv(rows_per_group, 32), cdiv(d.rank, 32 * WAVES_GEMM), d.groups);
-  hipLaunchKernelGGL(absorb_gemm<OutT>, grid, dim3(64 * WAVES_GEMM), 0, s, q, w_k, gamma_q,
+  dim3 grid(cdiv(rows_per_group, TM), cdiv(d.rank, TN), d.groups);
+  hipLaunchKernelGGL(absorb_gemm<OutT>, grid, dim3(256), 0, s, q, w_k, gamma_q,
                      gamma_k, static_cast<OutT*>(q_tilde), rows_per_group, d.heads, hpg,
                      d.head_dim, d.rank);
   hipError_t e = hipGetLastError();
