@@ -172,10 +172,7 @@ def main():
 
     def step(k, flags=0):
         r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
-        r.absorb()
-        r.append_new()
-        r.decode(flags)
-        r.combine()
+        r.step(flags)
 
     def attn(k, flags=0):
         r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]

@@ -3,14 +3,20 @@
 // alpha^q (decode-logit equation) and the separately normed, rotated RoPE query
 // (item 4).
 //
-// Two launches:
-//   absorb_gemm   q~[row, m] = sum_j W^K_g[m, j] * (gamma_q[j] gamma_k[g, j] q[row, j])
-//                 a float32 GEMM per KV group, [rows_g x d] . [d x r], on the
-//                 float32 matrix cores (v_mfma_f32_32x32x2_f32), 64 x 128 tiles
-//                 per block with both operands staged through LDS.
-//   absorb_rows   alpha^q and the RoPE query; one wave per query row, four
-//                 heads of one query token per block sharing the rotation
-//                 angles, formed once per block.
+// q~[row, m] = sum_j W^K_g[m, j] * (gamma_q[j] gamma_k[g, j] q[row, j]) is a
+// GEMM per KV group, [rows_g x d] . [d x r], in 64 x 128 tiles per block with
+// both operands staged through LDS.
+//   bf16 q~ (absorb_split, one launch): every float32 operand x is split into
+//     bf16 words hi = bf16(x), lo = bf16(x - hi), and the product is taken as
+//     hi.hi + hi.lo + lo.hi on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
+//     float32 accumulate).  The dropped lo.lo term and the rounding of lo are
+//     about 2^-17 of the product, far below the bf16 storage step of q~, at a
+//     sixteenth of the float32 matrix cost per product.  The same blocks also
+//     form alpha^q and the RoPE query of a share of their rows, while the
+//     first operand loads are in flight.
+//   float32 q~ (absorb_gemm + absorb_rows): the float32 matrix cores
+//     (v_mfma_f32_32x32x2_f32); then alpha^q and the RoPE query, one wave per
+//     query row, four heads of one query token per block.
 #include "qkn_internal.h"
 
 namespace qkn {
@@ -125,6 +131,271 @@ __global__ __launch_bounds__(256) void absorb_gemm(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// split-bf16 GEMM with the row work folded in (bf16 q~)
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int SK = 128;       // head-dim entries staged per step (all of d <= 128 at once)
+constexpr int SLD = SK + 8;   // LDS row of bf16 words (272 B: 16 rows hit distinct banks)
+constexpr int SPLIT_LDS = (2 * TM + 2 * TN) * SLD * 2 + SK * 4 + 2 * TM * 4;  // bytes
+
+// hi/lo bf16 words of four floats
+__device__ __forceinline__ void split4(float4 v, bf16x4& hi, bf16x4& lo) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  hi = __builtin_convertvector(x, bf16x4);
+  const f32x4 r = x - __builtin_convertvector(hi, f32x4);
+  lo = __builtin_convertvector(r, bf16x4);
+}
+
+// Row work of one wave: alpha^q and the normed, rotated RoPE query of up to
+// four global query rows (rows[u] < 0: none).  load() issues every load of the
+// batch; finish() does the arithmetic and the stores.  The angles of token
+// angle_tok for dims lane and lane + 64 are kept and formed again only when
+// the token changes (double precision: at positions of 2^18 a float angle is
+// off by ~1e-2 rad).
+constexpr int QR_BATCH = 4;
+struct QueryRows {
+  int row[QR_BATCH], tok[QR_BATCH], pos[QR_BATCH];
+  float qv[QR_BATCH][8];             // head_dim <= 512
+  float xa[QR_BATCH][2], xb[QR_BATCH][2];  // dims j and j + d_R / 2, j = lane + 64 k
+  float ga[2], gb[2];                      // gamma_qR at those dims
+
+  __device__ __forceinline__ void load(const float* __restrict__ q, const float* __restrict__ q_rope,
+                                       const int32_t* __restrict__ q_pos,
+                                       const float* __restrict__ gamma_qr, int head_dim, int rope_dim,
+                                       int lane) {
+    const int half = rope_dim / 2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = lane + 64 * k;
+      ga[k] = j < half ? gamma_qr[j] : 0.f;
+      gb[k] = j < half ? gamma_qr[j + half] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < QR_BATCH; ++u) {
+      const size_t r = row[u] >= 0 ? (size_t)row[u] : 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = lane + 64 * k;
+        qv[u][k] = (row[u] >= 0 && j < head_dim) ? q[r * head_dim + j] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = lane + 64 * k;
+        const bool ok = row[u] >= 0 && j < half;
+        xa[u][k] = ok ? q_rope[r * rope_dim + j] : 0.f;
+        xb[u][k] = ok ? q_rope[r * rope_dim + j + half] : 0.f;
+      }
+      pos[u] = (row[u] >= 0 && rope_dim > 0) ? q_pos[tok[u]] : 0;
+    }
+  }
+
+  __device__ __forceinline__ void finish(float* __restrict__ alpha_q,
+                                         uint16_t* __restrict__ q_rope_out, int& angle_tok,
+                                         float (&cs)[2], float (&sn)[2], int head_dim, int rope_dim,
+                                         float eps, float theta, int lane) {
+    const int half = rope_dim / 2;
+#pragma unroll
+    for (int u = 0; u < QR_BATCH; ++u) {
+      if (row[u] < 0) continue;  // uniform
+      const size_t r = (size_t)row[u];
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss = fmaf(qv[u][k], qv[u][k], ss);
+      ss = wave_sum(ss);
+      if (lane == 0) alpha_q[r] = 1.0f / sqrtf(ss / (float)head_dim + eps);
+      if (rope_dim == 0) continue;
+      if (tok[u] != angle_tok) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int j = lane + 64 * k;
+          cs[k] = 1.f;
+          sn[k] = 0.f;
+          if (j < half && theta != 0.f) rope_cos_sin(pos[u], j, rope_dim, theta, &cs[k], &sn[k]);
+        }
+        angle_tok = tok[u];
+      }
+      float sr = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) sr = fmaf(xa[u][k], xa[u][k], fmaf(xb[u][k], xb[u][k], sr));
+      sr = wave_sum(sr);
+      const float inv = 1.0f / sqrtf(sr / (float)rope_dim + eps);
+      uint16_t* out = q_rope_out + r * rope_dim;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = lane + 64 * k;
+        if (j < half) {
+          const float x1 = xa[u][k] * inv * ga[k];
+          const float x2 = xb[u][k] * inv * gb[k];
+          out[j] = f32_to_bf16(x1 * cs[k] - x2 * sn[k]);
+          out[j + half] = f32_to_bf16(x2 * cs[k] + x1 * sn[k]);
+        }
+      }
+    }
+  }
+};
+
+// Block of 4 waves: a 64-row x 128-column tile of q~ for one group, wave
+// (wr, wc) owning rows 32 wr .. +31 and columns 64 wc .. +63 (two 32 x 32
+// tiles).  The global row of each of the 64 tile rows is formed once into
+// LDS; the finished tile is written back through LDS in 16-byte pieces.  Per step of 128 head-dim entries the query rows (times
+// gamma_q gamma_k) and the W^K_g rows are split into hi/lo words as they are
+// stored to LDS.  Block (x, y) of group g also forms alpha^q and the RoPE
+// query of rows n0 + y * share .. of its tile, so every query row is done
+// once; the loads of that row work are issued first and its arithmetic runs
+// while the operand loads are in flight.
+__global__ __launch_bounds__(256) void absorb_split(
+    const float* __restrict__ q, const float* __restrict__ q_rope,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ w_k,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const float* __restrict__ gamma_qr, uint16_t* __restrict__ q_tilde,
+    float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int rows_per_group,
+    int heads, int heads_per_group, int head_dim, int rank, int rope_dim, float eps,
+    float theta) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint16_t* Ah = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Al = Ah + TM * SLD;
+  uint16_t* Bh = Al + TM * SLD;
+  uint16_t* Bl = Bh + TN * SLD;
+  float* fold = reinterpret_cast<float*>(Bl + TN * SLD);  // gamma_q gamma_k of the step
+  int* grow = reinterpret_cast<int*>(fold + SK);          // global row of tile row r, or -1
+  int* gtok = grow + TM;                                  // its query token (b, i)
+  const int g = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * TM, m0 = blockIdx.y * TN;
+  const float* wg = w_k + (size_t)g * rank * head_dim;
+  const float* gk = gamma_k + (size_t)g * head_dim;
+
+  if (tid < TM) {
+    const int n = n0 + tid;
+    const int bi = n / heads_per_group, hl = n % heads_per_group;
+    grow[tid] = n < rows_per_group ? bi * heads + g * heads_per_group + hl : -1;
+    gtok[tid] = bi;
+  }
+  __syncthreads();
+
+  // the block's share of the row work: its loads first
+  const int share = cdiv(TM, gridDim.y);
+  const int r_lo = min(TM, (int)blockIdx.y * share), r_hi = min(TM, r_lo + share);
+  QueryRows qr;
+#pragma unroll
+  for (int u = 0; u < QR_BATCH; ++u) {
+    const int lr = r_lo + wave + 4 * u;
+    qr.row[u] = lr < r_hi ? grow[lr] : -1;
+    qr.tok[u] = lr < r_hi ? gtok[lr] : 0;
+  }
+  qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
+
+  // operands of a step: A 64 x 128 floats = 2048 float4 (8 per thread), B 128 x 128 (16)
+  float4 ra[8], rb[16];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u, r = e >> 5, k = k0 + 4 * (e & 31);
+      const int gr = grow[r];
+      ra[u] = (gr >= 0 && k < head_dim) ? *reinterpret_cast<const float4*>(q + (size_t)gr * head_dim + k)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + 256 * u, r = e >> 5, k = k0 + 4 * (e & 31);
+      const int m = m0 + r;
+      rb[u] = (m < rank && k < head_dim) ? *reinterpret_cast<const float4*>(wg + (size_t)m * head_dim + k)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < SK) fold[tid] = k0 + tid < head_dim ? gamma_q[k0 + tid] * gk[k0 + tid] : 0.f;
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u, c = 4 * (e & 31), o = (e >> 5) * SLD + c;
+      float4 v = ra[u];
+      v.x *= fold[c];
+      v.y *= fold[c + 1];
+      v.z *= fold[c + 2];
+      v.w *= fold[c + 3];
+      bf16x4 hi, lo;
+      split4(v, hi, lo);
+      *reinterpret_cast<bf16x4*>(&Ah[o]) = hi;
+      *reinterpret_cast<bf16x4*>(&Al[o]) = lo;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + 256 * u, o = (e >> 5) * SLD + 4 * (e & 31);
+      bf16x4 hi, lo;
+      split4(rb[u], hi, lo);
+      *reinterpret_cast<bf16x4*>(&Bh[o]) = hi;
+      *reinterpret_cast<bf16x4*>(&Bl[o]) = lo;
+    }
+  };
+
+  fetch(0);
+  {
+    int angle_tok = -1;
+    float cs[2], sn[2];
+    qr.finish(alpha_q, q_rope_out, angle_tok, cs, sn, head_dim, rope_dim, eps, theta, lane);
+  }
+
+  f32x16 acc[2] = {};
+  const int r = lane & 31, kh = lane >> 5;
+  for (int k0 = 0; k0 < head_dim; k0 += SK) {
+    if (k0 > 0) {
+      __syncthreads();  // every wave is done with the previous step's tiles
+      fetch(k0);
+    }
+    __syncthreads();  // the fold factors of the step are visible
+    stash();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < SK / 16; ++ks) {
+      if (k0 + 16 * ks >= head_dim) break;  // uniform
+      // A operand: row 32 wr + r, entries 16 ks + 8 kh .. + 7; B operand: W^K row (column of q~)
+      const int ao = (32 * wr + r) * SLD + 16 * ks + 8 * kh;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[ao]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[ao]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int bo = (64 * wc + 32 * t + r) * SLD + 16 * ks + 8 * kh;
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[bo]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[bo]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // The tile goes out through LDS (in the place of the A operand words) as
+  // whole 16-byte pieces of q~ rows.  D[i][j]: column j = lane % 32, row
+  // i = (reg % 4) + 8 (reg / 4) + 4 (lane / 32).
+  __syncthreads();  // every wave is done with the operands
+  uint16_t* T = Ah;  // [TM][SLD]
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg)
+      T[(32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * kh) * SLD + 64 * wc + 32 * t + r] =
+          f32_to_bf16(acc[t][reg]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < TM * TN / 8 / 256; ++u) {
+    const int e = tid + 256 * u, row = e >> 4, c = 8 * (e & 15);
+    const int gr = grow[row];
+    if (gr >= 0 && m0 + c < rank)  // rank is a multiple of 8
+      *reinterpret_cast<uint4*>(q_tilde + (size_t)gr * rank + m0 + c) =
+          *reinterpret_cast<const uint4*>(&T[row * SLD + c]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 path
+// ---------------------------------------------------------------------------
 // alpha^q = 1/RMS(q) and the normed, rotated RoPE query of four heads of one
 // query token; the token's angles are formed once, in double precision.
 constexpr int ROWS_HEADS = 4;
@@ -198,9 +469,24 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
                                const int32_t* q_pos, const float* w_k, const float* gamma_q,
                                const float* gamma_k, const float* gamma_qr, void* q_tilde,
                                float* alpha_q, void* q_rope_normed, hipStream_t s) {
-  if (d.cache_dtype == QKN_BF16)
-    return launch_typed<uint16_t>(d, q, q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr, q_tilde,
-                                  alpha_q, q_rope_normed, s);
+  if (d.cache_dtype == QKN_BF16) {
+    if (d.rope_dim / 2 > 128) return hipErrorInvalidValue;
+    const int hpg = d.heads / d.groups;
+    const int rows_per_group = d.batch * d.s_q * hpg;
+    dim3 grid(cdiv(rows_per_group, TM), cdiv(d.rank, TN), d.groups);
+    static bool attr_set = false;
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&absorb_split),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, SPLIT_LDS);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(absorb_split, grid, dim3(256), SPLIT_LDS, s, q, q_rope, q_pos, w_k, gamma_q,
+                       gamma_k, gamma_qr, static_cast<uint16_t*>(q_tilde), alpha_q,
+                       static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,
+                       d.head_dim, d.rank, d.rope_dim, d.eps, d.rope_theta);
+    return hipGetLastError();
+  }
   return launch_typed<float>(d, q, q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr, q_tilde,
                              alpha_q, q_rope_normed, s);
 }

@@ -31,12 +31,39 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   extern __shared__ float cs[];                    // [rank] latent as stored, in float
   __shared__ float part[WAVES][MAX_HEAD_DIM];      // per-wave partial keys
   __shared__ float red[WAVES];
+  __shared__ float xn[256];                        // normed RoPE key (d_R <= 256)
   __shared__ int slot_row;                         // page * 64 + row, or -1
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = blockIdx.x;
   const int g = blockIdx.y;
+
+  // This wave's share of the projected key k[j] = sum_m c[m] W^K_g[m, j]:
+  // column block cb (64 columns, lane = column) over the row slice rs.  The
+  // first UNROLL rows of W^K_g are loaded before anything else, so that their
+  // latency overlaps the page lookup and the latent load.
+  const float* wg = w_k + (size_t)g * rank * head_dim;
+  const int ncb = cdiv(head_dim, 64);
+  const int nrs = WAVES / ncb;            // >= 2: head_dim <= 512
+  const int cb = wave % ncb, rs = wave / ncb;
+  const int per_slice = cdiv(rank, nrs);
+  const int j = 64 * cb + lane;
+  const int m_lo = rs * per_slice, m_hi = rs < nrs ? min(rank, m_lo + per_slice) : m_lo;
+  float wv[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u)
+    wv[u] = (m_lo + u < m_hi && j < head_dim) ? wg[(size_t)(m_lo + u) * head_dim + j] : 0.f;
+  // the RoPE key (wave 0 of the group-0 block): dims lane + 64 k (d_R <= 256)
+  const bool rope_wave = g == 0 && wave == 0 && rope_dim > 0;
+  float xr[4] = {};
+  int xpos = 0;
+  if (rope_wave) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + 64 * k < rope_dim) xr[k] = k_rope_new[(size_t)n * rope_dim + lane + 64 * k];
+    xpos = pos[n];
+  }
 
   if (tid == 0) {
     int sr = -1;
@@ -58,53 +85,51 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   const int sr = slot_row;
   if (sr < 0) return;  // uniform: nothing is written for a rejected token
 
-  const int row_stride = rank + rope_dim;
-  if (g == 0) {
-    for (int m = tid; m < rank; m += 64 * WAVES)
-      Elem<CacheT>::store(kv, (size_t)sr * row_stride + m, cs[m]);
-    // RoPE key (wave 0): normalised over d_R, then rotated
-    if (wave == 0 && rope_dim > 0) {
-      const float* x = k_rope_new + (size_t)n * rope_dim;
-      float ss = 0.f;
-      for (int j = lane; j < rope_dim; j += 64) ss = fmaf(x[j], x[j], ss);
-      ss = wave_sum(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)rope_dim + eps);
-      const int half = rope_dim / 2;
-      const int p = pos[n];
-      CacheT* out = kv + (size_t)sr * row_stride + rank;
-      for (int j = lane; j < half; j += 64) {
-        const float x1 = x[j] * inv * gamma_kr[j];
-        const float x2 = x[j + half] * inv * gamma_kr[j + half];
-        float c = 1.f, s = 0.f;
-        if (theta != 0.f) rope_cos_sin(p, j, rope_dim, theta, &c, &s);
-        Elem<CacheT>::store(out, j, x1 * c - x2 * s);
-        Elem<CacheT>::store(out, j + half, x2 * c + x1 * s);
-      }
-    }
-  }
-
-  // projected key of group g, k[j] = sum_m c[m] W^K_g[m, j]: wave w takes the
-  // column block cb (64 columns, lane = column) and the row slice rs
-  const float* wg = w_k + (size_t)g * rank * head_dim;
-  const int ncb = cdiv(head_dim, 64);
-  const int nrs = WAVES / ncb;            // >= 2: head_dim <= 512
-  const int cb = wave % ncb, rs = wave / ncb;
-  const int per_slice = cdiv(rank, nrs);
+  // projected key of group g over this wave's slice
   if (rs < nrs) {
-    const int j = 64 * cb + lane;
-    const int m_lo = rs * per_slice, m_hi = min(rank, m_lo + per_slice);
     float acc = 0.f;
     for (int m0 = m_lo; m0 < m_hi; m0 += UNROLL) {
-      float wv[UNROLL];
+      if (m0 != m_lo) {
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        wv[u] = (m0 + u < m_hi && j < head_dim) ? wg[(size_t)(m0 + u) * head_dim + j] : 0.f;
+        for (int u = 0; u < UNROLL; ++u)
+          wv[u] = (m0 + u < m_hi && j < head_dim) ? wg[(size_t)(m0 + u) * head_dim + j] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
         if (m0 + u < m_hi) acc = fmaf(cs[m0 + u], wv[u], acc);
     }
     if (j < head_dim) part[rs][j] = acc;
   }
+
+  // the latent as stored and the RoPE key (group-0 block), after the
+  // projection so that the W^K_g registers are free
+  const int row_stride = rank + rope_dim;
+  if (g == 0) {
+    for (int m = tid; m < rank; m += 64 * WAVES)
+      Elem<CacheT>::store(kv, (size_t)sr * row_stride + m, cs[m]);
+    // RoPE key: normalised over d_R, then rotated (dim d and d + d_R / 2
+    // are paired, which the normed values reach through LDS)
+    if (rope_wave) {
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ss = fmaf(xr[k], xr[k], ss);
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)rope_dim + eps);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (lane + 64 * k < rope_dim) xn[lane + 64 * k] = xr[k] * inv * gamma_kr[lane + 64 * k];
+      const int half = rope_dim / 2;
+      CacheT* out = kv + (size_t)sr * row_stride + rank;
+      for (int jj = lane; jj < half; jj += 64) {
+        const float x1 = xn[jj], x2 = xn[jj + half];
+        float c = 1.f, s = 0.f;
+        if (theta != 0.f) rope_cos_sin(xpos, jj, rope_dim, theta, &c, &s);
+        Elem<CacheT>::store(out, jj, x1 * c - x2 * s);
+        Elem<CacheT>::store(out, jj + half, x2 * c + x1 * s);
+      }
+    }
+  }
+
   __syncthreads();
   float ss = 0.f;
   for (int j = tid; j < head_dim; j += 64 * WAVES) {
@@ -128,7 +153,7 @@ hipError_t launch_typed(const qkn_mla_dims& d, int32_t n_tokens, const float* c_
                         const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
                         const int32_t* block_table, const float* w_k, const float* gamma_kr,
                         void* kv_cache, float* alpha_k_cache, int32_t* err_flag, hipStream_t s) {
-  if (d.head_dim > MAX_HEAD_DIM) return hipErrorInvalidValue;
+  if (d.head_dim > MAX_HEAD_DIM || d.rope_dim > 256) return hipErrorInvalidValue;
   dim3 grid(n_tokens, d.groups);
   const size_t shmem = (size_t)d.rank * sizeof(float);
   hipLaunchKernelGGL(append_kernel<CacheT>, grid, dim3(64 * WAVES), shmem, s, c_new, k_rope_new,

@@ -1,7 +1,8 @@
 // qkn_mla_combine: log-sum-exp merge of the split-KV partials.
 //   M = max_p lse_p, lse = M + ln sum_p e^{lse_p - M}, o = sum_p e^{lse_p - lse} o_p
 // One wave per (query row, 256-float slice of the latent); each lane owns four
-// consecutive latent floats, so every partial row is read with 16-byte loads.
+// consecutive latent floats, so every partial row is read with 16-byte loads,
+// eight splits at a time.
 #include <math.h>
 
 #include "qkn_internal.h"
@@ -10,6 +11,7 @@ namespace qkn {
 namespace {
 
 constexpr int kSlice = 256;
+constexpr int kBatch = 8;   // splits whose loads are in flight together
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -40,16 +42,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (lane == 0 && wid % slices == 0) lse_out[row] = lse;
   if (m0 >= rank) return;
   const float* op = o_part + (size_t)row * num_splits * rank + m0;
+  // splits in groups of kBatch: all loads of a group are issued before any is
+  // used; the sum still runs over p = 0, 1, 2, ... in order, skipping empty splits
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = 0; p < num_splits; ++p) {
-    const float l = lp[p];
-    if (l == -INFINITY) continue;
-    const float w = expf(l - lse);
-    const float4 v = *reinterpret_cast<const float4*>(op + (size_t)p * rank);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+  for (int p0 = 0; p0 < num_splits; p0 += kBatch) {
+    float4 v[kBatch];
+    float l[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u;
+      l[u] = p < num_splits ? lp[p] : -INFINITY;
+      v[u] = p < num_splits ? *reinterpret_cast<const float4*>(op + (size_t)p * rank)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (l[u] == -INFINITY) continue;
+      const float w = expf(l[u] - lse);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
+    }
   }
   *reinterpret_cast<float4*>(out + m0) = acc;
 }

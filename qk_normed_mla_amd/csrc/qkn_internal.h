@@ -38,32 +38,63 @@ template <> struct Elem<uint16_t> {
 };
 
 // ----------------------------------------------------------------------------
-// RoPE on the RMS-normed RoPE block (NeoX halves).  The angle pos * freq is
-// formed and reduced in double precision: at positions of 2^18 a float angle
-// would already be off by ~1e-2 rad.
+// RoPE on the RMS-normed RoPE block (NeoX halves): the angle pos * omega_j,
+// omega_j = theta^(-2 j / d_R), is formed and reduced in double precision (at
+// positions of 2^18 a float angle would already be off by ~1e-2 rad), and
+// its cosine and sine are taken in double on the reduced angle.  omega_j is w^j with w = theta^(-2/d_R),
+// raised by repeated squaring (at most 8 double products for j < 256; the
+// relative error stays ~1e-14), and the reduction subtracts k * 2 pi with 2 pi
+// in two double parts, which leaves the reduced angle good to ~1e-15 rad.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ void rope_cos_sin(int pos, int j, int rope_dim, float theta,
                                              float* c, float* s) {
-  double inv_freq = pow((double)theta, -2.0 * (double)j / (double)rope_dim);
-  double ang = (double)pos * inv_freq;
+  const double w = exp2(-2.0 / (double)rope_dim * log2((double)theta));
+  double omega = 1.0, b = w;
+  for (int e = j; e != 0; e >>= 1) {
+    if (e & 1) omega *= b;
+    b *= b;
+  }
+  const double ang = (double)pos * omega;
+  const double k = rint(ang * 0.15915494309189533577);          // ang / (2 pi)
+  const double r = fma(-k, 2.44929359829470635445e-16, fma(-k, 6.28318530717958623200, ang));
   double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  sincos(r, &sd, &cd);  // |r| <= pi: the short path
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
 }
 
 // ----------------------------------------------------------------------------
-// wave-level reductions (64 lanes)
+// wave-level reductions (64 lanes), all in registers: DPP lane permutations
+// within rows of 16 (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror), then v_permlane16_swap and v_permlane32_swap across rows.  Each
+// step combines a lane with one partner by a commutative operation, so every
+// lane ends with the same bits.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_partner<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_partner<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_partner<0x141>(v));  // row_half_mirror: the other quad of 8
+  v = op(v, dpp_partner<0x140>(v));  // row_mirror: the other half of 16
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));  // rows 2k and 2k + 1
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));  // the two halves
+  }
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
