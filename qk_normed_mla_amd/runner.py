@@ -2,12 +2,9 @@
 
 ``DecodeRunner`` uploads a workload's inputs (as drawn by ``workloads``), owns
 the paged cache, the alpha^k side cache, the query-side outputs and the split
-partials, and issues the four library calls of a step:
+partials, and issues the four library calls of a step in order:
 
-    absorb_query || append (the s_q new tokens) -> decode -> combine
-
-absorb_query and append touch disjoint buffers (the query side and the cache),
-so ``prepare`` runs them on two streams at once and joins them before decode.
+    absorb_query -> append (the s_q new tokens) -> decode -> combine
 
 torch is used for allocation and copies only; all arithmetic is in the HIP
 kernels.
@@ -90,7 +87,6 @@ class DecodeRunner:
         self.o_latent = torch.empty((B, sq, H, wl.rank), dtype=f32, device=dev)
         self.lse = torch.empty((B, sq, H), dtype=f32, device=dev)
         self.err_flag = torch.zeros((1,), dtype=torch.int32, device=dev)
-        self._side = None  # second stream of prepare()
 
     def alloc_partials(self, num_splits: int):
         wl = self.wl
@@ -139,16 +135,9 @@ class DecodeRunner:
                         self.o_latent, self.lse, stream)
 
     def prepare(self):
-        """absorb_query on the current stream and, at the same time, the append
-        of the new tokens on a second stream; the current stream waits for both."""
-        cur = torch.cuda.current_stream(self.device)
-        if self._side is None:
-            self._side = torch.cuda.Stream(self.device)
-        self._side.wait_stream(cur)
+        """The query side and the append of the new tokens."""
         self.absorb()
-        with torch.cuda.stream(self._side):
-            self.append_new()
-        cur.wait_stream(self._side)
+        self.append_new()
 
     def step(self, flags: int = 0):
         """One decode step on the current stream."""
