@@ -116,6 +116,9 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // One LDS-DMA load: 16 bytes per lane from rsrc + voff to LDS (M0 + 16 * lane).
 // The whole offset is in the vector operand, which is what the descriptor's
 // range check covers (reads at or past the descriptor size return zeros).
+// Every cache line is read exactly once, so the loads are marked
+// non-temporal (nt): they do not displace the split partials this kernel
+// writes, which the combine reads next.
 // Issued through asm so that the compiler does not hold every LDS read until
 // all DMA in flight has landed; completion is awaited explicitly (vmcnt)
 // before the barrier that publishes a stage.  Wait states: one after the
@@ -125,10 +128,10 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 template <bool FIRST_USE>
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
   if (FIRST_USE) {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
   } else {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
   }
 }
