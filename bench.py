@@ -203,18 +203,35 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def timed(g, reps=3):
-        """Median over reps of one replay, in ms, HIP events on the replay stream."""
-        stream = torch.cuda.current_stream()
-        out = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+    def warm(g, seconds=0.25):
+        """Untimed replays of g for about `seconds` of wall time: the GPU's
+        clocks ramp up over the first milliseconds of sustained work, and the
+        timings below are of the steady state."""
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
             g.replay()
-            b.record(stream)
             torch.cuda.synchronize()
-            out.append(a.elapsed_time(b))
-        return float(np.median(out))
+
+    def timed(graphs, reps=5):
+        """Per graph, the median over reps of one replay in ms.  The replays
+        of all graphs are interleaved back to back (no host sync between
+        them, so the GPU stays busy), each bracketed by HIP events on the
+        replay stream, after two untimed rounds."""
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            for g in graphs:
+                g.replay()
+        ev = []
+        for _ in range(reps):
+            for g in graphs:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                ev.append((a, b))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev]).reshape(reps, len(graphs))
+        return [float(np.median(t[:, j])) for j in range(len(graphs))]
 
     # the timed region: exactly K steps, one graph replay, barrier + sync on both sides
     g_steps = capture(step, args.steps)
@@ -224,6 +241,7 @@ def main():
     # replayed step must leave exactly the eager result
     if not torch.equal(r.o_latent, ref):
         raise RuntimeError("graph replay differs from the eager step")
+    warm(g_steps)
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -235,19 +253,22 @@ def main():
     if not torch.equal(r.o_latent, ref):
         raise RuntimeError("graph replay differs from the eager step")
 
-    # the decode kernel alone: back-to-back launches over the rotating replicas
+    # the decode kernel alone, and decode + combine: back-to-back launches over
+    # the rotating replicas.  QK-norm overhead: the decode kernel with and
+    # without the inverse-RMS factors, the graphs' replays interleaved
     n_dec = max(40, 4 * n_rep)
-    dec_ms = timed(capture(dec, n_dec)) / n_dec
-    log(f"step {ms_per_step * 1e3:.1f} us, decode kernel {dec_ms * 1e3:.1f} us")
-
-    # decode + combine, and the same kernel without the inverse-RMS factors
-    attn_ms = timed(capture(attn, n_dec)) / n_dec
+    graphs = [capture(dec, n_dec), capture(attn, n_dec)]
+    if not args.no_overhead:
+        graphs.append(capture(dec, n_dec, Q.QKN_DECODE_NO_ALPHA))
+    warm(graphs[0])
+    times = [t / n_dec for t in timed(graphs, reps=15)]
+    dec_ms, attn_ms = times[0], times[1]
+    log(f"step {ms_per_step * 1e3:.1f} us, decode kernel {dec_ms * 1e3:.1f} us, "
+        f"decode+combine {attn_ms * 1e3:.1f} us")
     overhead = None
     if not args.no_overhead:
-        plain_ms = timed(capture(attn, n_dec, Q.QKN_DECODE_NO_ALPHA)) / n_dec
-        attn_ms = timed(capture(attn, n_dec)) / n_dec
-        overhead = round((attn_ms / plain_ms - 1.0) * 100.0, 2)
-        log(f"decode+combine {attn_ms * 1e3:.1f} us with alpha, {plain_ms * 1e3:.1f} us without "
+        overhead = round((dec_ms / times[2] - 1.0) * 100.0, 2)
+        log(f"decode kernel {dec_ms * 1e3:.1f} us with alpha, {times[2] * 1e3:.1f} us without "
             f"({overhead:+.2f}%)")
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9

@@ -7,10 +7,12 @@
 // visible tokens t of the split,
 //   l_t = scale * ((q~ . c_t) alpha^q alpha^k_{t,g(h)} + q^R . k^R_t)
 //   o_p = sum_t softmax(l)_t c_t,   lse_p = ln sum_t e^{l_t}
-// The inverse-RMS factors are applied to the content logits in registers as a
-// row (alpha^q, one per head) by column (alpha^k, one per token) scaling before
-// the RoPE dot is accumulated; nothing extra is read or written for them beyond
-// the 4 bytes per token and group of the scalar cache.
+// The inverse-RMS factors are a row (alpha^q, one per head) by column
+// (alpha^k, one per token) scaling of the content logits: their product tile is
+// one float32 outer product on the matrix core, and it is applied in registers
+// as one fused multiply-add per logit that also adds the RoPE dot.  Nothing
+// extra is read or written for them beyond the 4 bytes per token and group of
+// the scalar cache.
 //
 // Work decomposition
 //   one workgroup (4 waves, one per SIMD) per (sequence b, split p, block of
@@ -30,9 +32,11 @@
 //                token, so a partial page reads zeros beyond it; an invalid
 //                page entry reads zeros throughout.  The loads are spread over
 //                the QK products.
-//   QK           S^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
-//                A = latent rows from LDS, B = q~ in registers), then
-//                S *= alpha^q alpha^k, then += K^R . q^R^T.
+//   QK           S_c^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
+//                A = latent rows from LDS, B = q~ in registers), then the
+//                RoPE dot R^T = K^R . q^R^T and the factor tile F^T = alpha^k
+//                alpha^q^T (v_mfma_f32_32x32x2f32); S = S_c F + R, one fused
+//                multiply-add per logit, in the first softmax steps.
 //   softmax      base 2 against a per-head reference fixed at the first
 //                visible tokens of the split, so the accumulator is never
 //                rescaled inside the loop.  QK-norm bounds the logits, so the
@@ -162,6 +166,13 @@ __device__ __forceinline__ int fresh_lane() {
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// Outer product of two float32 vectors in the 32 x 32 tile layout: lane l
+// gives a[l % 32] (row factor) and b[l % 32] (column factor); the second term
+// of the K = 2 product pairs lanes 32..63 of a with lanes 32..63 of b, which
+// must be 0 in b (a finite there).  Element (i, j) = a_i b_j, rounded once.
+__device__ __forceinline__ f32x16 outer32(float a, float b) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, f32x16{}, 0, 0, 0);
+}
 
 // PV product into an accumulator tile kept in the AGPR file.  Issued through
 // asm so that the compiler keeps the 256 accumulator registers of a wave there
@@ -266,6 +277,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   // query operands and page window in registers before any page load is
   // issued (the page loads are not visible to the compiler's own waits)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // column operand of the alpha^k alpha^q product tile (see outer32)
+  const float aq_col = hh == 0 ? aq : 0.f;
 
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS uint8_t*)smem));
   // validity of the pages of the stages in the ring, bit s mod 4 (uniform)
@@ -447,9 +460,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
         for (int k = 0; k < LOADS; ++k) load(pl, k);
       }
       if (wave_active) {
-        f32x16 sc = {};
+        // S_c (or S, without the inverse-RMS factors), the RoPE dot R and the
+        // factor tile F; past the last stage S_c = F = 0 and R = -inf
+        f32x16 sc = {}, rp = {}, fac = {};
         if (has_qk) {
-          // ---- QK: S^T[32 tok x 32 heads] over the 512 latents, then alpha, then RoPE ----
+          // ---- QK: S_c^T[32 tok x 32 heads] over the 512 latents, then RoPE and F ----
           // Row read of token l32, chunk 2 kk + hh:
           //   [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8)
           // RoPE row read, chunk 2 kk + hh (kk < 4):
@@ -465,17 +480,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < DR / 16; ++j) rx[j] = rp_b ^ (32u * j);
           }
-          // alpha^k of this lane's 16 tokens (4 runs of 4): prefetched with the
-          // RoPE rows ahead of the content products
-          f32x4 ak[4];
-          bf16x8 rope_a[DR / 16];
-          if (USE_ALPHA) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ak[j] = *(const LDS_AS f32x4*)(st_alpha + g * ST + 8 * j + 4 * hh);
-          }
-#pragma unroll
-          for (int kk = 0; kk < DR / 16; ++kk) rope_a[kk] = lds_read16(lds0 + rx[kk]);
+          // Content products S_c over the 512 latents, then the RoPE dot R^T =
+          // K^R . q^R^T.  Without the inverse-RMS factors R accumulates onto
+          // S_c.  With them R goes into an accumulator of its own and the tile
+          // F = alpha^k alpha^q (token by head) is one float32 outer product on
+          // the matrix core (outer32) from alpha^k of token l % 32 (one LDS
+          // read) and this lane's alpha^q; S = S_c F + R, one fused
+          // multiply-add per logit, is formed in the first softmax steps, under
+          // the matrix products of the previous stage's PV.
           {
+            bf16x8 rope_a[DR / 16];
+#pragma unroll
+            for (int kk = 0; kk < DR / 16; ++kk) rope_a[kk] = lds_read16(lds0 + rx[kk]);
+            float ak_row = 0.f;
+            if (USE_ALPHA) ak_row = st_alpha[g * ST + l32];
             constexpr int NK = R / 16;
             bf16x8 abuf[QK_AHEAD];
             auto rd = [&](int n) { return lds_read16(lds0 + qx[n & 7] + 256 * (n >> 3)); };
@@ -488,23 +506,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
               sc = mfma(a, qb[n], sc);
               if (n % 3 == 1 && n / 3 < LOADS) load(pl, n / 3);
             }
-          }
-          // S^T tile layout: lane holds head l32 and tokens
-          // r % 4 + 8 (r / 4) + 4 hh for its 16 registers r
-          if (USE_ALPHA) {
+            if (USE_ALPHA) {
+              fac = outer32(ak_row, aq_col);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sc[r] *= aq * ak[r >> 2][r & 3];
-          }
+              for (int kk = 0; kk < DR / 16; ++kk) rp = mfma(rope_a[kk], qrb[kk], rp);
+            } else {
 #pragma unroll
-          for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
+              for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
+            }
+          }
         }
         // ---- mask rows past the visible end (tail page, causal window, bad
         // page; past the last stage every row, which makes the softmax steps
-        // below a no-op without branching around them)
+        // below a no-op without branching around them).  S^T tile layout: lane
+        // holds head l32 and tokens r % 4 + 8 (r / 4) + 4 hh for its 16
+        // registers r.  With the factors the mask goes into R: S_c F is finite,
+        // so S = S_c F - inf = -inf.
         if (__builtin_expect(lim < ST, 0)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if ((r & 3) + 8 * (r >> 2) + 4 * hh >= lim) sc[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            if ((r & 3) + 8 * (r >> 2) + 4 * hh >= lim) {
+              if (USE_ALPHA) {
+                rp[r] = -INFINITY;
+              } else {
+                sc[r] = -INFINITY;
+              }
+            }
+          }
         }
         // ---- PV of the previous stage, with the probabilities of this one
         // computed between its products ----
@@ -513,10 +541,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
         auto softmax_step = [&](int n) {
           if (n == 0) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
+            for (int r = 0; r < 8; ++r) {
+              if (USE_ALPHA) sc[r] = fmaf(sc[r], fac[r], rp[r]);
+              mx = fmaxf(mx, sc[r]);
+            }
           } else if (n == 1) {
 #pragma unroll
-            for (int r = 8; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+            for (int r = 8; r < 16; ++r) {
+              if (USE_ALPHA) sc[r] = fmaf(sc[r], fac[r], rp[r]);
+              mx = fmaxf(mx, sc[r]);
+            }
           } else if (n == 2) {
             mx = pair_max(mx);
             m_seen = fmaxf(m_seen, mx);
