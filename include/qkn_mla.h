@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 1
+#define QKN_MLA_ABI_VERSION 2
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -61,6 +61,10 @@ typedef enum {
 } qkn_status;
 
 typedef enum { QKN_F32 = 0, QKN_BF16 = 1 } qkn_dtype;
+
+/* Bits that qkn_mla_append and qkn_mla_decode OR into *err_flag. */
+#define QKN_FLAG_INDEX 1         /* an index, position, length or page entry out of range */
+#define QKN_FLAG_PARTIAL_RANGE 2 /* a half-precision split partial beyond +-65504 */
 
 /* Flags of qkn_mla_decode. */
 #define QKN_DECODE_NO_ALPHA 1u      /* drop both inverse-RMS factors: plain absorbed
@@ -84,6 +88,15 @@ typedef struct {
   float rope_theta;          /* RoPE base; 0 disables the rotation */
   int32_t cache_dtype;       /* qkn_dtype of the cache and of q~ / normed RoPE query */
 } qkn_mla_dims;
+
+/*
+ * Element type of the split-KV partials o_partial of qkn_mla_decode and
+ * qkn_mla_combine ("partial dtype"): IEEE binary16 (half) when the cache is
+ * bfloat16, float32 when it is float32.  A partial is a convex combination of
+ * cached latent rows, so half keeps it to within 2^-11 of its own magnitude,
+ * eight times finer than the bfloat16 rounding of the latents it is made of,
+ * and halves the bytes the split-KV path writes and reads back.
+ */
 
 /* QKN_MLA_ABI_VERSION of the loaded library. */
 QKN_API int qkn_mla_abi_version(void);
@@ -149,7 +162,7 @@ QKN_API int qkn_mla_absorb_query(const qkn_mla_dims* dims, const float* q, const
  *   in/out: kv_cache [num_pages, 64, r + d_R] (cache dtype),
  *           alpha_k_cache [num_pages, 64, G] float32.
  *   err_flag (nullable) int32: a token whose sequence index, position or page
- *   entry is out of range is skipped and *err_flag is set to 1.
+ *   entry is out of range is skipped and QKN_FLAG_INDEX is ORed into *err_flag.
  *   n_tokens == 0 is a no-op.
  */
 QKN_API int qkn_mla_append(const qkn_mla_dims* dims, int32_t n_tokens, const float* c_new,
@@ -176,11 +189,13 @@ QKN_API int qkn_mla_append(const qkn_mla_dims* dims, int32_t n_tokens, const flo
  *   q_tilde [B,s_q,H,r], q_rope_normed [B,s_q,H,d_R] (cache dtype);
  *   alpha_q [B,s_q,H] float32; kv_cache, alpha_k_cache as written by append;
  *   block_table [B, max_pages_per_seq], seq_lens [B] int32 (T_b >= s_q).
- *   out: o_partial [B, s_q, H, num_splits, r] float32,
+ *   out: o_partial [B, s_q, H, num_splits, r] (partial dtype, see above),
  *        lse_partial [B, s_q, H, num_splits] float32.
- *   flags: QKN_DECODE_* bits.  err_flag (nullable): set to 1 when a sequence
- *   length exceeds max_pages_per_seq * 64 (it is clamped) or a page entry is
- *   out of range (those tokens are skipped).
+ *   flags: QKN_DECODE_* bits.  err_flag (nullable), bits ORed in:
+ *   QKN_FLAG_INDEX when a sequence length exceeds max_pages_per_seq * 64 (it
+ *   is clamped) or a page entry is out of range (those tokens are skipped);
+ *   QKN_FLAG_PARTIAL_RANGE when a half partial would exceed the half range
+ *   (latent entries beyond +-65504 in the cache); it is then stored as +-inf.
  *   Products run on the matrix cores (bf16 operands, float32 accumulation)
  *   when qkn_mla_decode_kernel_kind() says 1, otherwise on the vector ALUs in
  *   float32.
@@ -189,7 +204,7 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
                    const void* q_rope_normed, const void* kv_cache,
                    const float* alpha_k_cache, const int32_t* block_table,
                    const int32_t* seq_lens, int32_t num_splits, uint32_t flags,
-                   float* o_partial, float* lse_partial, int32_t* err_flag, void* stream);
+                   void* o_partial, float* lse_partial, int32_t* err_flag, void* stream);
 
 /*
  * qkn_mla_combine -- merge the split-KV partials of qkn_mla_decode.
@@ -201,11 +216,12 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
  *     M = max_p lse_p;  lse = M + ln sum_p e^{lse_p - M};
  *     o_latent = sum_p e^{lse_p - lse} o_p
  *   A row whose splits are all empty gets o_latent = 0 and lse = -inf.
- *   in: o_partial [B,s_q,H,num_splits,r], lse_partial [B,s_q,H,num_splits] float32
+ *   in: o_partial [B,s_q,H,num_splits,r] (partial dtype),
+ *       lse_partial [B,s_q,H,num_splits] float32
  *   out: o_latent [B, s_q, H, r] float32, lse [B, s_q, H] float32 (natural log).
  *   The value up-projection o = o_latent . W^V_g is left to the caller.
  */
-QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const float* o_partial,
+QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream);
 
 #ifdef __cplusplus

@@ -23,11 +23,14 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
+ABI_VERSION = 2
 QKN_OK = 0
 QKN_F32 = 0
 QKN_BF16 = 1
 QKN_DECODE_NO_ALPHA = 1
 QKN_DECODE_FORCE_GENERIC = 2
+QKN_FLAG_INDEX = 1
+QKN_FLAG_PARTIAL_RANGE = 2
 PAGE_SIZE = 64
 
 _c_int32 = ctypes.c_int32
@@ -84,6 +87,9 @@ def library() -> ctypes.CDLL:
                                        P, P, P, P]
         lib.qkn_mla_combine.restype = ctypes.c_int
         lib.qkn_mla_combine.argtypes = [D, _c_int32, P, P, P, P, P]
+        if lib.qkn_mla_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qkn_mla_abi_version()}, "
+                               f"this binding needs {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -117,6 +123,11 @@ def dims_for(wl, num_pages: int) -> Dims:
 
 def cache_torch_dtype(dims: Dims) -> torch.dtype:
     return torch.bfloat16 if dims.cache_dtype == QKN_BF16 else torch.float32
+
+
+def partial_torch_dtype(dims: Dims) -> torch.dtype:
+    """Element type of the split-KV partials: half for a bf16 cache."""
+    return torch.float16 if dims.cache_dtype == QKN_BF16 else torch.float32
 
 
 def _stream_ptr(stream) -> int:
@@ -214,7 +225,7 @@ def qkn_mla_decode(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_
         _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
         _ptr(seq_lens, "seq_lens", i32, d.batch),
         P, int(flags),
-        _ptr(o_partial, "o_partial", f32, rows * P * d.rank),
+        _ptr(o_partial, "o_partial", partial_torch_dtype(d), rows * P * d.rank),
         _ptr(lse_partial, "lse_partial", f32, rows * P),
         _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
         ctypes.c_void_p(_stream_ptr(stream)))
@@ -229,7 +240,7 @@ def qkn_mla_combine(dims: Dims, num_splits: int, o_partial, lse_partial, o_laten
     P = int(num_splits)
     st = library().qkn_mla_combine(
         ctypes.byref(d), P,
-        _ptr(o_partial, "o_partial", f32, rows * P * d.rank),
+        _ptr(o_partial, "o_partial", partial_torch_dtype(d), rows * P * d.rank),
         _ptr(lse_partial, "lse_partial", f32, rows * P),
         _ptr(o_latent, "o_latent", f32, rows * d.rank),
         _ptr(lse, "lse", f32, rows),

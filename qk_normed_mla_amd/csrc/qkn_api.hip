@@ -109,7 +109,7 @@ int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const float* a
                    const void* q_rope_normed, const void* kv_cache,
                    const float* alpha_k_cache, const int32_t* block_table,
                    const int32_t* seq_lens, int32_t num_splits, uint32_t flags,
-                   float* o_partial, float* lse_partial, int32_t* err_flag, void* stream) {
+                   void* o_partial, float* lse_partial, int32_t* err_flag, void* stream) {
   int kind = qkn_mla_decode_kernel_kind(dims, num_splits, flags);
   if (kind < 0) return kind;
   if (flags & ~(QKN_DECODE_NO_ALPHA | QKN_DECODE_FORCE_GENERIC)) return QKN_ERR_INVALID_ARG;
@@ -131,7 +131,7 @@ int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const float* a
                               : qkn::launch_decode_generic(*dims, a, s));
 }
 
-int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const float* o_partial,
+int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream) {
   int st = check_dims(dims);
   if (st != QKN_OK) return st;

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
       const int page = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
       if (page >= 0 && page < num_pages) sr = page * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
     }
-    if (sr < 0 && err_flag && g == 0) atomicOr(err_flag, 1);
+    if (sr < 0 && err_flag && g == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
     slot_row = sr;
   }
   // the latent rounded to the storage type (exact for a float cache)

@@ -1,4 +1,5 @@
-// Generic split-KV decode on the vector ALUs, float32 arithmetic throughout.
+// Generic split-KV decode on the vector ALUs, float32 arithmetic throughout
+// (the partials are stored in the partial dtype: half for a bf16 cache).
 // It serves the float32 cache and any size the matrix-core kernel does not
 // take (few heads, other ranks); it is also a second, independent GPU
 // implementation the matrix-core kernel is tested against.
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void decode_generic(
     const CacheT* __restrict__ q_tilde, const float* __restrict__ alpha_q,
     const CacheT* __restrict__ q_rope, const CacheT* __restrict__ kv,
     const float* __restrict__ alpha_k, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+    const int32_t* __restrict__ seq_lens, PartialOf<CacheT>* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int s_q, int heads,
     int groups, int rank, int rope_dim, int max_pages, int num_pages, int num_splits,
     float scale, int use_alpha) {
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void decode_generic(
 
   int T = seq_lens[b];
   if (T > max_pages * QKN_MLA_PAGE_SIZE || T < 0) {
-    if (err_flag && tid == 0 && p == 0 && blockIdx.x == 0 && i == 0) atomicOr(err_flag, 1);
+    if (err_flag && tid == 0 && p == 0 && blockIdx.x == 0 && i == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
     T = min(max(T, 0), max_pages * QKN_MLA_PAGE_SIZE);
   }
   const int n_vis = T - s_q + i + 1;  // tokens this query may see
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_generic(
         if (page >= 0 && page < num_pages)
           sr = page * QKN_MLA_PAGE_SIZE + t % QKN_MLA_PAGE_SIZE + 1;
         else if (err_flag)
-          atomicOr(err_flag, 1);
+          atomicOr(err_flag, QKN_FLAG_INDEX);
       }
       slot[tid] = sr;
     }
@@ -163,15 +164,19 @@ __global__ __launch_bounds__(256) void decode_generic(
     }
   }
   __syncthreads();
+  bool out_of_range = false;  // a half partial rounded to +-inf
 #pragma unroll
   for (int k = 0; k < kMaxAccPerThread; ++k) {
     const int m = tid + 256 * k;
     if (m >= rank) break;
     for (int h = 0; h < nh; ++h) {
       size_t row = (size_t)bi * heads + h0 + h;
-      o_part[(row * num_splits + p) * rank + m] = acc[h][k] * fac[h];
+      const auto v = static_cast<PartialOf<CacheT>>(acc[h][k] * fac[h]);
+      if constexpr (sizeof(v) == 2) out_of_range |= __builtin_isinf(static_cast<float>(v));
+      o_part[(row * num_splits + p) * rank + m] = v;
     }
   }
+  if (out_of_range && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
 }
 
 template <typename CacheT>
@@ -188,7 +193,8 @@ hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t 
   hipLaunchKernelGGL(decode_generic<CacheT>, grid, dim3(256), shmem, s,
                      static_cast<const CacheT*>(a.q_tilde), a.alpha_q,
                      static_cast<const CacheT*>(a.q_rope), static_cast<const CacheT*>(a.kv),
-                     a.alpha_k, a.block_table, a.seq_lens, a.o_part, a.lse_part, a.err_flag,
+                     a.alpha_k, a.block_table, a.seq_lens,
+                     static_cast<PartialOf<CacheT>*>(a.o_part), a.lse_part, a.err_flag,
                      d.s_q, d.heads, d.groups, d.rank, d.rope_dim, d.max_pages_per_seq,
                      d.num_pages, a.num_splits, d.softmax_scale, a.use_alpha ? 1 : 0);
   return hipGetLastError();

@@ -70,6 +70,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const uint16_t* __restrict__ q_tilde, const float* __restrict__ alpha_q,
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv,
     const float* __restrict__ alpha_k, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+    const int32_t* __restrict__ seq_lens, _Float16* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int s_q, int heads,
     int groups, int max_pages, int num_pages, int num_splits, int row_blocks, int n_work,
     int per_xcd, float scale) {
@@ -599,24 +601,40 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int ln = fresh_lane();
     const size_t row_e = ((size_t)b * s_q + i) * heads + h0 + (ln & 31);
-    float* out = o_part + (row_e * num_splits + p) * R;
-    // accumulator tile om: lane holds head l32 and latents 32 om + r % 4 + 8 (r / 4) + 4 hh
+    // accumulator tile om: lane holds head l32 and latents 32 om + r % 4 +
+    // 8 (r / 4) + 4 hh.  The two lanes of a head (l, l ^ 32) trade halves so
+    // that each stores 8 consecutive latents as one 16-byte write: lane hh
+    // takes latents 32 om + 16 j + 8 hh + 0..7 (registers 8 j .. 8 j + 7 of
+    // both lanes, 4 from each).
+    _Float16* out = o_part + (row_e * num_splits + p) * R + 8 * (ln >> 5);
+    float mabs = 0.f;
 #pragma unroll
     for (int om = 0; om < R / 32; ++om) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
+      for (int j = 0; j < 2; ++j) {
+        uint32_t h[4];  // latent pairs +0,1 / +2,3 of q = 2 j, then of q = 2 j + 1
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[om][4 * q + j] * inv;
-        *reinterpret_cast<f32x4*>(out + 32 * om + 8 * q + 4 * (ln >> 5)) = v;
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = acc[om][8 * j + 2 * k], x1 = acc[om][8 * j + 2 * k + 1];
+          mabs = fmaxf(mabs, fmaxf(fabsf(x0), fabsf(x1)));
+          h[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0 * inv, x1 * inv}, f16x2));
+        }
+        // lanes < 32 keep their q = 2 j pairs and take their partner's;
+        // lanes >= 32 take their partner's q = 2 j + 1 pairs and keep their own
+        const auto r0 = __builtin_amdgcn_permlane32_swap(h[0], h[2], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(h[1], h[3], false, false);
+        const u32x4 v = {r0[0], r1[0], r0[1], r1[1]};
+        *reinterpret_cast<u32x4*>(out + 32 * om + 16 * j) = v;
       }
     }
+    // a partial beyond the half range was stored as +-inf (|x / l| >= 65520)
+    if (mabs * inv >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
     if ((ln >> 5) == 0) {
       lse_part[row_e * num_splits + p] =
           l_tot > 0.f ? m_ref * scale + log2f(l_tot) * kLn2 : -INFINITY;
     }
   }
-  if (err && err_flag && lane == 0) atomicOr(err_flag, 1);
+  if (err && err_flag && lane == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
 }
 
 template <bool USE_ALPHA>
@@ -635,7 +653,8 @@ hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t 
   hipLaunchKernelGGL(decode_mfma_kernel<USE_ALPHA>, grid, dim3(64 * WAVES), LDS_BYTES, s,
                      static_cast<const uint16_t*>(a.q_tilde), a.alpha_q,
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint16_t*>(a.kv),
-                     a.alpha_k, a.block_table, a.seq_lens, a.o_part, a.lse_part, a.err_flag, d.s_q,
+                     a.alpha_k, a.block_table, a.seq_lens, static_cast<_Float16*>(a.o_part),
+                     a.lse_part, a.err_flag, d.s_q,
                      d.heads, d.groups, d.max_pages_per_seq, d.num_pages, a.num_splits, row_blocks,
                      n_work, per_xcd, d.softmax_scale);
   return hipGetLastError();

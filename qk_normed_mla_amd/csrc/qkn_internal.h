@@ -117,6 +117,19 @@ hipError_t launch_append(const qkn_mla_dims& d, int32_t n_tokens, const float* c
                          const int32_t* block_table, const float* w_k, const float* gamma_kr,
                          void* kv_cache, float* alpha_k_cache, int32_t* err_flag, hipStream_t s);
 
+// Element type of the split-KV partials for a cache of element type CacheT:
+// half for a bf16 cache (stored as uint16_t words), float32 for a float32 one.
+template <typename CacheT>
+struct PartialDtype {
+  using type = float;
+};
+template <>
+struct PartialDtype<uint16_t> {
+  using type = _Float16;
+};
+template <typename CacheT>
+using PartialOf = typename PartialDtype<CacheT>::type;
+
 struct DecodeArgs {
   const void* q_tilde;
   const float* alpha_q;
@@ -125,7 +138,7 @@ struct DecodeArgs {
   const float* alpha_k;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* o_part;
+  void* o_part;  // partial dtype: half for a bf16 cache, float32 for a float32 cache
   float* lse_part;
   int32_t* err_flag;
   int num_splits;
@@ -136,7 +149,7 @@ hipError_t launch_decode_generic(const qkn_mla_dims& d, const DecodeArgs& a, hip
 bool mfma_decode_supported(const qkn_mla_dims& d);
 hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
 
-hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const float* o_part,
+hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);
 
 }  // namespace qkn

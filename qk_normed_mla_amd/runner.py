@@ -16,8 +16,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (QKN_BF16, PAGE_SIZE, Dims, cache_torch_dtype, dims_for, qkn_mla_absorb_query,
-               qkn_mla_append, qkn_mla_combine, qkn_mla_decode)
+from . import (QKN_BF16, PAGE_SIZE, Dims, cache_torch_dtype, dims_for, partial_torch_dtype,
+               qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine, qkn_mla_decode)
 
 
 def _dev(x, device, dtype=None):
@@ -92,7 +92,8 @@ class DecodeRunner:
         wl = self.wl
         self.num_splits = int(num_splits)
         shape = (wl.batch, wl.s_q, wl.heads, self.num_splits)
-        self.o_partial = torch.empty(shape + (wl.rank,), dtype=torch.float32, device=self.device)
+        self.o_partial = torch.empty(shape + (wl.rank,), dtype=partial_torch_dtype(self.dims),
+                                     device=self.device)
         self.lse_partial = torch.empty(shape, dtype=torch.float32, device=self.device)
 
     # -- the four calls ------------------------------------------------------

@@ -33,7 +33,14 @@ from qk_normed_mla_amd.runner import DecodeRunner
 #    |dS_t| <= gamma_K * sum_m |q~_m c_tm| (standard bound, gamma_K = K u / (1 - K u),
 #    u = 2^-24), computed per row by logit_error_bound(); it adds to the lse bound
 #    and, through the weights (|dw/w| <= 2 max_t |dl_t|), to the latent bound.
+#  * the split partials are stored as half for a bf16 cache: each is a convex
+#    combination of the latent rows its split sees, so storing it moves it by
+#    at most 2^-11 of its largest entry, <= 2^-11 max_t |c_tm| (KERNEL_PART_ROUND,
+#    absolute, in the same units as KERNEL_P_ROUND); the combine's weights sum
+#    to 1, so the merged row moves by no more.  A float32 cache keeps float32
+#    partials (0).
 TOL_E2E = {"f32": 1e-4, "bf16": 1e-2}
+KERNEL_PART_ROUND = {"f32": 0.0, "bf16": 2.0 ** -11}
 TOL_KERNEL_GENERIC = 1e-5
 KERNEL_P_ROUND = 2.0 ** -7
 KERNEL_LSE = float(np.log1p(2.0 ** -9))

@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == 1
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"

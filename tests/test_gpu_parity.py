@@ -11,7 +11,8 @@ import torch
 import oracle_pins as P
 import qk_normed_mla_amd as Q
 import workloads as W
-from gpu_helpers import (KERNEL_LSE, KERNEL_P_ROUND, TOL_E2E, TOL_KERNEL_GENERIC, announce,
+from gpu_helpers import (KERNEL_LSE, KERNEL_P_ROUND, KERNEL_PART_ROUND, TOL_E2E,
+                         TOL_KERNEL_GENERIC, announce,
                          logit_error_bound, require_gpu, row_err, ulp_distance_bf16,
                          upload_words, run_e2e)
 from oracle import qkn_oracle as O
@@ -183,8 +184,10 @@ def _row_bounds(wl, inp, img, qi, use_alpha=True):
 def _compare_decode(wl, r, ref, kind, bounds=None):
     """Partials and combined result against the oracle.  kind 0 (float32
     kernel): 1e-5 row-relative.  kind 1 (bf16 probabilities): the derived
-    absolute bounds of gpu_helpers, per row."""
-    o_part = r.o_partial.cpu().numpy()
+    absolute bounds of gpu_helpers, per row.  Both add the half storage of the
+    partials for a bf16 cache (KERNEL_PART_ROUND)."""
+    part_round = KERNEL_PART_ROUND[wl.cache_dtype]
+    o_part = r.o_partial.float().cpu().numpy()
     lse_part = r.lse_partial.cpu().numpy()
     o_lat = r.o_latent.cpu().numpy()
     lse = r.lse.cpu().numpy()
@@ -200,13 +203,14 @@ def _compare_decode(wl, r, ref, kind, bounds=None):
             err = np.max(np.abs(got - want))
             scale = np.max(np.abs(want))
             worst_rel = max(worst_rel, err / max(scale, 1e-30))
+            cmax, dl = bounds[(b, i)]
             if kind == 1:
-                cmax, dl = bounds[(b, i)]
-                tol_o = (KERNEL_P_ROUND + 4.0 * dl[h]) * cmax + 1e-5 * scale
+                tol_o = (KERNEL_P_ROUND + part_round + 4.0 * dl[h]) * cmax + 1e-5 * scale
                 assert err <= tol_o, (b, i, h, err, tol_o)
                 assert abs(lg - lw) <= KERNEL_LSE + dl[h] + 1e-6, (b, i, h, lg, lw, dl[h])
             else:
-                assert err <= TOL_KERNEL_GENERIC * scale, (b, i, h, err / scale)
+                tol_o = TOL_KERNEL_GENERIC * scale + part_round * cmax
+                assert err <= tol_o, (b, i, h, err / scale)
                 assert abs(lg - lw) <= 1e-5, (b, i, h, lg, lw)
     return worst_rel
 
@@ -275,8 +279,8 @@ def test_decode_generic_kernel(name):
     wl = P.small(name)
     inp = W.make_inputs(wl, seed=25)
     announce(f"decode generic {name}")
-    r, ref, _ = _decode_on_image(wl, inp, 3, flags=Q.QKN_DECODE_FORCE_GENERIC)
-    _compare_decode(wl, r, ref, 0)
+    r, ref, bounds = _decode_on_image(wl, inp, 3, flags=Q.QKN_DECODE_FORCE_GENERIC)
+    _compare_decode(wl, r, ref, 0, bounds)
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsv3", "grouped"])
@@ -331,11 +335,13 @@ def test_split_invariance_and_empty_splits():
         if splits == 40:
             lp = r.lse_partial.cpu().numpy()
             assert np.all(np.isneginf(lp[..., 11:]))
-    # each result is within KERNEL_P_ROUND * max|c| of the exact one (bf16
-    # probabilities on the matrix cores), so two of them within twice that
+    # each result is within (KERNEL_P_ROUND + KERNEL_PART_ROUND) * max|c| of the
+    # exact one (bf16 probabilities on the matrix cores, half partials), so two
+    # of them within twice that
     cmax = float(np.max(np.abs(O.stored_value(inp["c"], "bf16"))))
+    tol = 2 * (KERNEL_P_ROUND + KERNEL_PART_ROUND["bf16"]) * cmax
     for splits in (3, 11, 40):
-        assert np.max(np.abs(outs[splits][0] - outs[1][0])) <= 2 * KERNEL_P_ROUND * cmax
+        assert np.max(np.abs(outs[splits][0] - outs[1][0])) <= tol
         assert np.max(np.abs(outs[splits][1] - outs[1][1])) <= 2 * KERNEL_LSE + 1e-4
 
 
@@ -421,11 +427,33 @@ def test_decode_flags_bad_lengths():
     r.seq_lens[1] = 64 * wl.max_pages_per_seq + 5
     r.decode()
     torch.cuda.synchronize()
-    assert int(r.err_flag.item()) == 1
-    assert np.all(np.isfinite(r.o_partial.cpu().numpy()[1][r.lse_partial.cpu().numpy()[1] > -np.inf]))
+    assert int(r.err_flag.item()) == Q.QKN_FLAG_INDEX
+    assert np.all(np.isfinite(r.o_partial.float().cpu().numpy()[1][r.lse_partial.cpu().numpy()[1] > -np.inf]))
     r.seq_lens.copy_(torch.from_numpy(inp["seq_lens"]).cuda())
     r.err_flag.zero_()
     r.block_table[0, 1] = inp["num_pages"] + 7
     r.decode()
     torch.cuda.synchronize()
-    assert int(r.err_flag.item()) == 1
+    assert int(r.err_flag.item()) == Q.QKN_FLAG_INDEX
+
+
+@pytest.mark.parametrize("flags", [0, Q.QKN_DECODE_FORCE_GENERIC])
+def test_half_partials_out_of_range_flagged(flags):
+    """Latents beyond the half range make the half partials +-inf and raise
+    QKN_FLAG_PARTIAL_RANGE; in-range latents of the same step raise nothing."""
+    wl = P.small("dsv3", batch=2, seq_len=128)
+    inp = W.make_inputs(wl, seed=37)
+    announce(f"half partial range flags={flags}")
+    r = run_e2e(wl, inp)
+    r.err_flag.zero_()
+    r.decode(flags)
+    torch.cuda.synchronize()
+    assert int(r.err_flag.item()) == 0
+    big = dict(inp)
+    big["c"] = inp["c"] * np.float32(1e6)   # |c| far beyond 65504, still a bf16 number
+    r2 = run_e2e(wl, big)
+    r2.err_flag.zero_()
+    r2.decode(flags)
+    torch.cuda.synchronize()
+    assert int(r2.err_flag.item()) == Q.QKN_FLAG_PARTIAL_RANGE
+    assert np.any(np.isinf(r2.o_partial.float().cpu().numpy()))
