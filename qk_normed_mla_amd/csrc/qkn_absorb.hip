@@ -11,9 +11,9 @@
 //     hi.hi + hi.lo + lo.hi on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
 //     float32 accumulate).  The dropped lo.lo term and the rounding of lo are
 //     about 2^-17 of the product, far below the bf16 storage step of q~, at a
-//     sixteenth of the float32 matrix cost per product.  The same blocks also
-//     form alpha^q and the RoPE query of a share of their rows, while the
-//     first operand loads are in flight.
+//     sixteenth of the float32 matrix cost per product.  The same blocks (8
+//     waves) also form alpha^q and the RoPE query of a share of their rows,
+//     while the first operand loads are in flight.
 //   float32 q~ (absorb_gemm + absorb_rows): the float32 matrix cores
 //     (v_mfma_f32_32x32x2_f32); then alpha^q and the RoPE query, one wave per
 //     query row, four heads of one query token per block.
@@ -239,16 +239,18 @@ struct QueryRows {
   }
 };
 
-// Block of 4 waves: a 64-row x 128-column tile of q~ for one group, wave
-// (wr, wc) owning rows 32 wr .. +31 and columns 64 wc .. +63 (two 32 x 32
-// tiles).  The global row of each of the 64 tile rows is formed once into
-// LDS; the finished tile is written back through LDS in 16-byte pieces.  Per step of 128 head-dim entries the query rows (times
-// gamma_q gamma_k) and the W^K_g rows are split into hi/lo words as they are
-// stored to LDS.  Block (x, y) of group g also forms alpha^q and the RoPE
-// query of rows n0 + y * share .. of its tile, so every query row is done
-// once; the loads of that row work are issued first and its arithmetic runs
-// while the operand loads are in flight.
-__global__ __launch_bounds__(256) void absorb_split(
+// Block of 8 waves: a 64-row x 128-column tile of q~ for one group, wave
+// (wr, wc) = (w / 4, w % 4) owning rows 32 wr .. +31 and columns 32 wc .. +31
+// (one 32 x 32 tile).  The global row of each of the 64 tile rows is formed
+// once into LDS; the finished tile is written back through LDS in 16-byte
+// pieces.  Per step of 128 head-dim entries the query rows (times gamma_q
+// gamma_k) and the W^K_g rows are split into hi/lo words as they are stored to
+// LDS.  Block (x, y) of group g also forms alpha^q and the RoPE query of its
+// share of the tile's rows (rows y * share .. of the tile), so every query row
+// is done once; the loads of the first batch of that row work are issued
+// first and its arithmetic runs while the operand loads are in flight.
+constexpr int SW = 8;  // waves per block
+__global__ __launch_bounds__(64 * SW) void absorb_split(
     const float* __restrict__ q, const float* __restrict__ q_rope,
     const int32_t* __restrict__ q_pos, const float* __restrict__ w_k,
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
@@ -256,6 +258,7 @@ __global__ __launch_bounds__(256) void absorb_split(
     float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int rows_per_group,
     int heads, int heads_per_group, int head_dim, int rank, int rope_dim, float eps,
     float theta) {
+  constexpr int NT = 64 * SW;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint16_t* Ah = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Al = Ah + TM * SLD;
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256) void absorb_split(
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
   const int n0 = blockIdx.x * TM, m0 = blockIdx.y * TN;
   const float* wg = w_k + (size_t)g * rank * head_dim;
   const float* gk = gamma_k + (size_t)g * head_dim;
@@ -280,31 +283,36 @@ __global__ __launch_bounds__(256) void absorb_split(
   }
   __syncthreads();
 
-  // the block's share of the row work: its loads first
+  // the block's share of the row work, in batches of SW * QR_BATCH rows: the
+  // loads of the first batch first
   const int share = cdiv(TM, gridDim.y);
   const int r_lo = min(TM, (int)blockIdx.y * share), r_hi = min(TM, r_lo + share);
   QueryRows qr;
+  auto pick_rows = [&](int base) {
 #pragma unroll
-  for (int u = 0; u < QR_BATCH; ++u) {
-    const int lr = r_lo + wave + 4 * u;
-    qr.row[u] = lr < r_hi ? grow[lr] : -1;
-    qr.tok[u] = lr < r_hi ? gtok[lr] : 0;
-  }
+    for (int u = 0; u < QR_BATCH; ++u) {
+      const int lr = base + wave + SW * u;
+      qr.row[u] = lr < r_hi ? grow[lr] : -1;
+      qr.tok[u] = lr < r_hi ? gtok[lr] : 0;
+    }
+  };
+  pick_rows(r_lo);
   qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
 
-  // operands of a step: A 64 x 128 floats = 2048 float4 (8 per thread), B 128 x 128 (16)
-  float4 ra[8], rb[16];
+  // operands of a step: A 64 x 128 floats = 2048 float4 (4 per thread), B 128 x 128 (8)
+  constexpr int NA = TM * SK / 4 / NT, NB = TN * SK / 4 / NT;
+  float4 ra[NA], rb[NB];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u, r = e >> 5, k = k0 + 4 * (e & 31);
+    for (int u = 0; u < NA; ++u) {
+      const int e = tid + NT * u, r = e >> 5, k = k0 + 4 * (e & 31);
       const int gr = grow[r];
       ra[u] = (gr >= 0 && k < head_dim) ? *reinterpret_cast<const float4*>(q + (size_t)gr * head_dim + k)
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = tid + 256 * u, r = e >> 5, k = k0 + 4 * (e & 31);
+    for (int u = 0; u < NB; ++u) {
+      const int e = tid + NT * u, r = e >> 5, k = k0 + 4 * (e & 31);
       const int m = m0 + r;
       rb[u] = (m < rank && k < head_dim) ? *reinterpret_cast<const float4*>(wg + (size_t)m * head_dim + k)
                                          : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -313,8 +321,8 @@ __global__ __launch_bounds__(256) void absorb_split(
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u, c = 4 * (e & 31), o = (e >> 5) * SLD + c;
+    for (int u = 0; u < NA; ++u) {
+      const int e = tid + NT * u, c = 4 * (e & 31), o = (e >> 5) * SLD + c;
       float4 v = ra[u];
       v.x *= fold[c];
       v.y *= fold[c + 1];
@@ -326,8 +334,8 @@ __global__ __launch_bounds__(256) void absorb_split(
       *reinterpret_cast<bf16x4*>(&Al[o]) = lo;
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = tid + 256 * u, o = (e >> 5) * SLD + 4 * (e & 31);
+    for (int u = 0; u < NB; ++u) {
+      const int e = tid + NT * u, o = (e >> 5) * SLD + 4 * (e & 31);
       bf16x4 hi, lo;
       split4(rb[u], hi, lo);
       *reinterpret_cast<bf16x4*>(&Bh[o]) = hi;
@@ -340,9 +348,15 @@ __global__ __launch_bounds__(256) void absorb_split(
     int angle_tok = -1;
     float cs[2], sn[2];
     qr.finish(alpha_q, q_rope_out, angle_tok, cs, sn, head_dim, rope_dim, eps, theta, lane);
+    // further batches when the share is larger than one batch (few column blocks)
+    for (int base = r_lo + SW * QR_BATCH; base < r_hi; base += SW * QR_BATCH) {
+      pick_rows(base);
+      qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
+      qr.finish(alpha_q, q_rope_out, angle_tok, cs, sn, head_dim, rope_dim, eps, theta, lane);
+    }
   }
 
-  f32x16 acc[2] = {};
+  f32x16 acc = {};
   const int r = lane & 31, kh = lane >> 5;
   for (int k0 = 0; k0 < head_dim; k0 += SK) {
     if (k0 > 0) {
@@ -357,17 +371,14 @@ __global__ __launch_bounds__(256) void absorb_split(
       if (k0 + 16 * ks >= head_dim) break;  // uniform
       // A operand: row 32 wr + r, entries 16 ks + 8 kh .. + 7; B operand: W^K row (column of q~)
       const int ao = (32 * wr + r) * SLD + 16 * ks + 8 * kh;
+      const int bo = (32 * wc + r) * SLD + 16 * ks + 8 * kh;
       const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[ao]);
       const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[ao]);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int bo = (64 * wc + 32 * t + r) * SLD + 16 * ks + 8 * kh;
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[bo]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[bo]);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[t], 0, 0, 0);
-      }
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[bo]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[bo]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
     }
   }
   // The tile goes out through LDS (in the place of the A operand words) as
@@ -376,16 +387,12 @@ __global__ __launch_bounds__(256) void absorb_split(
   __syncthreads();  // every wave is done with the operands
   uint16_t* T = Ah;  // [TM][SLD]
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int reg = 0; reg < 16; ++reg)
-      T[(32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * kh) * SLD + 64 * wc + 32 * t + r] =
-          f32_to_bf16(acc[t][reg]);
-  }
+  for (int reg = 0; reg < 16; ++reg)
+    T[(32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * kh) * SLD + 32 * wc + r] = f32_to_bf16(acc[reg]);
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < TM * TN / 8 / 256; ++u) {
-    const int e = tid + 256 * u, row = e >> 4, c = 8 * (e & 15);
+  for (int u = 0; u < TM * TN / 8 / NT; ++u) {
+    const int e = tid + NT * u, row = e >> 4, c = 8 * (e & 15);
     const int gr = grow[row];
     if (gr >= 0 && m0 + c < rank)  // rank is a multiple of 8
       *reinterpret_cast<uint4*>(q_tilde + (size_t)gr * rank + m0 + c) =
@@ -481,7 +488,7 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    hipLaunchKernelGGL(absorb_split, grid, dim3(256), SPLIT_LDS, s, q, q_rope, q_pos, w_k, gamma_q,
+    hipLaunchKernelGGL(absorb_split, grid, dim3(64 * SW), SPLIT_LDS, s, q, q_rope, q_pos, w_k, gamma_q,
                        gamma_k, gamma_qr, static_cast<uint16_t*>(q_tilde), alpha_q,
                        static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,
                        d.head_dim, d.rank, d.rope_dim, d.eps, d.rope_theta);

@@ -104,9 +104,24 @@ def test_append_rejects_bad_slots():
 
 @pytest.mark.parametrize("name", NAMES)
 def test_absorb_query(name):
-    wl = P.small(name)
+    _check_absorb(P.small(name), f"absorb {name}")
+
+
+# bf16 shapes with fewer column blocks per row tile (rank <= 384: each block
+# forms alpha^q and the RoPE query of more than one batch of rows) and a head
+# dim spanning two staging steps
+ABSORB_SHAPES = [("dsv3", dict(rank=128)), ("dsv3", dict(rank=256, heads=64)),
+                 ("grouped", dict(rank=384)), ("dsv3", dict(head_dim=256, rank=64))]
+
+
+@pytest.mark.parametrize("name,kw", ABSORB_SHAPES)
+def test_absorb_query_shapes(name, kw):
+    _check_absorb(P.small(name, **kw), f"absorb {name} {kw}")
+
+
+def _check_absorb(wl, case):
     inp = W.make_inputs(wl, seed=23)
-    announce(f"absorb {name}")
+    announce(case)
     r = DecodeRunner(wl, inp)
     r.absorb()
     torch.cuda.synchronize()
