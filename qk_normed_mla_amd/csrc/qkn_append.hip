@@ -6,18 +6,18 @@
 //
 // Grid: one block of 16 waves per (new token, KV group).  Every block forms
 // its group's projected key and scalar; the group-0 block also stores the
-// latent and the RoPE key.  W^K_g is read once per block, row by row across
-// the lanes (coalesced): each wave takes 64 columns of the key and a
-// contiguous slice of the latent's rows, with up to 64 rows of loads in
-// flight per lane.  The slices' partial keys are then added in a fixed
-// order, so the result does not depend on timing.
+// latent and the RoPE key.  W^K_g is read once per block in 16-byte pieces:
+// thread t takes four columns (t mod d/4) of the key over every RG-th row of
+// the latent (RG = 4096 / d row groups), with 16 rows in flight per thread, so
+// that a wave's load covers whole rows.  The row groups' partial keys are
+// then added in a fixed order, so the result does not depend on timing.
 #include "qkn_internal.h"
 
 namespace qkn {
 namespace {
 
 constexpr int WAVES = 16;
-constexpr int UNROLL = 64;  // rows of W^K_g in flight per lane
+constexpr int UNROLL = 16;  // rows of W^K_g (16 bytes each) in flight per thread
 constexpr int MAX_HEAD_DIM = 512;  // columns of W^K_g a block handles (the host checks head_dim)
 
 template <typename CacheT>
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
     int32_t* __restrict__ err_flag, int batch, int max_pages, int num_pages, int rank,
     int head_dim, int rope_dim, int groups, float eps, float theta) {
   extern __shared__ float cs[];                    // [rank] latent as stored, in float
-  __shared__ float part[WAVES][MAX_HEAD_DIM];      // per-wave partial keys
+  __shared__ float part[64 * WAVES * 4];           // [RG][head_dim] partial keys (RG * head_dim <= 4096)
   __shared__ float red[WAVES];
   __shared__ float xn[256];                        // normed RoPE key (d_R <= 256)
   __shared__ int slot_row;                         // page * 64 + row, or -1
@@ -39,21 +39,23 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   const int n = blockIdx.x;
   const int g = blockIdx.y;
 
-  // This wave's share of the projected key k[j] = sum_m c[m] W^K_g[m, j]:
-  // column block cb (64 columns, lane = column) over the row slice rs.  The
-  // first UNROLL rows of W^K_g are loaded before anything else, so that their
-  // latency overlaps the page lookup and the latent load.
+  // This thread's share of the projected key k[j] = sum_m c[m] W^K_g[m, j]:
+  // four columns 4 c4 .. 4 c4 + 3 (one 16-byte load per row) over the rows
+  // m = rg, rg + RG, ... of the latent (RG row groups).  The first UNROLL of
+  // them are loaded before anything else, so that their latency overlaps the
+  // page lookup and the latent load.
   const float* wg = w_k + (size_t)g * rank * head_dim;
-  const int ncb = cdiv(head_dim, 64);
-  const int nrs = WAVES / ncb;            // >= 2: head_dim <= 512
-  const int cb = wave % ncb, rs = wave / ncb;
-  const int per_slice = cdiv(rank, nrs);
-  const int j = 64 * cb + lane;
-  const int m_lo = rs * per_slice, m_hi = rs < nrs ? min(rank, m_lo + per_slice) : m_lo;
-  float wv[UNROLL];
+  const int C4 = head_dim / 4;            // head_dim is a multiple of 4, <= 512
+  const int RG = (64 * WAVES) / C4;       // >= 8
+  const int c4 = tid % C4, rg = tid / C4;
+  const bool proj = rg < RG;              // threads past RG * C4 have no share
+  float4 wv[UNROLL];
 #pragma unroll
-  for (int u = 0; u < UNROLL; ++u)
-    wv[u] = (m_lo + u < m_hi && j < head_dim) ? wg[(size_t)(m_lo + u) * head_dim + j] : 0.f;
+  for (int u = 0; u < UNROLL; ++u) {
+    const int m = rg + RG * u;
+    wv[u] = (proj && m < rank) ? *reinterpret_cast<const float4*>(wg + (size_t)m * head_dim + 4 * c4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   // the RoPE key (wave 0 of the group-0 block): dims lane + 64 k (d_R <= 256)
   const bool rope_wave = g == 0 && wave == 0 && rope_dim > 0;
   float xr[4] = {};
@@ -85,20 +87,32 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   const int sr = slot_row;
   if (sr < 0) return;  // uniform: nothing is written for a rejected token
 
-  // projected key of group g over this wave's slice
-  if (rs < nrs) {
-    float acc = 0.f;
-    for (int m0 = m_lo; m0 < m_hi; m0 += UNROLL) {
-      if (m0 != m_lo) {
+  // projected key of group g: this thread's rows, then the row groups' partial
+  // keys in LDS
+  if (proj) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u0 = 0; rg + RG * u0 < rank; u0 += UNROLL) {
+      if (u0 > 0) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-          wv[u] = (m0 + u < m_hi && j < head_dim) ? wg[(size_t)(m0 + u) * head_dim + j] : 0.f;
+        for (int u = 0; u < UNROLL; ++u) {
+          const int m = rg + RG * (u0 + u);
+          wv[u] = m < rank ? *reinterpret_cast<const float4*>(wg + (size_t)m * head_dim + 4 * c4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        if (m0 + u < m_hi) acc = fmaf(cs[m0 + u], wv[u], acc);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int m = rg + RG * (u0 + u);
+        if (m < rank) {
+          const float c = cs[m];
+          acc.x = fmaf(c, wv[u].x, acc.x);
+          acc.y = fmaf(c, wv[u].y, acc.y);
+          acc.z = fmaf(c, wv[u].z, acc.z);
+          acc.w = fmaf(c, wv[u].w, acc.w);
+        }
+      }
     }
-    if (j < head_dim) part[rs][j] = acc;
+    *reinterpret_cast<float4*>(&part[rg * head_dim + 4 * c4]) = acc;
   }
 
   // the latent as stored and the RoPE key (group-0 block), after the
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   float ss = 0.f;
   for (int j = tid; j < head_dim; j += 64 * WAVES) {
     float k = 0.f;
-    for (int w = 0; w < nrs; ++w) k += part[w][j];
+    for (int w = 0; w < RG; ++w) k += part[w * head_dim + j];
     ss = fmaf(k, k, ss);
   }
   ss = wave_sum(ss);
