@@ -32,11 +32,12 @@
 //                token, so a partial page reads zeros beyond it; an invalid
 //                page entry reads zeros throughout.  The loads are spread over
 //                the QK products.
-//   QK           S_c^T[32 tok x 32 heads] = C[32 x 512] . q~^T  (v_mfma_f32_32x32x16_bf16,
-//                A = latent rows from LDS, B = q~ in registers), then the
-//                RoPE dot R^T = K^R . q^R^T and the factor tile F^T = alpha^k
-//                alpha^q^T (v_mfma_f32_32x32x2f32); S = S_c F + R, one fused
-//                multiply-add per logit, in the first softmax steps.
+//   QK           the RoPE dot R^T = K^R . q^R^T and the factor tile F^T =
+//                alpha^k alpha^q^T (v_mfma_f32_32x32x2f32) first, off the path
+//                to the softmax, then S_c^T[32 tok x 32 heads] = C[32 x 512] . q~^T
+//                (v_mfma_f32_32x32x16_bf16, A = latent rows from LDS, B = q~ in
+//                registers); S = S_c F + R, one fused multiply-add per logit,
+//                in the first softmax steps.
 //   softmax      base 2 against a per-head reference fixed at the first
 //                visible tokens of the split, so the accumulator is never
 //                rescaled inside the loop.  QK-norm bounds the logits, so the
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
         // factor tile F; past the last stage S_c = F = 0 and R = -inf
         f32x16 sc = {}, rp = {}, fac = {};
         if (has_qk) {
-          // ---- QK: S_c^T[32 tok x 32 heads] over the 512 latents, then RoPE and F ----
+          // ---- QK: RoPE and F, then S_c^T[32 tok x 32 heads] over the 512 latents ----
           // Row read of token l32, chunk 2 kk + hh:
           //   [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8)
           // RoPE row read, chunk 2 kk + hh (kk < 4):
@@ -482,9 +483,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < DR / 16; ++j) rx[j] = rp_b ^ (32u * j);
           }
-          // Content products S_c over the 512 latents, then the RoPE dot R^T =
-          // K^R . q^R^T.  Without the inverse-RMS factors R accumulates onto
-          // S_c.  With them R goes into an accumulator of its own and the tile
+          // The RoPE dot R^T = K^R . q^R^T, then the content products S_c over
+          // the 512 latents.  Without the inverse-RMS factors S_c accumulates
+          // onto R.  With them R has an accumulator of its own and the tile
           // F = alpha^k alpha^q (token by head) is one float32 outer product on
           // the matrix core (outer32) from alpha^k of token l % 32 (one LDS
           // read) and this lane's alpha^q; S = S_c F + R, one fused
@@ -497,6 +498,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
             float ak_row = 0.f;
             if (USE_ALPHA) ak_row = st_alpha[g * ST + l32];
             constexpr int NK = R / 16;
+            // the RoPE products (and F) first: they do not depend on S_c, so the
+            // softmax can start as soon as the content chain ends
+            if (USE_ALPHA) {
+#pragma unroll
+              for (int kk = 0; kk < DR / 16; ++kk) rp = mfma(rope_a[kk], qrb[kk], rp);
+              fac = outer32(ak_row, aq_col);
+            } else {
+#pragma unroll
+              for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
+            }
             bf16x8 abuf[QK_AHEAD];
             auto rd = [&](int n) { return lds_read16(lds0 + qx[n & 7] + 256 * (n >> 3)); };
 #pragma unroll
@@ -507,14 +518,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
               if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
               sc = mfma(a, qb[n], sc);
               if (n % 3 == 1 && n / 3 < LOADS) load(pl, n / 3);
-            }
-            if (USE_ALPHA) {
-              fac = outer32(ak_row, aq_col);
-#pragma unroll
-              for (int kk = 0; kk < DR / 16; ++kk) rp = mfma(rope_a[kk], qrb[kk], rp);
-            } else {
-#pragma unroll
-              for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
             }
           }
         }
