@@ -217,6 +217,11 @@ def main():
         r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
         r.decode(flags)
 
+    def attn_proj(k, flags=0):
+        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
+        r.decode(flags)
+        r.combine_project()
+
     # eager warm-up (also the reference for the graph check below)
     for k in range(args.warmup):
         step(k)
@@ -294,11 +299,13 @@ def main():
     graphs = [capture(dec, n_dec), capture(attn, n_dec)]
     if not args.no_overhead:
         graphs.append(capture(dec, n_dec, Q.QKN_DECODE_NO_ALPHA))
+    # decode + the combine with the value up-projection (qkn_mla_combine_project)
+    graphs.append(capture(attn_proj, n_dec))
     warm(graphs[0])
     times = [t / n_dec for t in timed(graphs, reps=15)]
-    dec_ms, attn_ms = times[0], times[1]
+    dec_ms, attn_ms, proj_ms = times[0], times[1], times[-1]
     log(f"step {ms_per_step * 1e3:.1f} us, decode kernel {dec_ms * 1e3:.1f} us, "
-        f"decode+combine {attn_ms * 1e3:.1f} us")
+        f"decode+combine {attn_ms * 1e3:.1f} us, decode+combine_project {proj_ms * 1e3:.1f} us")
     overhead = None
     if not args.no_overhead:
         overhead = round((dec_ms / times[2] - 1.0) * 100.0, 2)
@@ -332,6 +339,7 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_combine_us": round(attn_ms * 1e3, 2),
+        "decode_combine_project_us": round(proj_ms * 1e3, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "qknorm_overhead_pct": overhead,
         "higher_is_better": True,

@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 2
+#define QKN_MLA_ABI_VERSION 3
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -219,10 +219,43 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
  *   in: o_partial [B,s_q,H,num_splits,r] (partial dtype),
  *       lse_partial [B,s_q,H,num_splits] float32
  *   out: o_latent [B, s_q, H, r] float32, lse [B, s_q, H] float32 (natural log).
- *   The value up-projection o = o_latent . W^V_g is left to the caller.
+ *   qkn_mla_combine_project also applies the value up-projection.
  */
 QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream);
+
+/* Flags of qkn_mla_combine_project.  o_latent and lse are the same bits in
+ * every form; o is within the same bound (the forms divide the reduction
+ * among waves differently) and the same bits on every run of one form. */
+#define QKN_PROJECT_FUSED 1u    /* one launch (merge and products per block) where
+                                   its shape conditions hold, whatever the size */
+#define QKN_PROJECT_TWO_PASS 2u /* qkn_mla_combine, then the products */
+
+/*
+ * qkn_mla_combine_project -- qkn_mla_combine followed by the value
+ * up-projection of every query row.
+ *   Source: on the absorbed path the attention-weighted sum is formed in
+ *   latent space and the head's value up-projection is applied to it once
+ *   (QK-Normed MLA summary, the absorbed form of the problem statement; GQLA
+ *   summary, section 2, the absorbed MLA path).
+ *
+ *     o_latent, lse  exactly as qkn_mla_combine writes them (same bits);
+ *     o[b,i,h,:]     = o_latent[b,i,h,:] . W^V_{g(h)}     (d_v = head_dim)
+ *   in: o_partial, lse_partial as for qkn_mla_combine;
+ *       w_v [G, r, head_dim] float32 (row m of W^V_g maps latent entry m).
+ *   out: o_latent [B,s_q,H,r], lse [B,s_q,H], o [B,s_q,H,head_dim], float32.
+ *   The products run on the matrix cores with both operands split into
+ *   bf16 hi + lo words (each product within 3 * 2^-16 of exact, float32
+ *   sums) when r is a multiple of 128 up to 512, head_dim is 32, 64, 128 or
+ *   256 and H/G is a multiple of 32; otherwise in float32 on the vector ALUs.
+ *   With half partials, at most 16 splits and enough rows (automatic), or with
+ *   QKN_PROJECT_FUSED, the merge and the products share one launch; otherwise
+ *   qkn_mla_combine runs first.  flags: QKN_PROJECT_* bits.
+ */
+QKN_API int qkn_mla_combine_project(const qkn_mla_dims* dims, int32_t num_splits,
+                            const void* o_partial, const float* lse_partial,
+                            const float* w_v, float* o_latent, float* lse, float* o,
+                            uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 QKN_OK = 0
 QKN_F32 = 0
 QKN_BF16 = 1
@@ -31,6 +31,8 @@ QKN_DECODE_NO_ALPHA = 1
 QKN_DECODE_FORCE_GENERIC = 2
 QKN_FLAG_INDEX = 1
 QKN_FLAG_PARTIAL_RANGE = 2
+QKN_PROJECT_FUSED = 1
+QKN_PROJECT_TWO_PASS = 2
 PAGE_SIZE = 64
 
 _c_int32 = ctypes.c_int32
@@ -87,6 +89,8 @@ def library() -> ctypes.CDLL:
                                        P, P, P, P]
         lib.qkn_mla_combine.restype = ctypes.c_int
         lib.qkn_mla_combine.argtypes = [D, _c_int32, P, P, P, P, P]
+        lib.qkn_mla_combine_project.restype = ctypes.c_int
+        lib.qkn_mla_combine_project.argtypes = [D, _c_int32, P, P, P, P, P, P, ctypes.c_uint32, P]
         if lib.qkn_mla_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qkn_mla_abi_version()}, "
                                f"this binding needs {ABI_VERSION}: rebuild it")
@@ -97,7 +101,7 @@ def library() -> ctypes.CDLL:
 EXPORTED_SYMBOLS = (
     "qkn_mla_abi_version", "qkn_status_string", "qkn_mla_check_dims",
     "qkn_mla_decode_kernel_kind", "qkn_mla_absorb_query", "qkn_mla_append",
-    "qkn_mla_decode", "qkn_mla_combine",
+    "qkn_mla_decode", "qkn_mla_combine", "qkn_mla_combine_project",
 )
 
 
@@ -246,3 +250,21 @@ def qkn_mla_combine(dims: Dims, num_splits: int, o_partial, lse_partial, o_laten
         _ptr(lse, "lse", f32, rows),
         ctypes.c_void_p(_stream_ptr(stream)))
     _check("qkn_mla_combine", st)
+
+
+def qkn_mla_combine_project(dims: Dims, num_splits: int, o_partial, lse_partial, w_v, o_latent,
+                            lse, o, flags: int = 0, stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    f32 = torch.float32
+    P = int(num_splits)
+    st = library().qkn_mla_combine_project(
+        ctypes.byref(d), P,
+        _ptr(o_partial, "o_partial", partial_torch_dtype(d), rows * P * d.rank),
+        _ptr(lse_partial, "lse_partial", f32, rows * P),
+        _ptr(w_v, "w_v", f32, d.groups * d.rank * d.head_dim),
+        _ptr(o_latent, "o_latent", f32, rows * d.rank),
+        _ptr(lse, "lse", f32, rows),
+        _ptr(o, "o", f32, rows * d.head_dim),
+        ctypes.c_uint32(int(flags)), ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_combine_project", st)

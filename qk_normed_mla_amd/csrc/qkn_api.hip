@@ -144,4 +144,20 @@ int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_
                                         static_cast<hipStream_t>(stream)));
 }
 
+int qkn_mla_combine_project(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
+                            const float* lse_partial, const float* w_v, float* o_latent,
+                            float* lse, float* o, uint32_t flags, void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return QKN_ERR_INVALID_ARG;
+  if (flags & ~(QKN_PROJECT_FUSED | QKN_PROJECT_TWO_PASS)) return QKN_ERR_INVALID_ARG;
+  if (!o_partial || !lse_partial || !w_v || !o_latent || !lse || !o) return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {o_partial, lse_partial, w_v, o_latent, lse, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_combine_project(*dims, num_splits, o_partial, lse_partial, w_v,
+                                                o_latent, lse, o, flags,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

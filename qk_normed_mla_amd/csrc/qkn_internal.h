@@ -151,5 +151,9 @@ hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStr
 
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);
+bool project_mfma_applies(const qkn_mla_dims& d);
+hipError_t launch_combine_project(const qkn_mla_dims& d, int num_splits, const void* o_part,
+                                  const float* lse_part, const float* w_v, float* o_lat,
+                                  float* lse, float* o, uint32_t flags, hipStream_t s);
 
 }  // namespace qkn

@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 from . import (QKN_BF16, PAGE_SIZE, Dims, cache_torch_dtype, dims_for, partial_torch_dtype,
-               qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine, qkn_mla_decode)
+               qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine, qkn_mla_combine_project,
+               qkn_mla_decode)
 
 
 def _dev(x, device, dtype=None):
@@ -42,6 +43,7 @@ class DecodeRunner:
         B, sq, H = wl.batch, wl.s_q, wl.heads
         f32 = torch.float32
         self.w_k = _dev(inputs["w_k"], dev)
+        self.w_v = _dev(inputs["w_v"], dev)
         self.gamma_q = _dev(inputs["gamma_q"], dev)
         self.gamma_k = _dev(inputs["gamma_k"], dev)
         self.gamma_qr = _dev(inputs["gamma_qr"], dev)
@@ -86,6 +88,7 @@ class DecodeRunner:
         self.alloc_partials(self.num_splits)
         self.o_latent = torch.empty((B, sq, H, wl.rank), dtype=f32, device=dev)
         self.lse = torch.empty((B, sq, H), dtype=f32, device=dev)
+        self.o = torch.empty((B, sq, H, wl.head_dim), dtype=f32, device=dev)
         self.err_flag = torch.zeros((1,), dtype=torch.int32, device=dev)
 
     def alloc_partials(self, num_splits: int):
@@ -134,6 +137,11 @@ class DecodeRunner:
     def combine(self, stream=None):
         qkn_mla_combine(self.dims, self.num_splits, self.o_partial, self.lse_partial,
                         self.o_latent, self.lse, stream)
+
+    def combine_project(self, flags: int = 0, stream=None):
+        """The combine and the value up-projection into self.o."""
+        qkn_mla_combine_project(self.dims, self.num_splits, self.o_partial, self.lse_partial,
+                                self.w_v, self.o_latent, self.lse, self.o, flags, stream)
 
     def prepare(self):
         """The query side and the append of the new tokens."""

@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 8, syms
+    assert len(syms) == 9, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 2
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 3
     for st in (0, -1, -2, -3, -4):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -125,3 +125,25 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         Q.qkn_mla_combine(d, 1, torch.zeros(8 * 64), torch.zeros(8), torch.zeros(8 * 64),
                           torch.zeros(8))
+
+
+def test_combine_project_rejects_bad_arguments():
+    """Host-side checks of qkn_mla_combine_project run before anything touches
+    a device: bad flags, split counts and missing or misaligned pointers."""
+    lib = Q.library()
+    d = good_dims()
+    ok = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected first
+    bad = ctypes.c_void_p((1 << 20) + 4)
+
+    def call(num_splits=8, flags=0, w_v=ok, o=ok, o_lat=ok):
+        return lib.qkn_mla_combine_project(ctypes.byref(d), num_splits, ok, ok, w_v, o_lat, ok, o,
+                                           ctypes.c_uint32(flags), None)
+    assert call(flags=4) == -1
+    assert call(num_splits=0) == -1
+    assert call(num_splits=5000) == -1
+    assert call(w_v=None) == -1
+    assert call(o=None) == -1
+    assert call(o_lat=None) == -1
+    assert call(o=bad) == -3
+    d.groups = 3
+    assert call() == -1

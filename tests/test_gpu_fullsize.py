@@ -4,7 +4,8 @@ benchmark times (its default split count), on sampled outputs.
 The whole step runs on the GPU (query absorption, append of the new tokens,
 split-KV decode, combine) over the full synthetic cache; the oracle then
 computes a sample of the output rows one by one from the float32 inputs by the
-explicit path (materialised keys, post-projection RMSNorm).  The sample covers
+explicit path (materialised keys, post-projection RMSNorm), including the
+value up-projection of qkn_mla_combine_project.  The sample covers
 the first, middle and last sequence, the first and last query token, and heads
 at both edges of every 32-head wave and every KV group.
 """
@@ -43,19 +44,27 @@ def test_full_size_sampled_rows(name):
     assert int(r.err_flag.item()) == 0
     o_lat = r.o_latent.cpu().numpy()
     lse = r.lse.cpu().numpy()
+    # the same merge with the value up-projection (fused or two-pass by size)
+    r.combine_project()
+    torch.cuda.synchronize()
+    assert np.array_equal(r.o_latent.cpu().numpy().view(np.int32), o_lat.view(np.int32))
+    o = r.o.cpu().numpy()
     del r
     torch.cuda.empty_cache()
 
     tol = TOL_E2E[wl.cache_dtype]
     heads = np.array([h for h in EDGE_HEADS if h < wl.heads])
-    worst, worst_lse, n = 0.0, 0.0, 0
+    worst, worst_lse, worst_o, n = 0.0, 0.0, 0.0, 0
     for b in sorted({0, wl.batch // 2, wl.batch - 1}):
         for i in sorted({0, wl.s_q - 1}):
             e = O.explicit_rows(wl, inp, b, i, heads=heads)
             for k, h in enumerate(heads):
                 worst = max(worst, row_err(o_lat[b, i, h], e["o_lat"][k]))
                 worst_lse = max(worst_lse, abs(float(lse[b, i, h]) - float(e["lse"][k])))
+                worst_o = max(worst_o, row_err(o[b, i, h], e["o"][k]))
                 n += 1
-    print(f"  {n} rows: latent row err {worst:.2e}, lse err {worst_lse:.2e}", flush=True)
+    print(f"  {n} rows: latent row err {worst:.2e}, lse err {worst_lse:.2e}, "
+          f"o row err {worst_o:.2e}", flush=True)
     assert worst <= tol
+    assert worst_o <= 2 * tol
     assert worst_lse <= tol
