@@ -162,18 +162,95 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
   }
 }
 
+constexpr int kBulkMinTokens = 4096;  // from here on alpha^k is one matrix product per group
+
+// The stores of the bulk path (bf16 cache): one wave per token for the slot,
+// the latent (16-byte stores of 8 bf16 words) and the RoPE key, with the
+// operations of append_kernel in the same order; alpha^k comes from
+// append_alpha_mfma.
+__global__ __launch_bounds__(256) void append_store_bulk(
+    const float* __restrict__ c_new, const float* __restrict__ k_rope_new,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_table, const float* __restrict__ gamma_kr,
+    uint16_t* __restrict__ kv, int32_t* __restrict__ err_flag, int n_tokens, int batch,
+    int max_pages, int num_pages, int rank, int rope_dim, float eps, float theta) {
+  __shared__ float xn_all[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 4 + wave;
+  if (n >= n_tokens) return;
+  int sr = -1;
+  const int b = seq_idx[n], p = pos[n];
+  if (b >= 0 && b < batch && p >= 0 && p < max_pages * QKN_MLA_PAGE_SIZE) {
+    const int page = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
+    if (page >= 0 && page < num_pages) sr = page * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
+  }
+  if (sr < 0) {
+    if (lane == 0 && err_flag) atomicOr(err_flag, QKN_FLAG_INDEX);
+    return;
+  }
+  const int row_stride = rank + rope_dim;
+  uint16_t* row = kv + (size_t)sr * row_stride;
+  for (int m0 = 8 * lane; m0 < rank; m0 += 8 * 64) {
+    const float4* src = reinterpret_cast<const float4*>(c_new + (size_t)n * rank + m0);
+    const float4 a = src[0], c = src[1];
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    uint4 w;
+    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wp[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(row + m0) = w;
+  }
+  if (rope_dim == 0) return;
+  float xr[4] = {};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (lane + 64 * k < rope_dim) xr[k] = k_rope_new[(size_t)n * rope_dim + lane + 64 * k];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ss = fmaf(xr[k], xr[k], ss);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)rope_dim + eps);
+  float* xn = xn_all[wave];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (lane + 64 * k < rope_dim) xn[lane + 64 * k] = xr[k] * inv * gamma_kr[lane + 64 * k];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  const int half = rope_dim / 2;
+  uint16_t* out = row + rank;
+  for (int jj = lane; jj < half; jj += 64) {
+    const float x1 = xn[jj], x2 = xn[jj + half];
+    float c = 1.f, s = 0.f;
+    if (theta != 0.f) rope_cos_sin(p, jj, rope_dim, theta, &c, &s);
+    out[jj] = f32_to_bf16(x1 * c - x2 * s);
+    out[jj + half] = f32_to_bf16(x2 * c + x1 * s);
+  }
+}
+
 template <typename CacheT>
 hipError_t launch_typed(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new,
                         const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
                         const int32_t* block_table, const float* w_k, const float* gamma_kr,
-                        void* kv_cache, float* alpha_k_cache, int32_t* err_flag, hipStream_t s) {
+                        void* kv_cache, float* alpha_k, int32_t* err_flag, hipStream_t s) {
   if (d.head_dim > MAX_HEAD_DIM || d.rope_dim > 256) return hipErrorInvalidValue;
-  dim3 grid(n_tokens, d.groups);
   const size_t shmem = (size_t)d.rank * sizeof(float);
-  hipLaunchKernelGGL(append_kernel<CacheT>, grid, dim3(64 * WAVES), shmem, s, c_new, k_rope_new,
-                     seq_idx, pos, block_table, w_k, gamma_kr, static_cast<CacheT*>(kv_cache),
-                     alpha_k_cache, err_flag, d.batch, d.max_pages_per_seq, d.num_pages, d.rank,
-                     d.head_dim, d.rope_dim, d.groups, d.eps, d.rope_theta);
+  if (n_tokens >= kBulkMinTokens && append_bulk_applies(d)) {
+    // stores and flags per token, then alpha^k of all tokens on the matrix cores
+    hipLaunchKernelGGL(append_store_bulk, dim3(cdiv(n_tokens, 4)), dim3(256), 0, s, c_new,
+                       k_rope_new, seq_idx, pos, block_table, gamma_kr,
+                       static_cast<uint16_t*>(kv_cache), err_flag, n_tokens, d.batch,
+                       d.max_pages_per_seq, d.num_pages, d.rank, d.rope_dim, d.eps, d.rope_theta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_append_alpha_bulk(d, n_tokens, c_new, seq_idx, pos, block_table, w_k, alpha_k, s);
+  }
+  dim3 grid(n_tokens, d.groups);
+  hipLaunchKernelGGL(append_kernel<CacheT>, grid, dim3(64 * WAVES), shmem, s, c_new,
+                     k_rope_new, seq_idx, pos, block_table, w_k, gamma_kr,
+                     static_cast<CacheT*>(kv_cache), alpha_k, err_flag, d.batch,
+                     d.max_pages_per_seq, d.num_pages, d.rank, d.head_dim, d.rope_dim, d.groups,
+                     d.eps, d.rope_theta);
   return hipGetLastError();
 }
 

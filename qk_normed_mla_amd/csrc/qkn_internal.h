@@ -151,6 +151,11 @@ hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStr
 
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);
+bool append_bulk_applies(const qkn_mla_dims& d);
+hipError_t launch_append_alpha_bulk(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new,
+                                    const int32_t* seq_idx, const int32_t* pos,
+                                    const int32_t* block_table, const float* w_k, float* alpha_k,
+                                    hipStream_t s);
 bool project_mfma_applies(const qkn_mla_dims& d);
 hipError_t launch_combine_project(const qkn_mla_dims& d, int num_splits, const void* o_part,
                                   const float* lse_part, const float* w_v, float* o_lat,

@@ -117,6 +117,17 @@ class DecodeRunner:
             qkn_mla_append(self.dims, c, kr, seq, pos, self.block_table, self.w_k, self.gamma_kr,
                            self.kv, self.alpha_k, self.err_flag, stream)
 
+    def history_inputs(self, limit: int = 1 << 18):
+        """Device copies of the first ``limit`` history tokens' append inputs
+        (latent, RoPE key, sequence, position)."""
+        r = np.asarray(self._old_rows)[:limit]
+        return (_dev(self.inp["c"][r], self.device), _dev(self.inp["k_rope"][r], self.device),
+                _dev(self._all_seq[r], self.device), _dev(self._all_pos[r], self.device))
+
+    def append_tokens(self, c, kr, seq, pos, stream=None):
+        qkn_mla_append(self.dims, c, kr, seq, pos, self.block_table, self.w_k, self.gamma_kr,
+                       self.kv, self.alpha_k, self.err_flag, stream)
+
     def fill_history(self, stream=None):
         """Append every token except the s_q newest of each sequence."""
         if len(self._old_rows):
