@@ -154,7 +154,11 @@ QKN_API int qkn_mla_absorb_query(const qkn_mla_dims* dims, const float* q, const
  *     kv_cache[page][row][r:r+d_R] = RoPE(gamma_kr * k_rope_new[n] / RMS, pos[n])
  *     alpha_k_cache[page][row][g]  = 1 / sqrt(mean((c . W^K_g)^2) + eps), g < G,
  *   where c is the latent AS STORED (so the scalar matches the cached latent).
- *   The projected key c . W^K_g is formed in registers only.
+ *   The projected key c . W^K_g is formed in registers only.  From 4096
+ *   tokens in one call (bf16 cache, d = 32, 64, 128 or 256) the keys of all
+ *   tokens are one matrix product per group on the matrix cores (the stored
+ *   bf16 latent times W^K_g split into three bf16 words: exact products,
+ *   float32 sums); the stored words are formed as for fewer tokens.
  *
  *   c_new [n_tokens, r], k_rope_new [n_tokens, d_R]  float32
  *   seq_idx, pos [n_tokens] int32;  block_table [B, max_pages_per_seq] int32
