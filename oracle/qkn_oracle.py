@@ -280,7 +280,7 @@ def absorbed_rows(wl, inp, b: int, i: int, heads=None) -> dict:
         p, lse = _softmax_stats(logits)
         o_lat = p @ C
         out_lat[sel] = o_lat
-        out_o[sel] = o_lat @ np.asarray(inp["w_v"][g], dtype=np.float64)
+        out_o[sel] = value_up_projection(wl, o_lat, inp["w_v"], hs)
         out_lse[sel] = lse
     return {"o": out_o, "o_lat": out_lat, "lse": out_lse}
 

@@ -105,6 +105,69 @@ def check_rope_properties():
     assert np.array_equal(O.rope(x, 99, 0.0), x)
 
 
+def check_rope_frequency_ladder():
+    """Every pair's frequency, not only the first: against the rotary embedding
+    of the transformers library (Llama's default rotary parameters, NeoX
+    rotate-half pairs (j, j + d_R/2)), and against angles worked out by hand.
+
+    The library computes its angles in float32, so positions stay small
+    (angle error ~1e-6) while a wrong ladder moves some angle by O(1)."""
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as ML
+
+    rng = np.random.default_rng(30)
+    for dR in (4, 8, 16, 64):
+        cfg = LlamaConfig(hidden_size=4 * dR, num_attention_heads=4, head_dim=dR,
+                          rope_theta=10000.0)
+        emb = ML.LlamaRotaryEmbedding(cfg)
+        pos = np.array([0, 1, 2, 3, 7, 13, 31, 50], dtype=np.int64)
+        x = rng.standard_normal((1, 1, len(pos), dR))
+        cos, sin = emb(torch.from_numpy(x), torch.from_numpy(pos)[None, :])
+        ref, _ = ML.apply_rotary_pos_emb(torch.from_numpy(x), torch.from_numpy(x), cos, sin)
+        got = O.rope(x[0, 0], pos, 10000.0)
+        assert np.allclose(got, ref[0, 0].numpy(), rtol=0, atol=2e-5), \
+            f"d_R={dR}: RoPE differs from the library by {np.max(np.abs(got - ref[0, 0].numpy()))}"
+    # Hand-worked angles at theta = 10000: the pair j of a d_R-wide block turns
+    # at 10000^(-2j/d_R) radians per position, so
+    #   d_R = 4, j = 1: 10^-2  -> position 100 turns it by exactly 1 rad;
+    #   d_R = 8, j = 1: 10^-1  -> position 10 gives 1 rad; j = 3: 10^-3 -> position 1000.
+    for dR, j, pos in ((4, 1, 100), (8, 1, 10), (8, 2, 100), (8, 3, 1000), (16, 4, 100)):
+        half = dR // 2
+        e = np.zeros(dR)
+        e[j] = 1.0
+        got = O.rope(e, pos, 10000.0)
+        want = np.zeros(dR)
+        want[j], want[j + half] = math.cos(1.0), math.sin(1.0)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (dR, j, pos, got)
+        # the partner coordinate turns the other way round
+        e2 = np.zeros(dR)
+        e2[j + half] = 1.0
+        want2 = np.zeros(dR)
+        want2[j], want2[j + half] = -math.sin(1.0), math.cos(1.0)
+        assert np.allclose(O.rope(e2, pos, 10000.0), want2, rtol=0, atol=1e-12)
+
+
+def check_value_up_projection(name):
+    """The value side of the absorbed path, o = o^lat W^V_g, against the explicit
+    path's o = sum_t p_t (c_t W^V_g) with the values materialised: equal by
+    linearity, to float64 rounding, for every head of every group."""
+    wl = small(name)
+    inp = W.make_inputs(wl, seed=31)
+    heads = np.arange(wl.heads)
+    worst = 0.0
+    for b in range(wl.batch):
+        for i in range(wl.s_q):
+            e = O.explicit_rows(wl, inp, b, i)
+            o = O.value_up_projection(wl, e["o_lat"], inp["w_v"], heads)
+            worst = max(worst, rel_err(o, e["o"]))
+            # a subset of heads, out of order, maps each head to its own group
+            sub = heads[::-7]
+            o_sub = O.value_up_projection(wl, e["o_lat"][sub], inp["w_v"], sub)
+            worst = max(worst, rel_err(o_sub, e["o"][sub]))
+    assert worst <= 1e-10, f"{name}: value up-projection vs explicit values {worst:.3e}"
+    return worst
+
+
 # ---------------------------------------------------------------------------
 # the method: exact equivalence and closed forms
 # ---------------------------------------------------------------------------

@@ -49,6 +49,34 @@ def _rope_sign_error(x, pos, theta):
     return np.concatenate([y[..., :half], y2[..., half:]], axis=-1)
 
 
+def _rope_wrong_ladder(x, pos, theta):
+    # frequencies theta^(-j/d_R) instead of theta^(-2j/d_R): the first pair is
+    # still right, every other pair turns too fast
+    x = np.asarray(x, dtype=np.float64)
+    if theta == 0.0 or x.shape[-1] == 0:
+        return x.copy()
+    dR = x.shape[-1]
+    half = dR // 2
+    inv_freq = float(theta) ** (-np.arange(half, dtype=np.float64) / dR)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * np.cos(ang) - x2 * np.sin(ang),
+                           x2 * np.cos(ang) + x1 * np.sin(ang)], axis=-1)
+
+
+def _value_projection_group0(wl, o_lat, w_v, heads):
+    # every head takes group 0's W^V
+    return np.stack([np.asarray(o_lat[k], dtype=np.float64) @ np.asarray(w_v[0], dtype=np.float64)
+                     for k in range(len(heads))])
+
+
+def _value_projection_wrong_group_map(wl, o_lat, w_v, heads):
+    # heads dealt to groups round-robin (h mod G) instead of in blocks
+    return np.stack([np.asarray(o_lat[k], dtype=np.float64)
+                     @ np.asarray(w_v[int(h) % wl.groups], dtype=np.float64)
+                     for k, h in enumerate(heads)])
+
+
 def _bf16_truncate(x):
     x = np.ascontiguousarray(x, dtype=np.float32)
     return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
@@ -113,6 +141,13 @@ MUTATIONS = {
     "sum instead of mean in RMS": ("inv_rms", _inv_rms_sum_not_mean,
                                    [P.check_rmsnorm_against_torch]),
     "RoPE half rotated backwards": ("rope", _rope_sign_error, [P.check_rope_properties]),
+    "RoPE frequency ladder theta^(-j/d_R)": ("rope", _rope_wrong_ladder,
+                                             [P.check_rope_frequency_ladder]),
+    "value projection uses group 0's W^V": ("value_up_projection", _value_projection_group0,
+                                            [lambda: P.check_value_up_projection("grouped")]),
+    "value projection maps heads to groups round-robin": (
+        "value_up_projection", _value_projection_wrong_group_map,
+        [lambda: P.check_value_up_projection("grouped")]),
     "bf16 truncation instead of RNE": ("f32_to_bf16_bits", _bf16_truncate,
                                        [P.check_bf16_against_torch]),
     "causal window off by one": ("visible_count", _visible_off_by_one,

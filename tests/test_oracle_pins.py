@@ -22,6 +22,15 @@ def test_rope_properties():
     P.check_rope_properties()
 
 
+def test_rope_frequency_ladder():
+    P.check_rope_frequency_ladder()
+
+
+@pytest.mark.parametrize("name", ["tiny", "grouped", "mtp"])
+def test_value_up_projection(name):
+    P.check_value_up_projection(name)
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_explicit_equals_absorbed(name):
     # the pages' exactness claim: both formulations agree in exact arithmetic
