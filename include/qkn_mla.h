@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 3
+#define QKN_MLA_ABI_VERSION 4
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -60,11 +60,15 @@ typedef enum {
   QKN_ERR_HIP = -4          /* the HIP runtime reported an error on launch    */
 } qkn_status;
 
-typedef enum { QKN_F32 = 0, QKN_BF16 = 1 } qkn_dtype;
+typedef enum { QKN_F32 = 0, QKN_BF16 = 1, QKN_F16 = 2 } qkn_dtype;
 
 /* Bits that qkn_mla_append and qkn_mla_decode OR into *err_flag. */
 #define QKN_FLAG_INDEX 1         /* an index, position, length or page entry out of range */
 #define QKN_FLAG_PARTIAL_RANGE 2 /* a half-precision split partial beyond +-65504 */
+#define QKN_FLAG_RESTART 4       /* informational, not an error: a split of the
+                                    matrix-core decode took its exact restart (a
+                                    logit outgrew the split's exponent reference
+                                    by more than 2^96); the result is unaffected */
 
 /* Flags of qkn_mla_decode. */
 #define QKN_DECODE_NO_ALPHA 1u      /* drop both inverse-RMS factors: plain absorbed
@@ -91,15 +95,34 @@ typedef struct {
 
 /*
  * Element type of the split-KV partials o_partial of qkn_mla_decode and
- * qkn_mla_combine ("partial dtype"): IEEE binary16 (half) when the cache is
- * bfloat16, float32 when it is float32.  A partial is a convex combination of
- * cached latent rows, so half keeps it to within 2^-11 of its own magnitude,
- * eight times finer than the bfloat16 rounding of the latents it is made of,
- * and halves the bytes the split-KV path writes and reads back.
+ * qkn_mla_combine ("partial dtype"), as qkn_mla_partial_dtype() returns it:
+ * today IEEE binary16 (QKN_F16) when the cache is bfloat16 and float32 when it
+ * is float32.  A partial is a convex combination of cached latent rows, so
+ * half keeps it to within 2^-11 of its own magnitude, eight times finer than
+ * the bfloat16 rounding of the latents it is made of, and halves the bytes
+ * the split-KV path writes and reads back.  Callers that do not need the
+ * partials themselves use qkn_mla_decode_attend with a workspace sized by
+ * qkn_mla_decode_workspace_bytes and need not know this type at all.
  */
 
 /* QKN_MLA_ABI_VERSION of the loaded library. */
 QKN_API int qkn_mla_abi_version(void);
+
+/* Partial dtype (QKN_F16 or QKN_F32) for these dims, or a negative qkn_status
+ * when the dims are invalid. */
+QKN_API int qkn_mla_partial_dtype(const qkn_mla_dims* dims);
+
+/*
+ * Bytes of device workspace qkn_mla_decode_attend needs for `num_splits`
+ * split-KV partitions: the partials o_partial [B, s_q, H, num_splits, r]
+ * (partial dtype) and lse_partial [B, s_q, H, num_splits] float32, each
+ * starting on a 256-byte boundary.  Returns 0 when the dims or num_splits are
+ * invalid (every valid request needs more than 0 bytes).
+ *   Source: the split-KV partitions whose partial results the log-sum-exp
+ *   combine merges (the long-context decode of the QK-Normed MLA summary,
+ *   "Resultados", reaching 256k tokens).
+ */
+QKN_API size_t qkn_mla_decode_workspace_bytes(const qkn_mla_dims* dims, int32_t num_splits);
 
 /* Static text for a qkn_status value. */
 QKN_API const char* qkn_status_string(int status);
@@ -199,7 +222,8 @@ QKN_API int qkn_mla_append(const qkn_mla_dims* dims, int32_t n_tokens, const flo
  *   QKN_FLAG_INDEX when a sequence length exceeds max_pages_per_seq * 64 (it
  *   is clamped) or a page entry is out of range (those tokens are skipped);
  *   QKN_FLAG_PARTIAL_RANGE when a half partial would exceed the half range
- *   (latent entries beyond +-65504 in the cache); it is then stored as +-inf.
+ *   (latent entries beyond +-65504 in the cache); it is then stored as +-inf;
+ *   QKN_FLAG_RESTART (informational) when a split took the exact restart.
  *   Products run on the matrix cores (bf16 operands, float32 accumulation)
  *   when qkn_mla_decode_kernel_kind() says 1, otherwise on the vector ALUs in
  *   float32.
@@ -227,6 +251,29 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
  */
 QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream);
+
+/*
+ * qkn_mla_decode_attend -- qkn_mla_decode followed by qkn_mla_combine, with
+ * the split partials in a caller-provided workspace.
+ *   Source: as for qkn_mla_decode and qkn_mla_combine.
+ *
+ *   Writes o_latent [B, s_q, H, r] and lse [B, s_q, H] (float32) with the same
+ *   bits as qkn_mla_decode into partials, then qkn_mla_combine of them, for
+ *   the same arguments and flags.  `workspace` is a device buffer of
+ *   `workspace_bytes` >= qkn_mla_decode_workspace_bytes(dims, num_splits)
+ *   bytes, 256-byte aligned, owned by the caller; its contents on entry do not
+ *   matter and on return are unspecified.  Two calls that share a workspace
+ *   must be ordered on one stream.  A workspace that is too small or
+ *   misaligned is rejected (QKN_ERR_INVALID_ARG / QKN_ERR_ALIGNMENT) before
+ *   anything is launched.  err_flag as for qkn_mla_decode.
+ */
+QKN_API int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde,
+                          const float* alpha_q, const void* q_rope_normed,
+                          const void* kv_cache, const float* alpha_k_cache,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t num_splits, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, float* o_latent, float* lse,
+                          int32_t* err_flag, void* stream);
 
 /* Flags of qkn_mla_combine_project.  o_latent and lse are the same bits in
  * every form; o is within the same bound (the forms divide the reduction

@@ -7,7 +7,8 @@ call fails, an exception is raised.
 
 The functions carry the names of the C entry points (include/qkn_mla.h):
 
-    qkn_mla_absorb_query, qkn_mla_append, qkn_mla_decode, qkn_mla_combine
+    qkn_mla_absorb_query, qkn_mla_append, qkn_mla_decode, qkn_mla_combine,
+    qkn_mla_decode_attend, qkn_mla_combine_project
 
 and check on the host that every tensor is a contiguous device tensor of the
 dtype and element count the kernels and their grids assume before launching.
@@ -23,14 +24,16 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 QKN_OK = 0
 QKN_F32 = 0
 QKN_BF16 = 1
+QKN_F16 = 2
 QKN_DECODE_NO_ALPHA = 1
 QKN_DECODE_FORCE_GENERIC = 2
 QKN_FLAG_INDEX = 1
 QKN_FLAG_PARTIAL_RANGE = 2
+QKN_FLAG_RESTART = 4
 QKN_PROJECT_FUSED = 1
 QKN_PROJECT_TWO_PASS = 2
 PAGE_SIZE = 64
@@ -78,6 +81,10 @@ def library() -> ctypes.CDLL:
         lib.qkn_status_string.argtypes = [ctypes.c_int]
         lib.qkn_mla_check_dims.restype = ctypes.c_int
         lib.qkn_mla_check_dims.argtypes = [D]
+        lib.qkn_mla_partial_dtype.restype = ctypes.c_int
+        lib.qkn_mla_partial_dtype.argtypes = [D]
+        lib.qkn_mla_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.qkn_mla_decode_workspace_bytes.argtypes = [D, _c_int32]
         lib.qkn_mla_decode_kernel_kind.restype = ctypes.c_int
         lib.qkn_mla_decode_kernel_kind.argtypes = [D, _c_int32, ctypes.c_uint32]
         lib.qkn_mla_absorb_query.restype = ctypes.c_int
@@ -87,6 +94,9 @@ def library() -> ctypes.CDLL:
         lib.qkn_mla_decode.restype = ctypes.c_int
         lib.qkn_mla_decode.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
                                        P, P, P, P]
+        lib.qkn_mla_decode_attend.restype = ctypes.c_int
+        lib.qkn_mla_decode_attend.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
+                                              P, ctypes.c_size_t, P, P, P, P]
         lib.qkn_mla_combine.restype = ctypes.c_int
         lib.qkn_mla_combine.argtypes = [D, _c_int32, P, P, P, P, P]
         lib.qkn_mla_combine_project.restype = ctypes.c_int
@@ -100,8 +110,9 @@ def library() -> ctypes.CDLL:
 
 EXPORTED_SYMBOLS = (
     "qkn_mla_abi_version", "qkn_status_string", "qkn_mla_check_dims",
+    "qkn_mla_partial_dtype", "qkn_mla_decode_workspace_bytes",
     "qkn_mla_decode_kernel_kind", "qkn_mla_absorb_query", "qkn_mla_append",
-    "qkn_mla_decode", "qkn_mla_combine", "qkn_mla_combine_project",
+    "qkn_mla_decode", "qkn_mla_decode_attend", "qkn_mla_combine", "qkn_mla_combine_project",
 )
 
 
@@ -129,9 +140,32 @@ def cache_torch_dtype(dims: Dims) -> torch.dtype:
     return torch.bfloat16 if dims.cache_dtype == QKN_BF16 else torch.float32
 
 
+_TORCH_OF = {QKN_F32: torch.float32, QKN_BF16: torch.bfloat16, QKN_F16: torch.float16}
+
+
 def partial_torch_dtype(dims: Dims) -> torch.dtype:
-    """Element type of the split-KV partials: half for a bf16 cache."""
-    return torch.float16 if dims.cache_dtype == QKN_BF16 else torch.float32
+    """Element type of the split-KV partials, as the library reports it."""
+    code = library().qkn_mla_partial_dtype(ctypes.byref(dims))
+    if code < 0:
+        raise QknError("qkn_mla_partial_dtype", code)
+    return _TORCH_OF[code]
+
+
+def decode_workspace_bytes(dims: Dims, num_splits: int) -> int:
+    """Device bytes qkn_mla_decode_attend needs for ``num_splits`` partitions."""
+    n = int(library().qkn_mla_decode_workspace_bytes(ctypes.byref(dims), int(num_splits)))
+    if n == 0:
+        raise QknError("qkn_mla_decode_workspace_bytes", -1)
+    return n
+
+
+def alloc_decode_workspace(dims: Dims, num_splits: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of the size qkn_mla_decode_workspace_bytes states
+    (torch's allocator returns 256-byte aligned blocks)."""
+    ws = torch.empty(decode_workspace_bytes(dims, num_splits), dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace not 256-byte aligned")
+    return ws
 
 
 def _stream_ptr(stream) -> int:
@@ -234,6 +268,35 @@ def qkn_mla_decode(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_
         _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
         ctypes.c_void_p(_stream_ptr(stream)))
     _check("qkn_mla_decode", st)
+
+
+def qkn_mla_decode_attend(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,
+                          block_table, seq_lens, num_splits: int, flags: int, workspace,
+                          o_latent, lse, err_flag=None, stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    need = decode_workspace_bytes(d, num_splits)
+    if workspace is None or workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 device tensor of at least {need} bytes")
+    st = library().qkn_mla_decode_attend(
+        ctypes.byref(d),
+        _ptr(q_tilde, "q_tilde", ct, rows * d.rank),
+        _ptr(alpha_q, "alpha_q", f32, rows),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(alpha_k_cache, "alpha_k_cache", f32, d.num_pages * PAGE_SIZE * d.groups),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", i32, d.batch),
+        int(num_splits), int(flags),
+        _ptr(workspace, "workspace", torch.uint8, workspace.numel()),
+        ctypes.c_size_t(workspace.numel()),
+        _ptr(o_latent, "o_latent", f32, rows * d.rank),
+        _ptr(lse, "lse", f32, rows),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_decode_attend", st)
 
 
 def qkn_mla_combine(dims: Dims, num_splits: int, o_partial, lse_partial, o_latent, lse,

@@ -481,13 +481,8 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
     const int hpg = d.heads / d.groups;
     const int rows_per_group = d.batch * d.s_q * hpg;
     dim3 grid(cdiv(rows_per_group, TM), cdiv(d.rank, TN), d.groups);
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&absorb_split),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, SPLIT_LDS);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&absorb_split), SPLIT_LDS);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(absorb_split, grid, dim3(64 * SW), SPLIT_LDS, s, q, q_rope, q_pos, w_k, gamma_q,
                        gamma_k, gamma_qr, static_cast<uint16_t*>(q_tilde), alpha_q,
                        static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,

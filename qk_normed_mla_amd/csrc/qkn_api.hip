@@ -2,6 +2,9 @@
 // Every check runs before any HIP call, so a rejected call touches no device.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "qkn_internal.h"
 
@@ -37,7 +40,66 @@ int check_dims(const qkn_mla_dims* d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QKN_OK : QKN_ERR_HIP; }
 
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// The partials of one qkn_mla_decode_attend call inside its workspace:
+// o_partial at 0, lse_partial at lse_offset, both on 256-byte boundaries.
+struct WorkspaceLayout {
+  size_t lse_offset, total;
+};
+WorkspaceLayout workspace_layout(const qkn_mla_dims& d, int num_splits) {
+  const size_t rows = (size_t)d.batch * d.s_q * d.heads * num_splits;
+  const size_t elem = d.cache_dtype == QKN_BF16 ? 2 : 4;  // the partial dtype
+  WorkspaceLayout w;
+  w.lse_offset = round256(rows * d.rank * elem);
+  w.total = w.lse_offset + round256(rows * 4);
+  return w;
+}
+
+// Checks of qkn_mla_decode's arguments (not the partials); returns the kernel
+// kind (0 generic, 1 matrix cores) or a negative status.
+int check_decode_args(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
+                      const void* q_rope_normed, const void* kv_cache,
+                      const float* alpha_k_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, int32_t num_splits, uint32_t flags) {
+  int kind = qkn_mla_decode_kernel_kind(dims, num_splits, flags);
+  if (kind < 0) return kind;
+  if (flags & ~(QKN_DECODE_NO_ALPHA | QKN_DECODE_FORCE_GENERIC)) return QKN_ERR_INVALID_ARG;
+  const bool rope = dims->rope_dim > 0;
+  if (!q_tilde || !alpha_q || !kv_cache || !alpha_k_cache || !block_table || !seq_lens)
+    return QKN_ERR_INVALID_ARG;
+  if (rope && !q_rope_normed) return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_tilde, alpha_q, kv_cache, alpha_k_cache, block_table, seq_lens};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  if (rope && !aligned16(q_rope_normed)) return QKN_ERR_ALIGNMENT;
+  return kind;
+}
+
+hipError_t launch_decode(int kind, const qkn_mla_dims& d, const qkn::DecodeArgs& a,
+                         hipStream_t s) {
+  return kind == 1 ? qkn::launch_decode_mfma(d, a, s) : qkn::launch_decode_generic(d, a, s);
+}
+
 }  // namespace
+
+namespace qkn {
+
+hipError_t set_lds_limit_once(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;  // (kernel, device)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& k : done)
+    if (k.first == fn && k.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(fn, dev);
+  return e;
+}
+
+}  // namespace qkn
 
 extern "C" {
 
@@ -55,6 +117,17 @@ const char* qkn_status_string(int status) {
 }
 
 int qkn_mla_check_dims(const qkn_mla_dims* dims) { return check_dims(dims); }
+
+int qkn_mla_partial_dtype(const qkn_mla_dims* dims) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  return dims->cache_dtype == QKN_BF16 ? QKN_F16 : QKN_F32;
+}
+
+size_t qkn_mla_decode_workspace_bytes(const qkn_mla_dims* dims, int32_t num_splits) {
+  if (check_dims(dims) != QKN_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return workspace_layout(*dims, num_splits).total;
+}
 
 int qkn_mla_decode_kernel_kind(const qkn_mla_dims* dims, int32_t num_splits, uint32_t flags) {
   int st = check_dims(dims);
@@ -110,25 +183,41 @@ int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const float* a
                    const float* alpha_k_cache, const int32_t* block_table,
                    const int32_t* seq_lens, int32_t num_splits, uint32_t flags,
                    void* o_partial, float* lse_partial, int32_t* err_flag, void* stream) {
-  int kind = qkn_mla_decode_kernel_kind(dims, num_splits, flags);
+  const int kind = check_decode_args(dims, q_tilde, alpha_q, q_rope_normed, kv_cache,
+                                     alpha_k_cache, block_table, seq_lens, num_splits, flags);
   if (kind < 0) return kind;
-  if (flags & ~(QKN_DECODE_NO_ALPHA | QKN_DECODE_FORCE_GENERIC)) return QKN_ERR_INVALID_ARG;
-  const bool rope = dims->rope_dim > 0;
-  if (!q_tilde || !alpha_q || !kv_cache || !alpha_k_cache || !block_table || !seq_lens ||
-      !o_partial || !lse_partial)
-    return QKN_ERR_INVALID_ARG;
-  if (rope && !q_rope_normed) return QKN_ERR_INVALID_ARG;
-  const void* ptrs[] = {q_tilde, alpha_q, kv_cache, alpha_k_cache, block_table, seq_lens,
-                        o_partial, lse_partial};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
-  if (rope && !aligned16(q_rope_normed)) return QKN_ERR_ALIGNMENT;
+  if (!o_partial || !lse_partial) return QKN_ERR_INVALID_ARG;
+  if (!aligned16(o_partial) || !aligned16(lse_partial)) return QKN_ERR_ALIGNMENT;
+  qkn::DecodeArgs a{q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache, block_table,
+                    seq_lens, o_partial, lse_partial, err_flag, num_splits,
+                    (flags & QKN_DECODE_NO_ALPHA) == 0};
+  return hip_status(launch_decode(kind, *dims, a, static_cast<hipStream_t>(stream)));
+}
+
+int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
+                          const void* q_rope_normed, const void* kv_cache,
+                          const float* alpha_k_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t num_splits, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, float* o_latent, float* lse,
+                          int32_t* err_flag, void* stream) {
+  const int kind = check_decode_args(dims, q_tilde, alpha_q, q_rope_normed, kv_cache,
+                                     alpha_k_cache, block_table, seq_lens, num_splits, flags);
+  if (kind < 0) return kind;
+  if (!workspace || !o_latent || !lse) return QKN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QKN_ERR_ALIGNMENT;
+  if (!aligned16(o_latent) || !aligned16(lse)) return QKN_ERR_ALIGNMENT;
+  const WorkspaceLayout w = workspace_layout(*dims, num_splits);
+  if (workspace_bytes < w.total) return QKN_ERR_INVALID_ARG;
+  void* o_partial = workspace;
+  float* lse_partial =
+      reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + w.lse_offset);
   qkn::DecodeArgs a{q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache, block_table,
                     seq_lens, o_partial, lse_partial, err_flag, num_splits,
                     (flags & QKN_DECODE_NO_ALPHA) == 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(kind == 1 ? qkn::launch_decode_mfma(*dims, a, s)
-                              : qkn::launch_decode_generic(*dims, a, s));
+  hipError_t e = launch_decode(kind, *dims, a, s);
+  if (e != hipSuccess) return QKN_ERR_HIP;
+  return hip_status(qkn::launch_combine(*dims, num_splits, o_partial, lse_partial, o_latent, lse, s));
 }
 
 int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,

@@ -185,13 +185,9 @@ hipError_t launch_nt(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new
   constexpr int D = NT * 32;
   constexpr int KC = chunk_rows(D);
   const size_t lds = (size_t)3 * KC * (D + W_PAD) * 2 + WAVES * 32 * 32 * 4;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&append_alpha_mfma<NT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&append_alpha_mfma<NT>),
+                                          (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(append_alpha_mfma<NT>, dim3(cdiv(n_tokens, TOK), d.groups), dim3(64 * WAVES),
                      lds, s, c_new, seq_idx, pos, block_table, w_k, alpha_k, n_tokens, d.batch,
                      d.max_pages_per_seq, d.num_pages, d.rank, d.groups, d.eps);

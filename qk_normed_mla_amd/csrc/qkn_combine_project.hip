@@ -319,15 +319,8 @@ size_t project_lds_max() {
 }
 template <bool MERGE>
 hipError_t set_lds_limit() {
-  static bool done = false;
-  if (!done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&project_mfma<MERGE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)project_lds_max());
-    if (e != hipSuccess) return e;
-    done = true;
-  }
-  return hipSuccess;
+  return set_lds_limit_once(reinterpret_cast<const void*>(&project_mfma<MERGE>),
+                            (int)project_lds_max());
 }
 }  // namespace
 

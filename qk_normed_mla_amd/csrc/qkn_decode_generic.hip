@@ -182,13 +182,9 @@ __global__ __launch_bounds__(256) void decode_generic(
 template <typename CacheT>
 hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
   const size_t shmem = (size_t)(HB + TC) * (d.rank + d.rope_dim) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_generic<CacheT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&decode_generic<CacheT>),
+                                          128 * 1024);
+  if (e != hipSuccess) return e;
   dim3 grid(cdiv(d.heads, HB), a.num_splits, d.batch * d.s_q);
   hipLaunchKernelGGL(decode_generic<CacheT>, grid, dim3(256), shmem, s,
                      static_cast<const CacheT*>(a.q_tilde), a.alpha_q,

@@ -231,6 +231,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   const int l32 = lane & 31;  // head within the wave
   const int hh = lane >> 5;   // which 8-wide half of a 16-long reduction step
   int err = 0;
+  bool restarted = false;
 
   int T = seq_lens[b];
   if (T < 0 || T > max_pages * PAGE) {
@@ -323,7 +324,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const size_t row0s = (size_t)(pg >= 0 ? pg : 0) * PAGE + (s & 1) * ST;  // cache row
     StagePlan pl;
     pl.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0s * ROW_BYTES, nv * ROW_BYTES);
-    pl.ra = buffer_rsrc(alpha_k + row0s * groups, nv * groups * 4);
+    // the alpha-free instantiation reads no alpha^k bytes: its loads are still
+    // issued (every stage keeps the same load count) but read nothing
+    pl.ra = buffer_rsrc(alpha_k + row0s * groups, USE_ALPHA ? nv * groups * 4 : 0);
     pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
     asm volatile("" : "+s"(pl.buf));  // keep the per-load LDS addresses out of loop-invariant registers
     return pl;
@@ -593,6 +596,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
       __syncthreads();
       if (tid == 0) *flag = 0;
       m_ref = m_seen;
+      restarted = true;
     }
   } while (again);
 
@@ -638,17 +642,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     }
   }
   if (err && err_flag && lane == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
+  if (restarted && err_flag && tid == 0) atomicOr(err_flag, QKN_FLAG_RESTART);
 }
 
 template <bool USE_ALPHA>
 hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<USE_ALPHA>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = set_lds_limit_once(
+      reinterpret_cast<const void*>(&decode_mfma_kernel<USE_ALPHA>), LDS_BYTES);
+  if (e != hipSuccess) return e;
   const int row_blocks = cdiv(d.s_q * d.heads, ROWS_PER_WG);
   const int n_work = d.batch * a.num_splits * row_blocks;
   const int per_xcd = cdiv(n_work, 8);

@@ -99,6 +99,10 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Raises the dynamic LDS limit of kernel `fn` to `bytes` on the current device,
+// once per (kernel, device).  Safe to call from several host threads at once.
+hipError_t set_lds_limit_once(const void* fn, int bytes);
+
 // Tokens per split-KV partition: ceil(T / P) rounded up to whole 64-token pages.
 __host__ __device__ __forceinline__ int split_len(int T, int P) {
   return QKN_MLA_PAGE_SIZE * cdiv(cdiv(T, P), QKN_MLA_PAGE_SIZE);

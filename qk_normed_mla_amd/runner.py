@@ -16,9 +16,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (QKN_BF16, PAGE_SIZE, Dims, cache_torch_dtype, dims_for, partial_torch_dtype,
-               qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine, qkn_mla_combine_project,
-               qkn_mla_decode)
+from . import (QKN_BF16, PAGE_SIZE, Dims, alloc_decode_workspace, cache_torch_dtype, dims_for,
+               partial_torch_dtype, qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine,
+               qkn_mla_combine_project, qkn_mla_decode, qkn_mla_decode_attend)
 
 
 def _dev(x, device, dtype=None):
@@ -144,6 +144,18 @@ class DecodeRunner:
                        self.alpha_k if alpha_k is None else alpha_k, self.block_table,
                        self.seq_lens, self.num_splits, flags, self.o_partial, self.lse_partial,
                        self.err_flag, stream)
+
+    def attend(self, flags: int = 0, stream=None, kv=None, alpha_k=None):
+        """Decode and combine in one library call, the partials in a workspace
+        sized by the library (allocated on first use)."""
+        if getattr(self, "_ws_splits", None) != self.num_splits:
+            self.workspace = alloc_decode_workspace(self.dims, self.num_splits, self.device)
+            self._ws_splits = self.num_splits
+        qkn_mla_decode_attend(self.dims, self.q_tilde, self.alpha_q, self.q_rope_normed,
+                              self.kv if kv is None else kv,
+                              self.alpha_k if alpha_k is None else alpha_k, self.block_table,
+                              self.seq_lens, self.num_splits, flags, self.workspace,
+                              self.o_latent, self.lse, self.err_flag, stream)
 
     def combine(self, stream=None):
         qkn_mla_combine(self.dims, self.num_splits, self.o_partial, self.lse_partial,

@@ -11,39 +11,39 @@ from qk_normed_mla_amd.runner import DecodeRunner
 
 # Tolerances.  Floating point: row-normwise max relative error
 # max |gpu - ref| / max |ref| over each latent row (b, i, h), and absolute error
-# on lse.  Float32 cache: 1e-4; bf16 cache with float32 accumulation: 1e-2
-# end to end (from the float32 inputs against the float64 explicit path).
+# on lse.  Float32 cache: 1e-4; bf16 cache with float32 accumulation: 1e-2.
+# Every floating-point comparison is held to these, end to end (float32 inputs
+# against the float64 explicit path) and for the decode kernel alone (on the
+# oracle's own stored state) alike.
 #
-# The decode kernel alone, run on the oracle's own stored state:
-#  * vector-ALU kernel (float32 throughout): 1e-5 row-relative.
-#  * matrix-core kernel: each probability enters the P.C product rounded to
-#    bf16, p~_t = p_t (1 + e_t) with |e_t| <= 2^-9, and the row is normalised by
-#    the sum of the same rounded values, so o = sum_t w_t c_t stays a convex
-#    combination whose weights moved by w_t (e_t - e_mean) / (1 + e_mean), i.e.
-#    by at most ~2^-8 relative.  Hence |delta o_m| <= 2^-8 sum_t w_t |c_tm - o_m|
-#    <= 2^-8 * 2 max_t |c_tm| = 2^-7 max_t |c_tm|.  The split-KV combine keeps
-#    one rounding per token, so the bound holds for the merged result too.  It
-#    is absolute, per row, in units of the largest latent entry the row can
-#    see (KERNEL_P_ROUND), plus 1e-5 relative for float32 accumulation.  lse
-#    moves by <= ln(1 + 2^-9) from the rounding of the weights, plus the float32
-#    error of the logits themselves: a K = 576 dot accumulated in float32 is off
-#    by ~576 * 2^-24 * sum |q~_m c_m| (~1e-3 for the unnormalised logits of the
-#    alpha-free test), times the softmax scale; 2e-4 covers it.
-#    The logits themselves carry the float32 error of a K-term dot product,
-#    |dS_t| <= gamma_K * sum_m |q~_m c_tm| (standard bound, gamma_K = K u / (1 - K u),
-#    u = 2^-24), computed per row by logit_error_bound(); it adds to the lse bound
-#    and, through the weights (|dw/w| <= 2 max_t |dl_t|), to the latent bound.
-#  * the split partials are stored as half for a bf16 cache: each is a convex
-#    combination of the latent rows its split sees, so storing it moves it by
-#    at most 2^-11 of its largest entry, <= 2^-11 max_t |c_tm| (KERNEL_PART_ROUND,
-#    absolute, in the same units as KERNEL_P_ROUND); the combine's weights sum
-#    to 1, so the merged row moves by no more.  A float32 cache keeps float32
-#    partials (0).
+# The decode kernel alone is also held element by element to a bound derived
+# from its arithmetic, with the oracle's float64 weights w_t of the same tokens
+# (one split for a partial, every visible token for the merged row) and the
+# exact result o:
+#  * the matrix-core kernel feeds each probability into the P.C product rounded
+#    to bf16, p~_t = p_t (1 + e_t), |e_t| <= u = 2^-8, and normalises by the sum
+#    of the same rounded values; its logits carry the float32 error of a
+#    K-term dot product, |dl_t| <= D (logit_error_bound(), natural-log units,
+#    plus the exponent's own rounding).  The weights it uses are
+#    w~_t = w_t f_t / sum_s w_s f_s with f_t = (1 + e_t) e^{dl_t}, so
+#    |w~_t / w_t - 1| <= R - 1, R = (1 + u) / (1 - u) * e^{2 D}.  Since both
+#    weight sets sum to 1,
+#        o~_m - o_m = sum_t (w~_t - w_t)(c_tm - o_m),
+#        |o~_m - o_m| <= (R - 1) * S_m,   S_m = sum_t w_t |c_tm - o_m|.
+#  * the sums run in float32 over n tokens: gamma_n (A_m + |o_m|), with
+#    A_m = sum_t w_t |c_tm| (the P.C sum and its normaliser).
+#  * for a bf16 cache the split partials are stored as IEEE half (relative
+#    step 2^-11): 2^-11 |o_p,m| for a partial; the combine's weights sum to 1,
+#    so the merged row moves by at most 2^-11 A_m.
+#  * lse: ln R from the weights plus D from the logits, plus float32 rounding.
+# The vector-ALU kernel keeps probabilities and partials (for a float32 cache)
+# in float32: the same form with u = 2^-24.
 TOL_E2E = {"f32": 1e-4, "bf16": 1e-2}
-KERNEL_PART_ROUND = {"f32": 0.0, "bf16": 2.0 ** -11}
+U_PROB = {1: 2.0 ** -8, 0: 2.0 ** -24}      # probability rounding, by kernel kind
+U_PART = {"f32": 0.0, "bf16": 2.0 ** -11}   # storage of the split partials
+# a float32 cache keeps float32 partials: the vector-ALU kernel's row-relative bar
 TOL_KERNEL_GENERIC = 1e-5
-KERNEL_P_ROUND = 2.0 ** -7
-KERNEL_LSE = float(np.log1p(2.0 ** -9))
+KERNEL_PART_ROUND = U_PART
 
 
 def gamma_k(k: int) -> float:
@@ -100,3 +100,27 @@ def run_e2e(wl, inp, num_splits=None, flags=0, kv_fill_word=None):
     r.step(flags)
     torch.cuda.synchronize()
     return r
+
+
+def weighted_moments(C, w, o):
+    """S_m = sum_t w_t |c_tm - o_m| and A_m = sum_t w_t |c_tm| for weights w [n]
+    over latent rows C [n, r] with the exact result o [r]."""
+    return w @ np.abs(C - o[None, :]), w @ np.abs(C)
+
+
+def kernel_elementwise_bound(kind, cache_dtype, w, C, o, D, n, partial):
+    """Per-element bound on |o~_m - o_m| for one row (see the derivation at the
+    top of this module).  ``partial``: the row is a stored split partial (its
+    own half step) rather than the merged row."""
+    u = U_PROB[kind]
+    R = (1.0 + u) / (1.0 - u) * np.exp(2.0 * D)
+    S, A = weighted_moments(C, w, o)
+    g = gamma_k(n + 1)
+    half = U_PART[cache_dtype]
+    store = half * (np.abs(o) if partial else A)
+    return (R - 1.0) * S * 1.001 + g * (A + np.abs(o)) + store + 1e-7 * np.max(np.abs(o))
+
+
+def kernel_lse_bound(kind, D, n):
+    u = U_PROB[kind]
+    return float(np.log((1.0 + u) / (1.0 - u))) + D + 2.0 * gamma_k(n + 1) + 2e-6

@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 9, syms
+    assert len(syms) == 12, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 3
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 4
     for st in (0, -1, -2, -3, -4):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -147,3 +147,64 @@ def test_combine_project_rejects_bad_arguments():
     assert call(o=bad) == -3
     d.groups = 3
     assert call() == -1
+
+
+def test_partial_dtype_query():
+    """The partial dtype comes from the library: half for a bf16 cache, float32
+    for a float32 cache, an error status for invalid dims."""
+    import torch
+    lib = Q.library()
+    assert lib.qkn_mla_partial_dtype(ctypes.byref(good_dims())) == Q.QKN_F16
+    assert lib.qkn_mla_partial_dtype(ctypes.byref(good_dims(cache_dtype="f32"))) == Q.QKN_F32
+    assert lib.qkn_mla_partial_dtype(ctypes.byref(good_dims(heads=0))) == -1
+    assert lib.qkn_mla_partial_dtype(None) == -1
+    assert Q.partial_torch_dtype(good_dims()) == torch.float16
+    assert Q.partial_torch_dtype(good_dims(cache_dtype="f32")) == torch.float32
+
+
+@pytest.mark.parametrize("kw,splits", [
+    (dict(), 8), (dict(cache_dtype="f32"), 3), (dict(batch=64, s_q=4), 4),
+    (dict(batch=1, heads=8, rank=64, head_dim=32, rope_dim=16), 1), (dict(batch=3), 37),
+])
+def test_workspace_bytes(kw, splits):
+    """Both partial arrays fit, each starting on a 256-byte boundary: o_partial
+    [rows, P, r] in the partial dtype, then lse_partial [rows, P] float32."""
+    d = good_dims(**kw)
+    n = Q.decode_workspace_bytes(d, splits)
+    rows = d.batch * d.s_q * d.heads * splits
+    elem = 2 if d.cache_dtype == Q.QKN_BF16 else 4
+    o_bytes = -(-rows * d.rank * elem // 256) * 256
+    lse_bytes = -(-rows * 4 // 256) * 256
+    assert n == o_bytes + lse_bytes
+    assert n % 256 == 0
+
+
+def test_workspace_bytes_invalid():
+    lib = Q.library()
+    assert lib.qkn_mla_decode_workspace_bytes(ctypes.byref(good_dims()), 0) == 0
+    assert lib.qkn_mla_decode_workspace_bytes(ctypes.byref(good_dims()), 5000) == 0
+    assert lib.qkn_mla_decode_workspace_bytes(ctypes.byref(good_dims(groups=3)), 4) == 0
+    assert lib.qkn_mla_decode_workspace_bytes(None, 4) == 0
+
+
+def test_decode_attend_rejects_bad_workspace():
+    """A missing, misaligned or short workspace is refused before any launch."""
+    lib = Q.library()
+    d = good_dims()
+    P = ctypes.c_void_p
+    ok = P(1 << 20)  # never dereferenced: every call below is rejected first
+    need = Q.decode_workspace_bytes(d, 8)
+
+    def call(ws=ok, nbytes=need, splits=8, flags=0, o_lat=ok, q=ok):
+        return lib.qkn_mla_decode_attend(ctypes.byref(d), q, ok, ok, ok, ok, ok, ok, splits,
+                                         ctypes.c_uint32(flags), ws, ctypes.c_size_t(nbytes),
+                                         o_lat, ok, None, None)
+    assert call(ws=None) == -1
+    assert call(nbytes=need - 1) == -1
+    assert call(nbytes=0) == -1
+    assert call(ws=P((1 << 20) + 128)) == -3   # 16-byte but not 256-byte aligned
+    assert call(o_lat=None) == -1
+    assert call(q=None) == -1
+    assert call(q=P((1 << 20) + 8)) == -3
+    assert call(splits=0) == -1
+    assert call(flags=16) == -1
