@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 4
+#define QKN_MLA_ABI_VERSION 5
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -57,7 +57,9 @@ typedef enum {
   QKN_ERR_INVALID_ARG = -1, /* null pointer, non-positive or inconsistent size */
   QKN_ERR_UNSUPPORTED = -2, /* a size the kernels do not handle (see checks)  */
   QKN_ERR_ALIGNMENT = -3,   /* a pointer not 16-byte aligned                  */
-  QKN_ERR_HIP = -4          /* the HIP runtime reported an error on launch    */
+  QKN_ERR_HIP = -4,         /* the HIP runtime reported an error on launch    */
+  QKN_ERR_SCRATCH = -5      /* the request needs more than the static scratch
+                               of qkn_mla_decode_attend_noalloc holds          */
 } qkn_status;
 
 typedef enum { QKN_F32 = 0, QKN_BF16 = 1, QKN_F16 = 2 } qkn_dtype;
@@ -274,6 +276,37 @@ QKN_API int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde,
                           int32_t num_splits, uint32_t flags, void* workspace,
                           size_t workspace_bytes, float* o_latent, float* lse,
                           int32_t* err_flag, void* stream);
+
+/* Bytes of the static device scratch array of qkn_mla_decode_attend_noalloc. */
+#define QKN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * qkn_mla_decode_attend_noalloc -- qkn_mla_decode_attend with the split
+ * partials in a static device array of the library instead of a caller
+ * workspace.  For callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ *   Same arguments, results and bits as qkn_mla_decode_attend without
+ *   `workspace` / `workspace_bytes`.  The call allocates nothing: no hipMalloc,
+ *   hipFree or allocating library routine.  The partials go to a file-scope
+ *   __device__ array of QKN_NOALLOC_SCRATCH_BYTES (64 MiB); every device the
+ *   library runs on holds its own copy from the library's first use there
+ *   until the process ends.  Its address is looked up once per device, on the
+ *   first call made with that device current.
+ *   A request whose qkn_mla_decode_workspace_bytes() exceeds
+ *   QKN_NOALLOC_SCRATCH_BYTES is rejected with QKN_ERR_SCRATCH before
+ *   anything is launched (e.g. 4096 query rows at r = 512 take at most 15
+ *   splits).  Every call on one device shares that device's array, which
+ *   keeps the last call's contents (nothing in it needs to start at zero):
+ *   calls that overlap on one device -- on two streams, or from two host
+ *   threads without ordering -- race on it and must not be issued.
+ */
+QKN_API int qkn_mla_decode_attend_noalloc(const qkn_mla_dims* dims, const void* q_tilde,
+                                  const float* alpha_q, const void* q_rope_normed,
+                                  const void* kv_cache, const float* alpha_k_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t num_splits, uint32_t flags, float* o_latent,
+                                  float* lse, int32_t* err_flag, void* stream);
 
 /* Flags of qkn_mla_combine_project.  o_latent and lse are the same bits in
  * every form; o is within the same bound (the forms divide the reduction

@@ -81,6 +81,22 @@ hipError_t launch_decode(int kind, const qkn_mla_dims& d, const qkn::DecodeArgs&
   return kind == 1 ? qkn::launch_decode_mfma(d, a, s) : qkn::launch_decode_generic(d, a, s);
 }
 
+// Decode into the partials laid out in `ws` (workspace_layout), then combine.
+int attend_in(int kind, const qkn_mla_dims& d, const void* q_tilde, const float* alpha_q,
+              const void* q_rope_normed, const void* kv_cache, const float* alpha_k_cache,
+              const int32_t* block_table, const int32_t* seq_lens, int32_t num_splits,
+              uint32_t flags, void* ws, float* o_latent, float* lse, int32_t* err_flag,
+              hipStream_t s) {
+  const WorkspaceLayout w = workspace_layout(d, num_splits);
+  void* o_partial = ws;
+  float* lse_partial = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.lse_offset);
+  qkn::DecodeArgs a{q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache, block_table,
+                    seq_lens, o_partial, lse_partial, err_flag, num_splits,
+                    (flags & QKN_DECODE_NO_ALPHA) == 0};
+  if (launch_decode(kind, d, a, s) != hipSuccess) return QKN_ERR_HIP;
+  return hip_status(qkn::launch_combine(d, num_splits, o_partial, lse_partial, o_latent, lse, s));
+}
+
 }  // namespace
 
 namespace qkn {
@@ -112,6 +128,9 @@ const char* qkn_status_string(int status) {
     case QKN_ERR_UNSUPPORTED: return "unsupported size for these kernels";
     case QKN_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case QKN_ERR_HIP: return "HIP runtime error on launch";
+    case QKN_ERR_SCRATCH:
+      return "request exceeds the static scratch of qkn_mla_decode_attend_noalloc "
+             "(QKN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -206,18 +225,29 @@ int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde, const f
   if (!workspace || !o_latent || !lse) return QKN_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QKN_ERR_ALIGNMENT;
   if (!aligned16(o_latent) || !aligned16(lse)) return QKN_ERR_ALIGNMENT;
-  const WorkspaceLayout w = workspace_layout(*dims, num_splits);
-  if (workspace_bytes < w.total) return QKN_ERR_INVALID_ARG;
-  void* o_partial = workspace;
-  float* lse_partial =
-      reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + w.lse_offset);
-  qkn::DecodeArgs a{q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache, block_table,
-                    seq_lens, o_partial, lse_partial, err_flag, num_splits,
-                    (flags & QKN_DECODE_NO_ALPHA) == 0};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode(kind, *dims, a, s);
-  if (e != hipSuccess) return QKN_ERR_HIP;
-  return hip_status(qkn::launch_combine(*dims, num_splits, o_partial, lse_partial, o_latent, lse, s));
+  if (workspace_bytes < workspace_layout(*dims, num_splits).total) return QKN_ERR_INVALID_ARG;
+  return attend_in(kind, *dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,
+                   block_table, seq_lens, num_splits, flags, workspace, o_latent, lse, err_flag,
+                   static_cast<hipStream_t>(stream));
+}
+
+int qkn_mla_decode_attend_noalloc(const qkn_mla_dims* dims, const void* q_tilde,
+                                  const float* alpha_q, const void* q_rope_normed,
+                                  const void* kv_cache, const float* alpha_k_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t num_splits, uint32_t flags, float* o_latent,
+                                  float* lse, int32_t* err_flag, void* stream) {
+  const int kind = check_decode_args(dims, q_tilde, alpha_q, q_rope_normed, kv_cache,
+                                     alpha_k_cache, block_table, seq_lens, num_splits, flags);
+  if (kind < 0) return kind;
+  if (!o_latent || !lse) return QKN_ERR_INVALID_ARG;
+  if (!aligned16(o_latent) || !aligned16(lse)) return QKN_ERR_ALIGNMENT;
+  if (workspace_layout(*dims, num_splits).total > QKN_NOALLOC_SCRATCH_BYTES) return QKN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (qkn::noalloc_scratch(&scratch) != hipSuccess || !scratch) return QKN_ERR_HIP;
+  return attend_in(kind, *dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,
+                   block_table, seq_lens, num_splits, flags, scratch, o_latent, lse, err_flag,
+                   static_cast<hipStream_t>(stream));
 }
 
 int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,

@@ -161,6 +161,9 @@ hipError_t launch_append_alpha_bulk(const qkn_mla_dims& d, int32_t n_tokens, con
                                     const int32_t* block_table, const float* w_k, float* alpha_k,
                                     hipStream_t s);
 bool project_mfma_applies(const qkn_mla_dims& d);
+// Device address of the library's static scratch array on the current device
+// (QKN_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned).
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_combine_project(const qkn_mla_dims& d, int num_splits, const void* o_part,
                                   const float* lse_part, const float* w_v, float* o_lat,
                                   float* lse, float* o, uint32_t flags, hipStream_t s);

@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 13, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,8 +47,8 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 4
-    for st in (0, -1, -2, -3, -4):
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 5
+    for st in (0, -1, -2, -3, -4, -5):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
 
@@ -208,3 +208,28 @@ def test_decode_attend_rejects_bad_workspace():
     assert call(q=P((1 << 20) + 8)) == -3
     assert call(splits=0) == -1
     assert call(flags=16) == -1
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch():
+    """The allocation-free variant refuses, before any launch, a request whose
+    partials would not fit its static scratch, and bad arguments as the
+    workspace variant does."""
+    lib = Q.library()
+    P = ctypes.c_void_p
+    ok = P(1 << 20)  # never dereferenced: every call below is rejected first
+
+    def call(d, splits, o_lat=ok, q=ok):
+        return lib.qkn_mla_decode_attend_noalloc(ctypes.byref(d), q, ok, ok, ok, ok, ok, ok, splits,
+                                                 ctypes.c_uint32(0), o_lat, ok, None, None)
+    big = good_dims(batch=64, s_q=4)             # 32768 rows: 4 splits need 128 MiB of partials
+    assert Q.decode_workspace_bytes(big, 4) > Q.NOALLOC_SCRATCH_BYTES
+    assert call(big, 4) == Q.QKN_ERR_SCRATCH
+    d = good_dims(batch=32)                      # 4096 rows: 16 splits need 64 MiB + the lse
+    assert Q.decode_workspace_bytes(d, 16) > Q.NOALLOC_SCRATCH_BYTES
+    assert Q.decode_workspace_bytes(d, 15) <= Q.NOALLOC_SCRATCH_BYTES
+    assert call(d, 16) == Q.QKN_ERR_SCRATCH
+    assert call(d, 8, o_lat=None) == -1
+    assert call(d, 8, q=None) == -1
+    assert call(d, 8, o_lat=P((1 << 20) + 4)) == -3
+    assert call(good_dims(groups=3), 8) == -1
+    assert "static scratch" in Q.status_string(Q.QKN_ERR_SCRATCH)
