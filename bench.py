@@ -9,13 +9,20 @@ replicas of the cache so that consecutive steps never re-read a cache that
 could still sit in the 256 MB last-level cache (at least 512 MB is touched
 between two reads of a replica).
 
-Prints one JSON line.  ``value`` is the latent-cache read rate of the step:
-algorithmic cache bytes (every visible token's latent + RoPE key + alpha^k,
-once) divided by the step time.  ``roofline`` rates the decode kernel alone
-(HIP events on its stream) against the 8 TB/s HBM peak; ``cpu_baseline`` is
-the float64 CPU oracle timed on a bounded sample on the host's cores.
+Prints one JSON line.  The headline workload (default ``mtp``: 64 sequences of
+1024-16384 tokens, 4 query tokens per step, the largest configuration) sets
+``value``: the latent-cache read rate of the step, algorithmic cache bytes
+(every visible token's latent + RoPE key + alpha^k, once) divided by the step
+time of exactly K timed steps.  ``roofline`` rates its decode kernel alone (HIP
+events on its stream) against the peak of its bound: bf16 matrix-core FLOP/s
+when the workload's arithmetic intensity is past the ridge, else 8 TB/s of HBM.
+``workloads`` carries the same figures for the other bf16 workloads (dsv3,
+grouped, long); ``qknorm_sweep`` the cost of the inverse-RMS factors over a
+batch-1 context sweep from 4k to 256k tokens; ``cpu_baseline`` the float64 CPU
+oracle timed on a bounded sample on the host's cores (and on one core).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp]
+                    [--only] [--no-cpu] [--no-sweep]
 """
 from __future__ import annotations
 
@@ -104,16 +111,25 @@ def load_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, target_s=12.0):
-    """The oracle's decode over the stored state, timed on the host's cores on a
-    sample of whole sequences (each with all its heads), scaled to cache GB/s.
-    Building each sequence's stored state is set-up and is not timed."""
-    from oracle import qkn_oracle as O
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, target_s=12.0, one_core_s=5.0):
+    """The oracle's decode over the stored state, timed on the host's cores on a
+    sample of whole sequences (each with all its heads), scaled to cache GB/s;
+    then the same on one core.  Building each sequence's stored state is
+    set-up and is not timed."""
+    from oracle import qkn_oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     qi = O.query_image(wl, inp)
     offs = inp["tok_offsets"]
     nseq = len(inp["seq_lens"])
@@ -130,152 +146,69 @@ def cpu_baseline(wl, inp, target_s=12.0):
         prepared.append((one_wl, {k: v[b:b + 1] for k, v in qi.items()}, img,
                          one["block_table"], one["seq_lens"],
                          T * (2 * (wl.rank + wl.rope_dim) + 4 * wl.groups)))
-    done, t_spent, nbytes = 0, 0.0, 0
-    while t_spent < target_s:
-        one_wl, q1, img, bt, sl, nb = prepared[done % len(prepared)]
-        t0 = time.perf_counter()
-        O.decode_on_image(one_wl, q1, img["kv"], img["alpha_k"], bt, sl, wl.num_splits)
-        t_spent += time.perf_counter() - t0
-        nbytes += nb
-        done += 1
+
+    def run(seconds):
+        done, t_spent, nbytes = 0, 0.0, 0
+        while t_spent < seconds:
+            one_wl, q1, img, bt, sl, nb = prepared[done % len(prepared)]
+            t0 = time.perf_counter()
+            O.decode_on_image(one_wl, q1, img["kv"], img["alpha_k"], bt, sl, wl.num_splits)
+            t_spent += time.perf_counter() - t0
+            nbytes += nb
+            done += 1
+        return done, t_spent, nbytes
+
+    done, t_spent, nbytes = run(target_s)
+    with threadpool_limits(limits=1):
+        done1, t1, nbytes1 = run(one_core_s)
+    lens = [int(x) for x in inp["seq_lens"][:len(prepared)]]
     return {"value": round(nbytes / t_spent / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "one_core": {"value": round(nbytes1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "sample": f"{done1} decodes, {t1:.1f} s"},
             "sample": f"{done} single-sequence decodes cycling over the first "
-                      f"{len(prepared)} of {nseq} sequences (each {int(inp['seq_lens'][0])} "
-                      f"tokens mean, all {wl.heads} heads), float64 NumPy decode over the "
+                      f"{len(prepared)} of {nseq} sequences (lengths {lens}, all {wl.heads} "
+                      f"heads, {wl.s_q} query tokens each), float64 NumPy decode over the "
                       f"stored bf16 cache, {t_spent:.1f} s of host time"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsv3")
-    ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = default)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
-    ap.add_argument("--no-overhead", action="store_true", help="skip the alpha-free timing")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB a few times (the reference "
-                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
-                                   "is not sharded across GPUs (--gpus must be 1)"}))
-        sys.exit(2)
+class Timer:
+    """HIP graphs of back-to-back launches and their steady-state timing."""
 
-    import numpy as np
-    import torch
+    def __init__(self, torch):
+        self.torch = torch
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 4}), flush=True)
-        return
-
-    import qk_normed_mla_amd as Q
-    import workloads as W
-    from qk_normed_mla_amd.runner import DecodeRunner
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    wl = W.WORKLOADS[args.workload]
-    log(f"workload {wl.name}: generating inputs")
-    inp = W.make_inputs(wl, seed=0)
-    splits = args.splits or default_splits(wl, inp["seq_lens"])
-    wl = wl.replace(num_splits=splits)
-    flops, nbytes = W.flops_and_bytes(wl, inp["seq_lens"], 2 if wl.cache_dtype == "bf16" else 4)
-    kind = Q.decode_kernel_kind(Q.dims_for(wl, inp["num_pages"]), splits)
-    log(f"B={wl.batch} s_q={wl.s_q} H={wl.heads} G={wl.groups} T~{int(np.mean(inp['seq_lens']))} "
-        f"splits={splits} kernel={'mfma' if kind == 1 else 'generic'} cache bytes={nbytes / 1e6:.1f} MB")
-
-    r = DecodeRunner(wl, inp, num_splits=splits)
-    log("filling the cache")
-    r.fill_history()
-    r.append_new()
-    torch.cuda.synchronize()
-    # bulk append: up to 2^18 history tokens in one qkn_mla_append call, inputs in
-    # HBM (rewrites the same slots with the same values)
-    hist = r.history_inputs()
-    n_fill = int(hist[0].shape[0])
-    fill = None
-    if n_fill:
-        r.append_tokens(*hist)
-        fe = []
-        for _ in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            r.append_tokens(*hist)
-            b.record()
-            fe.append((a, b))
-        torch.cuda.synchronize()
-        fill_ms = min(a.elapsed_time(b) for a, b in fe)
-        fill = {"tokens": n_fill, "ms": round(fill_ms, 3),
-                "mtok_per_s": round(n_fill / fill_ms / 1e3, 2)}
-        log(f"bulk append of {n_fill} tokens: {fill_ms:.3f} ms")
-    del hist
-    cache_bytes = r.kv.numel() * r.kv.element_size() + r.alpha_k.numel() * 4
-    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / cache_bytes) + 1)
-    kvs = [r.kv] + [r.kv.clone() for _ in range(n_rep - 1)]
-    aks = [r.alpha_k] + [r.alpha_k.clone() for _ in range(n_rep - 1)]
-    log(f"{n_rep} cache replicas of {cache_bytes / 1e6:.1f} MB rotate across steps")
-
-    def step(k, flags=0):
-        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
-        r.step(flags)
-
-    def attn(k, flags=0):
-        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
-        r.decode(flags)
-        r.combine()
-
-    def dec(k, flags=0):
-        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
-        r.decode(flags)
-
-    def attn_proj(k, flags=0):
-        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
-        r.decode(flags)
-        r.combine_project()
-
-    # eager warm-up (also the reference for the graph check below)
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    ref = r.o_latent.clone()
-
-    def capture(fn, n, flags=0):
-        """A HIP graph of n calls fn(k, flags), k = 0 .. n-1 (launch overhead of
-        the Python binding stays outside the timed region)."""
+    def capture(self, fn, n):
+        """A HIP graph of n calls fn(k), k = 0 .. n-1 (launch overhead of the
+        Python binding stays outside the timed region)."""
+        torch = self.torch
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
                 for k in range(n):
-                    fn(k, flags)
+                    fn(k)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         return g
 
-    def warm(g, seconds=0.25):
+    def warm(self, g, seconds=0.25):
         """Untimed replays of g for about `seconds` of wall time: the GPU's
         clocks ramp up over the first milliseconds of sustained work, and the
         timings below are of the steady state."""
+        torch = self.torch
         t_end = time.perf_counter() + seconds
         while time.perf_counter() < t_end:
             g.replay()
             torch.cuda.synchronize()
 
-    def timed(graphs, reps=5):
+    def timed(self, graphs, reps=5):
         """Per graph, the median over reps of one replay in ms.  The replays
         of all graphs are interleaved back to back (no host sync between
         them, so the GPU stays busy), each bracketed by HIP events on the
         replay stream, after two untimed rounds."""
+        torch = self.torch
         stream = torch.cuda.current_stream()
         for _ in range(2):
             for g in graphs:
@@ -292,15 +225,95 @@ def main():
         t = np.array([a.elapsed_time(b) for a, b in ev]).reshape(reps, len(graphs))
         return [float(np.median(t[:, j])) for j in range(len(graphs))]
 
-    # the timed region: exactly K steps, one graph replay, barrier + sync on both sides
-    g_steps = capture(step, args.steps)
+
+def roofline_of(flops, nbytes, seconds, traffic):
+    """The decode kernel against the peak of its bound (matrix-core FLOP/s past
+    the ridge, HBM bandwidth below it)."""
+    ai = flops / nbytes
+    if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        a = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
+    a = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+
+
+def measure(Q, W, torch, timer, wl, inp, splits, *, steps, warmup, overhead=True,
+            history_fill=False):
+    """Every figure of one workload: the step (exactly `steps` timed steps in
+    one graph replay), the decode kernel alone, decode + combine, decode +
+    combine with the value up-projection, and the decode kernel without the
+    inverse-RMS factors."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    flops, nbytes = W.flops_and_bytes(wl, inp["seq_lens"], 2 if wl.cache_dtype == "bf16" else 4)
+    kind = Q.decode_kernel_kind(Q.dims_for(wl, inp["num_pages"]), splits)
+    log(f"{wl.name}: B={wl.batch} s_q={wl.s_q} H={wl.heads} G={wl.groups} "
+        f"T~{int(np.mean(inp['seq_lens']))} splits={splits} kernel={'mfma' if kind == 1 else 'generic'} "
+        f"cache bytes={nbytes / 1e6:.1f} MB")
+    r = DecodeRunner(wl, inp, num_splits=splits)
+    r.fill_history()
+    r.prepare()                           # the query side and the new tokens
+    torch.cuda.synchronize()
+    fill = None
+    if history_fill:
+        # bulk append: up to 2^18 history tokens in one qkn_mla_append call,
+        # inputs in HBM (rewrites the same slots with the same values)
+        hist = r.history_inputs()
+        n_fill = int(hist[0].shape[0])
+        if n_fill:
+            r.append_tokens(*hist)
+            fe = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                r.append_tokens(*hist)
+                b.record()
+                fe.append((a, b))
+            torch.cuda.synchronize()
+            fill_ms = min(a.elapsed_time(b) for a, b in fe)
+            fill = {"workload": wl.name, "tokens": n_fill, "ms": round(fill_ms, 3),
+                    "mtok_per_s": round(n_fill / fill_ms / 1e3, 2)}
+            log(f"bulk append of {n_fill} tokens: {fill_ms:.3f} ms")
+        del hist
+    cache_bytes = r.kv.numel() * r.kv.element_size() + r.alpha_k.numel() * 4
+    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / cache_bytes) + 1)
+    kvs = [r.kv] + [r.kv.clone() for _ in range(n_rep - 1)]
+    aks = [r.alpha_k] + [r.alpha_k.clone() for _ in range(n_rep - 1)]
+    log(f"{n_rep} cache replicas of {cache_bytes / 1e6:.1f} MB rotate across launches")
+
+    def use(k):
+        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
+
+    # restarts of the exact fixed-reference softmax, with and without the factors
+    restarted = {}
+    for name, fl in (("alpha", 0), ("no_alpha", Q.QKN_DECODE_NO_ALPHA)):
+        r.err_flag.zero_()
+        r.decode(fl)
+        torch.cuda.synchronize()
+        restarted[name] = bool(int(r.err_flag.item()) & Q.QKN_FLAG_RESTART)
+    r.err_flag.zero_()
+
+    # eager warm-up (also the reference for the graph check below)
+    for k in range(warmup):
+        use(k)
+        r.step()
+    torch.cuda.synchronize()
+    ref = r.o_latent.clone()
+
+    def step(k):
+        use(k)
+        r.step()
+
+    g_steps = timer.capture(step, steps)
     g_steps.replay()                      # untimed replay
     torch.cuda.synchronize()
     # all replicas hold the same cache and the step is deterministic, so every
     # replayed step must leave exactly the eager result
     if not torch.equal(r.o_latent, ref):
         raise RuntimeError("graph replay differs from the eager step")
-    warm(g_steps)
+    timer.warm(g_steps)
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -308,46 +321,217 @@ def main():
     g_steps.replay()
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = t0.elapsed_time(t1) / steps
     if not torch.equal(r.o_latent, ref):
         raise RuntimeError("graph replay differs from the eager step")
 
-    # the decode kernel alone, and decode + combine: back-to-back launches over
-    # the rotating replicas.  QK-norm overhead: the decode kernel with and
-    # without the inverse-RMS factors, the graphs' replays interleaved
+    # back-to-back launches over the rotating replicas: the decode kernel
+    # alone, decode + combine, decode + combine_project; the decode kernel
+    # without the factors; the graphs' replays interleaved
     n_dec = max(40, 4 * n_rep)
-    graphs = [capture(dec, n_dec), capture(attn, n_dec)]
-    if not args.no_overhead:
-        graphs.append(capture(dec, n_dec, Q.QKN_DECODE_NO_ALPHA))
-    # decode + the combine with the value up-projection (qkn_mla_combine_project)
-    graphs.append(capture(attn_proj, n_dec))
-    warm(graphs[0])
-    times = [t / n_dec for t in timed(graphs, reps=15)]
-    dec_ms, attn_ms, proj_ms = times[0], times[1], times[-1]
-    log(f"step {ms_per_step * 1e3:.1f} us, decode kernel {dec_ms * 1e3:.1f} us, "
-        f"decode+combine {attn_ms * 1e3:.1f} us, decode+combine_project {proj_ms * 1e3:.1f} us")
-    overhead = None
-    if not args.no_overhead:
-        overhead = round((dec_ms / times[2] - 1.0) * 100.0, 2)
-        log(f"decode kernel {dec_ms * 1e3:.1f} us with alpha, {times[2] * 1e3:.1f} us without "
-            f"({overhead:+.2f}%)")
 
-    value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (dec_ms * 1e-3) / 1e9
-    ai = flops / nbytes
-    bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name)}
-    else:
-        tf = flops / (dec_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                "traffic": load_traffic(wl.name)}
+    def dec(k):
+        use(k)
+        r.decode()
+
+    def attn(k):
+        use(k)
+        r.decode()
+        r.combine()
+
+    def attn_proj(k):
+        use(k)
+        r.decode()
+        r.combine_project()
+
+    def dec_plain(k):
+        use(k)
+        r.decode(Q.QKN_DECODE_NO_ALPHA)
+
+    fns = [dec, attn, attn_proj] + ([dec_plain] if overhead else [])
+    graphs = [timer.capture(f, n_dec) for f in fns]
+    timer.warm(graphs[0])
+    times = [t / n_dec for t in timer.timed(graphs, reps=15)]
+    dec_ms, attn_ms, proj_ms = times[0], times[1], times[2]
+    log(f"{wl.name}: step {ms_per_step * 1e3:.1f} us, decode kernel {dec_ms * 1e3:.1f} us, "
+        f"decode+combine {attn_ms * 1e3:.1f} us, decode+combine_project {proj_ms * 1e3:.1f} us")
+    ov = None
+    if overhead:
+        ov = round((dec_ms / times[3] - 1.0) * 100.0, 2)
+        log(f"{wl.name}: decode kernel {dec_ms * 1e3:.1f} us with alpha, {times[3] * 1e3:.1f} us "
+            f"without ({ov:+.2f}%)" + ("; the alpha-free kernel restarted" if restarted["no_alpha"] else ""))
+    out = {
+        "workload": wl.name, "batch": wl.batch, "s_q": wl.s_q, "heads": wl.heads,
+        "kv_groups": wl.groups, "rank": wl.rank, "rope_dim": wl.rope_dim,
+        "seq_len": int(np.mean(inp["seq_lens"])), "num_splits": splits,
+        "kernel": "mfma" if kind == 1 else "generic",
+        "cache_bytes": nbytes, "flops": flops,
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_cache_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "decode_combine_us": round(attn_ms * 1e3, 2),
+        "decode_combine_project_us": round(proj_ms * 1e3, 2),
+        "decode_hbm_frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_mfma_frac": round(flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "decode_combine_hbm_frac": round(nbytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "qknorm_overhead_pct": None if (ov is None or restarted["no_alpha"]) else ov,
+        "restarted": restarted,
+    }
+    if ov is not None and restarted["no_alpha"]:
+        out["qknorm_overhead_note"] = ("not comparable: without the inverse-RMS factors the "
+                                       "logits outgrow the fixed softmax reference and the "
+                                       f"kernel takes the exact restart ({ov:+.2f}% measured)")
+    res = {"summary": out, "ms_per_step": ms_per_step, "dec_ms": dec_ms, "flops": flops,
+           "nbytes": nbytes, "fill": fill}
+    del graphs, g_steps, kvs, aks, r
+    torch.cuda.empty_cache()
+    return res
+
+
+def qknorm_sweep(Q, W, torch, timer, lengths=(4096, 8192, 16384, 32768, 65536, 131072, 262144)):
+    """Batch-1 decode + combine (128 heads, r = 512, d_R = 64, latent scales
+    log-normal sigma 0.5) with and without the inverse-RMS factors over a
+    context sweep.  One 262144-token cache is drawn; three copies of it are
+    resident, and each launch reads a different window of pages (a block table
+    per window), so that at least 512 MB are read between two reads of one
+    window and none is served from the last-level cache."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    T_max = max(lengths)
+    wl = W.WORKLOADS["long"].replace(name="sweep", seq_len=T_max, latent_log_sigma=0.5)
+    inp = W.make_inputs(wl, seed=1)
+    r = DecodeRunner(wl, inp, num_splits=1)
+    r.fill_history()
+    r.append_new()
+    torch.cuda.synchronize()
+    copies = 3
+    pages = int(inp["num_pages"])
+    kv = torch.cat([r.kv] * copies, dim=0)
+    ak = torch.cat([r.alpha_k] * copies, dim=0)
+    del r
+    torch.cuda.empty_cache()
+    out = []
+    for T in lengths:
+        wlT = wl.replace(seq_len=T)
+        P = default_splits(wlT, [T])
+        ppw = -(-T // 64)                        # pages per window
+        n_win = (pages * copies) // ppw
+        bytes_T = T * (2 * (wl.rank + wl.rope_dim) + 4 * wl.groups)
+        need = min(n_win, math.ceil(MIN_ROTATION_BYTES / bytes_T) + 1)
+        n_launch = max(24, need)
+        tables = [torch.arange(w * ppw, (w + 1) * ppw, dtype=torch.int32, device="cuda")[None, :]
+                  for w in range(need)]
+        dims = Q.dims_for(wlT, pages * copies)
+        inpT = dict(inp, seq_lens=np.array([T], np.int32))
+        rT = DecodeRunner(wlT, dict(inpT, num_pages=1, block_table=np.zeros((1, ppw), np.int32),
+                                    c=inp["c"][:T], k_rope=inp["k_rope"][:T],
+                                    tok_offsets=np.array([0, T])), num_splits=P)
+        rT.absorb()
+        ws = Q.alloc_decode_workspace(dims, P)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def attend(k, flags, rT=rT, dims=dims, tables=tables, ws=ws, P=P, err=err):
+            Q.qkn_mla_decode_attend(dims, rT.q_tilde, rT.alpha_q, rT.q_rope_normed, kv, ak,
+                                    tables[k % len(tables)], rT.seq_lens, P, flags, ws,
+                                    rT.o_latent, rT.lse, err)
+
+        restarted = {}
+        for name, fl in (("alpha", 0), ("no_alpha", Q.QKN_DECODE_NO_ALPHA)):
+            err.zero_()
+            for k in range(len(tables)):
+                attend(k, fl)
+            torch.cuda.synchronize()
+            restarted[name] = bool(int(err.item()) & Q.QKN_FLAG_RESTART)
+        graphs = [timer.capture(lambda k: attend(k, 0), n_launch),
+                  timer.capture(lambda k: attend(k, Q.QKN_DECODE_NO_ALPHA), n_launch)]
+        timer.warm(graphs[0], 0.15)
+        t_a, t_n = [t / n_launch for t in timer.timed(graphs, reps=11)]
+        ov = (t_a / t_n - 1.0) * 100.0
+        rec = {"seq_len": T, "num_splits": P, "decode_combine_us": round(t_a * 1e3, 2),
+               "no_alpha_us": round(t_n * 1e3, 2),
+               "cache_gbs": round(bytes_T / (t_a * 1e-3) / 1e9, 1),
+               "overhead_pct": None if restarted["no_alpha"] else round(ov, 2),
+               "restarted": restarted}
+        log(f"sweep T={T}: {t_a * 1e3:.1f} us with alpha, {t_n * 1e3:.1f} us without "
+            f"({ov:+.2f}%), splits {P}, windows {len(tables)}")
+        out.append(rec)
+        del graphs, rT, ws
+        torch.cuda.empty_cache()
+    del kv, ak
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mtp", help="the headline workload")
+    ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = default)")
+    ap.add_argument("--only", action="store_true", help="the headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch-1 QK-norm sweep")
+    ap.add_argument("--no-overhead", action="store_true", help="skip the alpha-free timings")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
+                                   "is not sharded across GPUs (--gpus must be 1)"}))
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 4}), flush=True)
+        return
+
+    import qk_normed_mla_amd as Q
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    Q.library()
+    timer = Timer(torch)
+
+    def run(name, headline):
+        wl = W.WORKLOADS[name]
+        log(f"workload {name}: generating inputs")
+        inp = W.make_inputs(wl, seed=0)
+        splits = (args.splits if headline and args.splits else 0) or default_splits(wl, inp["seq_lens"])
+        wl = wl.replace(num_splits=splits)
+        res = measure(Q, W, torch, timer, wl, inp, splits,
+                      steps=args.steps if headline else 10,
+                      warmup=args.warmup if headline else 3,
+                      overhead=not args.no_overhead, history_fill=headline)
+        return wl, inp, res
+
+    wl, inp, head = run(args.workload, True)
+    others = []
+    if not args.only:
+        for name in ("dsv3", "grouped", "long", "mtp"):
+            if name != args.workload:
+                others.append(run(name, False)[2]["summary"])
+    sweep = None
+    if not args.only and not args.no_sweep:
+        log("batch-1 QK-norm overhead sweep")
+        sweep = qknorm_sweep(Q, W, torch, timer)
+
+    hs = head["summary"]
+    roof = roofline_of(head["flops"], head["nbytes"], head["dec_ms"] * 1e-3, load_traffic(wl.name))
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(wl, inp)
+    value = head["nbytes"] / (head["ms_per_step"] * 1e-3) / 1e9
     out = {
         "metric": "MLA decode-attn latent-cache GB/s (% HBM peak) and us/step, h=128 r=512",
         "value": round(value, 1),
@@ -355,25 +539,26 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "us_per_step": round(head["ms_per_step"] * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "decode_combine_us": round(attn_ms * 1e3, 2),
-        "decode_combine_project_us": round(proj_ms * 1e3, 2),
-        "history_fill": fill,
-        "decode_kernel_us": round(dec_ms * 1e3, 2),
-        "qknorm_overhead_pct": overhead,
+        "decode_kernel_us": hs["decode_kernel_us"],
+        "decode_combine_us": hs["decode_combine_us"],
+        "decode_combine_project_us": hs["decode_combine_project_us"],
+        "qknorm_overhead_pct": hs["qknorm_overhead_pct"],
+        "history_fill": head["fill"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.cache_dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "s_q": wl.s_q, "heads": wl.heads,
-                   "kv_groups": wl.groups, "rank": wl.rank, "rope_dim": wl.rope_dim,
-                   "seq_len": int(np.mean(inp["seq_lens"])), "num_splits": splits,
-                   "cache": wl.cache_dtype, "cache_bytes": nbytes, "flops": flops,
-                   "kernel": "mfma" if kind == 1 else "generic"},
+        "config": {k: v for k, v in hs.items()
+                   if k in ("workload", "batch", "s_q", "heads", "kv_groups", "rank", "rope_dim",
+                            "seq_len", "num_splits", "kernel", "cache_bytes", "flops")}
+                  | {"cache": wl.cache_dtype},
         "roofline": roof,
+        "workloads": [hs] + others,
+        "qknorm_sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
