@@ -462,6 +462,32 @@ def qknorm_sweep(Q, W, torch, timer, lengths=(4096, 8192, 16384, 32768, 65536, 1
     return out
 
 
+def profile_run(Q, W, torch, name, launches):
+    """Only `launches` eager decode + combine calls of one workload over its
+    rotating cache replicas, after one warm-up call: the program the
+    rocprofv3 counter and trace summaries are taken from."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, seed=0)
+    splits = default_splits(wl, inp["seq_lens"])
+    r = DecodeRunner(wl, inp, num_splits=splits)
+    r.fill_history()
+    r.prepare()
+    cache_bytes = r.kv.numel() * r.kv.element_size() + r.alpha_k.numel() * 4
+    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / cache_bytes) + 1)
+    kvs = [r.kv] + [r.kv.clone() for _ in range(n_rep - 1)]
+    aks = [r.alpha_k] + [r.alpha_k.clone() for _ in range(n_rep - 1)]
+    torch.cuda.synchronize()
+    for k in range(launches + 1):
+        r.kv, r.alpha_k = kvs[k % n_rep], aks[k % n_rep]
+        r.decode()
+        r.combine()
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": name, "num_splits": splits, "launches": launches + 1,
+                      "replicas": n_rep}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -473,6 +499,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch-1 QK-norm sweep")
     ap.add_argument("--no-overhead", action="store_true", help="skip the alpha-free timings")
+    ap.add_argument("--profile", type=int, default=0, metavar="N",
+                    help="only run N + 1 eager decode + combine calls of --workload (the "
+                         "program rocprofv3 profiles) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -500,6 +529,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Q.library()
+    if args.profile:
+        profile_run(Q, W, torch, args.workload, args.profile)
+        return
     timer = Timer(torch)
 
     def run(name, headline):

@@ -60,6 +60,8 @@
 // LDS banks.
 #include <math.h>
 
+#include <type_traits>
+
 #include "qkn_internal.h"
 
 namespace qkn {
@@ -104,6 +106,23 @@ constexpr float kLn2 = 0.6931471805599453f;
 // by measuring, on gfx950, every invertible map for the two read patterns of
 // this kernel (32 rows x one chunk for QK, 8 rows x 4 chunks of transposed
 // 8-byte reads for PV); this one runs both near the best rate seen.
+// f(integral_constant<int, I>) for I = B .. E - 1, in order, each I a
+// compile-time constant: the products of a stage and the vector steps placed
+// between them are straight-line code whatever the size of the loop body.
+template <int B, int E>
+struct Unroll {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, B>{});
+    Unroll<B + 1, E>::run(f);
+  }
+};
+template <int E>
+struct Unroll<E, E> {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
+
 __device__ __forceinline__ int swz(int t) {
   return static_cast<int>((0x81d4a3f6e7b2c590ull >> (4 * (t & 15))) & 15);
 }
@@ -157,13 +176,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const LDS_AS uint8_t* p) {
       reinterpret_cast<LDS_AS bf16x4*>(const_cast<LDS_AS uint8_t*>(p)));
 }
 
-// The lane index, re-materialised where it is used: the empty volatile asm
-// keeps per-lane offsets derived from it from being hoisted out of the page
-// loop and held in registers for the whole kernel.
-__device__ __forceinline__ int fresh_lane() {
-  int l = threadIdx.x & 63;
-  asm volatile("" : "+v"(l));
-  return l;
+// A per-lane value the compiler must take as new at this point: the empty
+// volatile asm keeps the addresses derived from it inside the stage loop (one
+// instruction each per stage) instead of being hoisted out of the loop and
+// held in registers for the whole kernel, where they would not fit.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -214,7 +233,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int s_q, int heads,
     int groups, int max_pages, int num_pages, int num_splits, int row_blocks, int n_work,
     int per_xcd, float scale) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // a static allocation: its LDS address (0) is known when the kernel is
+  // compiled, so stage offsets fold into the read instructions
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
   // blocks are dealt to the 8 XCDs round-robin; give consecutive work items
   // (the row blocks and splits of one sequence) to the same XCD and L2
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   int wbase = 0;
   int pwin;
   auto load_window = [&](int base) {
-    const int j = first_page + base + fresh_lane();
+    const int j = first_page + base + lane;
     pwin = j < max_pages ? block_table[(size_t)b * max_pages + j] : -1;
   };
   load_window(0);
@@ -284,30 +305,64 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   // column operand of the alpha^k alpha^q product tile (see outer32)
   const float aq_col = hh == 0 ? aq : 0.f;
 
+  // ---- per-lane constants of the LDS traffic (stage offsets are added per
+  // stage, or folded into the instructions' immediate offsets) ----
+  // DMA: content token t = w + 4k goes to chunk lane ^ f(t), i.e. byte
+  // (16 lane) ^ (16 f(t)) of its row
+  const uint32_t lane16 = static_cast<uint32_t>(lane << 4);
+  // RoPE keys of tokens 8w .. 8w + 7: token 8w + lane / 8, chunk (lane % 8) ^ f_R(token)
+  const uint32_t dma_r = static_cast<uint32_t>(
+      (8 * w + (lane >> 3)) * ROW_BYTES + R * 2 + (((lane & 7) ^ swz_rope(8 * w + (lane >> 3))) << 4));
+  // alpha^k of the stage transposed to [G][32 tokens]: slot i = g * 32 + t
+  // takes element (t, g) of the rows; wave w fills slots 8Gw .. 8Gw + 8G - 1
+  const bool dma_a_lane = lane < 8 * groups;
+  const uint32_t dma_a = static_cast<uint32_t>(
+      (((8 * groups * w + lane) & 31) * groups + ((8 * groups * w + lane) >> 5)) * 4);
+  // QK row read of token l32, chunk 2 kk + hh:
+  //   [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8)
+  const uint32_t qk_lane = static_cast<uint32_t>(l32 * 1024 + ((hh ^ swz(l32)) << 4));
+  // RoPE row read, chunk 2 kk + hh (kk < 4): [l32*128 + ((hh ^ f_R(l32)) << 4)] ^ (32 kk)
+  const uint32_t rp_lane =
+      static_cast<uint32_t>(l32 * 128 + ((hh ^ swz_rope(l32)) << 4) + CONTENT_BYTES);
+  // PV transposed read of latents 32 om .. +31, tokens 16 ks + 4 hh + (0..3)
+  // [+ 8]: within a 16-lane group G, row t = 4 hh + l16 / 4, chunk 4 om + 2 G +
+  // (l16 % 4) / 2, byte 8 (l16 % 2):
+  //   [t*1024 + 8 (l16 % 2) + ((c_lo ^ f(t)) << 4)] ^ (64 (om % 4)) + 256 (om / 4) + 16384 ks
+  // with c_lo = 2 G + (l16 % 4) / 2; the + 8 rows use their own base.
+  uint32_t pv_lane0, pv_lane1;
+  {
+    const int l16 = lane & 15, G16 = (lane >> 4) & 1;
+    const int t = 4 * hh + (l16 >> 2);
+    const int c_lo = 2 * G16 + ((l16 & 3) >> 1);
+    pv_lane0 = static_cast<uint32_t>(t * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t)) << 4));
+    pv_lane1 = static_cast<uint32_t>((t + 8) * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t + 8)) << 4));
+  }
+  const uint32_t ak_lane = static_cast<uint32_t>(CONTENT_BYTES + ROPE_BYTES + (g * ST + l32) * 4);
+
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS uint8_t*)smem));
+  const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
   // validity of the pages of the stages in the ring, bit s mod 4 (uniform)
   uint32_t vmask = 0;
 
   // The 10 loads of this wave for stage s (tokens lo + 32 s ..) into buffer
   // s mod 4: 8 content rows, a quarter of the RoPE block, and a quarter of
   // alpha^k on lanes 0 .. 8G-1 (lane 0 always takes part, so every wave
-  // issues all 10 and the vmcnt bookkeeping holds).  plan() looks the page up
-  // and builds the descriptors; load(k) issues load k.
-  struct StagePlan {
-    i32x4 rs, ra;  // KV rows of the stage, alpha^k rows of the stage
-    uint32_t buf;  // LDS address of the stage buffer
+  // issues all 10 and the vmcnt bookkeeping holds).  The two stages of a page
+  // share its plan: plan_page() looks the page up and builds descriptors that
+  // end at its last valid token; load(k) issues load k of either half (the
+  // second half starts 32 rows into the page).
+  struct PagePlan {
+    i32x4 rs, ra;  // KV rows of the page, alpha^k rows of the page
   };
-  auto plan = [&](int s) {
+  auto plan_page = [&](int s) {  // s: the first stage of the page (even)
     const int rel = s >> 1;  // page of the split
+    PagePlan pp;
     if (s >= n_st) {
-      // no such stage: its loads read nothing (size 0) and write zeros into
-      // a buffer nobody reads, which keeps the load count of every stage the same
-      StagePlan pl;
-      pl.rs = buffer_rsrc(kv, 0);
-      pl.ra = buffer_rsrc(alpha_k, 0);
-      pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
-      asm volatile("" : "+s"(pl.buf));
-      return pl;
+      // no such page: its loads read nothing (size 0) and write zeros into a
+      // buffer nobody reads, which keeps the load count of every stage the same
+      pp.rs = buffer_rsrc(kv, 0);
+      pp.ra = buffer_rsrc(alpha_k, 0);
+      return pp;
     }
     if (rel < wbase || rel >= wbase + 64) {  // uniform; once per 64 pages
       wbase = rel & ~63;
@@ -318,48 +373,51 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     }
     int pg = __builtin_amdgcn_readlane(pwin, rel - wbase);
     pg = (pg >= 0 && pg < num_pages) ? pg : -1;
-    vmask = (vmask & ~(1u << (s & 3))) | ((pg >= 0 ? 1u : 0u) << (s & 3));
+    const uint32_t ok = pg >= 0 ? 3u : 0u;  // validity of both stages of the page
+    vmask = (vmask & ~(3u << (s & 3))) | (ok << (s & 3));
     const int tok0 = lo + s * ST;
-    const int nv = pg >= 0 ? min(ST, T - tok0) : 0;   // valid rows of the stage
-    const size_t row0s = (size_t)(pg >= 0 ? pg : 0) * PAGE + (s & 1) * ST;  // cache row
-    StagePlan pl;
-    pl.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0s * ROW_BYTES, nv * ROW_BYTES);
+    const int nv = pg >= 0 ? min(PAGE, T - tok0) : 0;   // valid rows of the page
+    const size_t row0s = (size_t)(pg >= 0 ? pg : 0) * PAGE;  // cache row
+    pp.rs = buffer_rsrc(reinterpret_cast<const uint8_t*>(kv) + row0s * ROW_BYTES, nv * ROW_BYTES);
     // the alpha-free instantiation reads no alpha^k bytes: its loads are still
     // issued (every stage keeps the same load count) but read nothing
-    pl.ra = buffer_rsrc(alpha_k + row0s * groups, USE_ALPHA ? nv * groups * 4 : 0);
+    pp.ra = buffer_rsrc(alpha_k + row0s * groups, USE_ALPHA ? nv * groups * 4 : 0);
+    return pp;
+  };
+  struct StagePlan {
+    i32x4 rs, ra;    // the page's descriptors
+    uint32_t buf;    // LDS address of the stage buffer
+    uint32_t half;   // which half of the page (0, 1)
+    uint32_t l16;    // 16 * lane, taken as new for this stage (see opaque)
+  };
+  auto stage_plan = [&](const PagePlan& pp, int s) {
+    StagePlan pl;
+    pl.rs = pp.rs;
+    pl.ra = pp.ra;
     pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
     asm volatile("" : "+s"(pl.buf));  // keep the per-load LDS addresses out of loop-invariant registers
+    pl.half = static_cast<uint32_t>(s & 1);
+    pl.l16 = opaque(lane16);
     return pl;
   };
   auto load = [&](const StagePlan& pl, int k) {
-    const int ln = fresh_lane();
     if (k < ST / WAVES) {
       // content token t = w + 4k at t * ROW_BYTES; the lane's chunk is lane ^ f(t)
       const int t = w + WAVES * k;
+      const uint32_t voff = (pl.l16 ^ static_cast<uint32_t>(swz(t) << 4)) +
+                            static_cast<uint32_t>(t * ROW_BYTES) + pl.half * (ST * ROW_BYTES);
       if (k == 0) {
-        dma16<true>(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
+        dma16<true>(pl.buf + t * 1024, voff, pl.rs);
       } else {
-        dma16<false>(pl.buf + t * 1024, t * ROW_BYTES + ((ln ^ swz(t)) << 4), pl.rs);
+        dma16<false>(pl.buf + t * 1024, voff, pl.rs);
       }
     } else if (k == ST / WAVES) {
-      // RoPE keys of tokens 8w .. 8w + 7: token 8 w + lane / 8, chunk (lane % 8) ^ f_R(token)
-      const int t = 8 * w + (ln >> 3);
-      dma16<false>(pl.buf + CONTENT_BYTES + w * 1024, t * ROW_BYTES + R * 2 + (((ln & 7) ^ swz_rope(t)) << 4), pl.rs);
+      dma16<false>(pl.buf + CONTENT_BYTES + w * 1024, opaque(dma_r) + pl.half * (ST * ROW_BYTES), pl.rs);
     } else {
-      // alpha^k of the stage, transposed to [G][32 tokens] on the way: slot
-      // i = g * 32 + t of the 32 G floats takes element (t, g) of the rows;
-      // wave w fills slots 8 G w .. 8 G w + 8 G - 1, one per lane
-      if (ln < 8 * groups) {
-        const int i = 8 * groups * w + ln;
+      if (dma_a_lane)
         dma4_first(pl.buf + CONTENT_BYTES + ROPE_BYTES + 32 * groups * w,
-                   ((i & 31) * groups + (i >> 5)) * 4, pl.ra);
-      }
+                   opaque(dma_a) + pl.half * (ST * 4 * groups), pl.ra);
     }
-  };
-  auto issue = [&](int s) {
-    const StagePlan pl = plan(s);
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) load(pl, k);
   };
 
   f32x16 acc[R / 32];
@@ -367,61 +425,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   float m_seen = -INFINITY;  // largest logit of this head seen so far
   float l_run = 0.f;         // this lane's share of the softmax denominator
   const float c2 = scale * kLog2e;  // logits -> log2 units
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // restart flag: set by any wave whose logits outgrew the reference, read by
   // all after the next barrier
   volatile LDS_AS int* flag = (volatile LDS_AS int*)((LDS_AS uint8_t*)smem + FLAG_OFFSET);
   if (tid == 0) *flag = 0;
-
-  const LDS_AS uint8_t* lds0 = (LDS_AS uint8_t*)smem;
-
-  // PV of stage s with the probabilities pb (token order of the S^T tile):
-  // O^T[512 x 32] += C^T[512 x 32 tok] . P^T over two 16-token steps.
-  // Transposed read of latents 32 om .. +31, tokens 16 ks + 4 hh + (0..3)
-  // [+ 8]: within a 16-lane group G, row t = 4 hh + l16 / 4, chunk 4 om + 2 G +
-  // (l16 % 4) / 2, byte 8 (l16 % 2):
-  //   [t*1024 + 8 (l16 % 2) + ((c_lo ^ f(t)) << 4)] ^ (64 (om % 4)) + 256 (om / 4) + 16384 ks
-  // with c_lo = 2 G + (l16 % 4) / 2; the + 8 rows use their own base.
-  // fill(n) runs after the n-th product: vector ALU work that needs no matrix
-  // result of this PV step, issued while the matrix core works on it
-  auto pv_stage = [&](int s, const bf16x8 (&pb)[2], auto&& fill) {
-    const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
-    // the four XOR variants of both bases, so that every read below is a
-    // register plus an immediate (stage offsets leave bits 5-9 alone)
-    uint32_t xb0[4], xb1[4];
-    {
-      const int ln = fresh_lane();
-      const int l16 = ln & 15, G = (ln >> 4) & 1, h = ln >> 5;
-      const int t = 4 * h + (l16 >> 2);
-      const int c_lo = 2 * G + ((l16 & 3) >> 1);
-      const uint32_t b0 = t * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t)) << 4) + stage_off;
-      const uint32_t b1 = (t + 8) * 1024 + 8 * (l16 & 1) + ((c_lo ^ swz(t + 8)) << 4) + stage_off;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xb0[j] = b0 ^ (64u * j);
-        xb1[j] = b1 ^ (64u * j);
-      }
-    }
-    // products n = (ks, om) in that order
-    constexpr int NP = 2 * (R / 32);
-    bf16x8 abuf[PV_AHEAD];
-    auto rd = [&](int n) {
-      const int ks = n / (R / 32), om = n % (R / 32);
-      const uint32_t off = 256 * (om >> 2) + 16384 * ks;
-      const bf16x4 lo4 = lds_read_tr(lds0 + xb0[om & 3] + off);
-      const bf16x4 hi4 = lds_read_tr(lds0 + xb1[om & 3] + off);
-      return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-#pragma unroll
-    for (int n = 0; n < PV_AHEAD; ++n) abuf[n] = rd(n);
-#pragma unroll
-    for (int n = 0; n < NP; ++n) {
-      const bf16x8 a = abuf[n % PV_AHEAD];
-      if (n + PV_AHEAD < NP) abuf[n % PV_AHEAD] = rd(n + PV_AHEAD);
-      mfma_acc(acc[n % (R / 32)], a, pb[n / (R / 32)]);
-      fill(n);
-    }
-  };
 
   // PV of "stage -1" reads buffer 3 with zero probabilities: clear that
   // buffer once so that it holds finite values (later it only ever holds
@@ -438,153 +447,211 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 #pragma unroll
     for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
     l_run = 0.f;
-    issue(0);
-    issue(1);
+    PagePlan page = plan_page(0);
+    {
+      const StagePlan p0 = stage_plan(page, 0);
+#pragma unroll
+      for (int k = 0; k < LOADS; ++k) load(p0, k);
+      const StagePlan p1 = stage_plan(page, 1);
+#pragma unroll
+      for (int k = 0; k < LOADS; ++k) load(p1, k);
+    }
     asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage 0 has landed
     __syncthreads();
-    bf16x8 pprev[2] = {};  // probabilities of the previous stage
+    // probabilities of the previous stage / of this one, swapped every stage
+    bf16x8 pA[2] = {}, pB[2];
+
+    // PV of stage sp with the probabilities pb: O^T[512 x 32] += C^T[512 x 32
+    // tok] . P^T over two 16-token steps, products n = (ks, om) in that
+    // order, operands read PV_AHEAD products ahead; fill(n) runs after the
+    // n-th product (vector work that needs no result of this PV)
+    auto pv_stage = [&](int sp, const bf16x8 (&pb)[2], auto&& fill) {
+      const uint32_t off_s = (sp & (NSTAGE - 1)) * STAGE_BYTES;
+      uint32_t xb0[4], xb1[4];
+      const uint32_t b0 = opaque(pv_lane0), b1 = opaque(pv_lane1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xb0[j] = (b0 ^ (64u * j)) + off_s;
+        xb1[j] = (b1 ^ (64u * j)) + off_s;
+      }
+      constexpr int NP = 2 * (R / 32);
+      bf16x8 pbuf[PV_AHEAD];
+      auto rdp = [&](int n) {
+        const int ks = n / (R / 32), om = n % (R / 32);
+        const uint32_t off = 256 * (om >> 2) + 16384 * ks;
+        const bf16x4 lo4 = lds_read_tr(lds0 + xb0[om & 3] + off);
+        const bf16x4 hi4 = lds_read_tr(lds0 + xb1[om & 3] + off);
+        return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int n = 0; n < PV_AHEAD; ++n) pbuf[n] = rdp(n);
+      __builtin_amdgcn_sched_barrier(0);
+      Unroll<0, NP>::run([&](auto N) {
+        constexpr int n = decltype(N)::value;
+        const bf16x8 a = pbuf[n % PV_AHEAD];
+        if constexpr (n + PV_AHEAD < NP) pbuf[n % PV_AHEAD] = rdp(n + PV_AHEAD);
+        mfma_acc(acc[n % (R / 32)], a, pb[n / (R / 32)]);
+        fill(N);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
 
     // iteration s: QK and softmax of stage s (s < n_st) and PV of stage s - 1;
     // it ends with the one barrier of the iteration, after which stage s + 1
     // is in LDS, every wave is done with stage s - 1, and the restart flag
     // of stage s is visible
-    for (int s = 0; s <= n_st; ++s) {
+    // one iteration; HALF = s mod 2 (the stages of a page alternate), pprev the
+    // probabilities of stage s - 1, pnew those of stage s.  Returns whether the
+    // split must restart.
+    auto iteration = [&](auto HALF, int s, bf16x8 (&pprev)[2], bf16x8 (&pnew)[2]) -> bool {
       const bool has_qk = s < n_st;
-      // the loads of stage s + 2 go into the buffer of stage s - 2
-      const StagePlan pl = plan(s + 2);
+      // the loads of stage s + 2 go into the buffer of stage s - 2; an even
+      // stage s + 2 starts a page and takes its plan, an odd one reuses it
+      if constexpr (decltype(HALF)::value == 0) page = plan_page(s + 2);
+      const StagePlan pl = stage_plan(page, s + 2);
       const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
-      const LDS_AS float* st_alpha = (const LDS_AS float*)(lds0 + stage_off + CONTENT_BYTES + ROPE_BYTES);
       const int tok0 = lo + s * ST;
       const bool page_ok = (vmask >> (s & 3)) & 1u;
       if (has_qk && !page_ok) err = 1;
-      // rows r of this stage with r < lim are visible to this wave
+      // rows r of this stage with r < lim are visible to this wave; past the
+      // last stage none (the softmax steps then only produce zeros)
       const int lim = (has_qk && page_ok) ? hi_w - tok0 : 0;
       int overflow = 0;
 
       if (!wave_active) {
 #pragma unroll
         for (int k = 0; k < LOADS; ++k) load(pl, k);
-      }
-      if (wave_active) {
-        // S_c (or S, without the inverse-RMS factors), the RoPE dot R and the
-        // factor tile F; past the last stage S_c = F = 0 and R = -inf
-        f32x16 sc = {}, rp = {}, fac = {};
+      } else {
+        // ---- QK: S_c^T[32 tok x 32 heads] over the 512 latents (with the
+        // RoPE dot first when there are no factors).  The latent rows are read
+        // QK_AHEAD products ahead; the scheduling fences keep every read and
+        // product at its place in that order.
+        // past the last stage the tiles keep whatever they hold: every row
+        // is masked to -inf before it is used
+        f32x16 sc, fac;
+        bf16x8 rope_a[DR / 16];
         if (has_qk) {
-          // ---- QK: RoPE and F, then S_c^T[32 tok x 32 heads] over the 512 latents ----
-          // Row read of token l32, chunk 2 kk + hh:
-          //   [l32*1024 + ((hh ^ f(l32)) << 4)] ^ (32 (kk % 8)) + 256 (kk / 8)
-          // RoPE row read, chunk 2 kk + hh (kk < 4):
-          //   [l32*128 + ((hh ^ f_R(l32)) << 4)] ^ (32 kk)
-          uint32_t qx[8], rx[DR / 16];
-          {
-            const int ln = fresh_lane();
-            const int t = ln & 31, h = ln >> 5;
-            const uint32_t qk_b = t * 1024 + ((h ^ swz(t)) << 4) + stage_off;
-            const uint32_t rp_b = t * 128 + ((h ^ swz_rope(t)) << 4) + stage_off + CONTENT_BYTES;
+          const uint32_t rp_l = opaque(rp_lane);
+          constexpr int NK = R / 16;
+          bf16x8 abuf[QK_AHEAD];
+          // each read forms its own address right before it (one xor-add
+          // from the lane base, which is taken as new for every read), so no
+          // address is held in a register across the chain
+          uint32_t qx[8];
+          const uint32_t qk_l = opaque(qk_lane);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qx[j] = qk_b ^ (32u * j);
+          for (int j = 0; j < 8; ++j) qx[j] = (qk_l ^ (32u * j)) + stage_off;
+          auto rd = [&](int n) { return lds_read16(lds0 + qx[n & 7] + 256 * (n >> 3)); };
 #pragma unroll
-            for (int j = 0; j < DR / 16; ++j) rx[j] = rp_b ^ (32u * j);
+          for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
+          if (!USE_ALPHA) {
+#pragma unroll
+            for (int kk = 0; kk < DR / 16; ++kk)
+              rope_a[kk] = lds_read16(lds0 + ((rp_l ^ (32u * kk)) + stage_off));
           }
-          // The RoPE dot R^T = K^R . q^R^T, then the content products S_c over
-          // the 512 latents.  Without the inverse-RMS factors S_c accumulates
-          // onto R.  With them R has an accumulator of its own and the tile
-          // F = alpha^k alpha^q (token by head) is one float32 outer product on
-          // the matrix core (outer32) from alpha^k of token l % 32 (one LDS
-          // read) and this lane's alpha^q; S = S_c F + R, one fused
-          // multiply-add per logit, is formed in the first softmax steps, under
-          // the matrix products of the previous stage's PV.
-          {
-            bf16x8 rope_a[DR / 16];
+          __builtin_amdgcn_sched_barrier(0);
+          if (!USE_ALPHA) {
+            sc = mfma(rope_a[0], qrb[0], f32x16{});
 #pragma unroll
-            for (int kk = 0; kk < DR / 16; ++kk) rope_a[kk] = lds_read16(lds0 + rx[kk]);
-            float ak_row = 0.f;
-            if (USE_ALPHA) ak_row = st_alpha[g * ST + l32];
-            constexpr int NK = R / 16;
-            // the RoPE products (and F) first: they do not depend on S_c, so the
-            // softmax can start as soon as the content chain ends
-            if (USE_ALPHA) {
-#pragma unroll
-              for (int kk = 0; kk < DR / 16; ++kk) rp = mfma(rope_a[kk], qrb[kk], rp);
-              fac = outer32(ak_row, aq_col);
+            for (int kk = 1; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float ak_row = 0.f;
+          Unroll<0, NK>::run([&](auto N) {
+            constexpr int n = decltype(N)::value;
+            const bf16x8 a = abuf[n % QK_AHEAD];
+            if constexpr (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
+            if constexpr (USE_ALPHA && n == 0) {
+              sc = mfma(a, qb[n], f32x16{});
             } else {
-#pragma unroll
-              for (int kk = 0; kk < DR / 16; ++kk) sc = mfma(rope_a[kk], qrb[kk], sc);
-            }
-            bf16x8 abuf[QK_AHEAD];
-            auto rd = [&](int n) { return lds_read16(lds0 + qx[n & 7] + 256 * (n >> 3)); };
-#pragma unroll
-            for (int n = 0; n < QK_AHEAD; ++n) abuf[n] = rd(n);
-#pragma unroll
-            for (int n = 0; n < NK; ++n) {
-              const bf16x8 a = abuf[n % QK_AHEAD];
-              if (n + QK_AHEAD < NK) abuf[n % QK_AHEAD] = rd(n + QK_AHEAD);
               sc = mfma(a, qb[n], sc);
-              if (n % 3 == 1 && n / 3 < LOADS) load(pl, n / 3);
             }
-          }
-        }
-        // ---- mask rows past the visible end (tail page, causal window, bad
-        // page; past the last stage every row, which makes the softmax steps
-        // below a no-op without branching around them).  S^T tile layout: lane
-        // holds head l32 and tokens r % 4 + 8 (r / 4) + 4 hh for its 16
-        // registers r.  With the factors the mask goes into R: S_c F is finite,
-        // so S = S_c F - inf = -inf.
-        if (__builtin_expect(lim < ST, 0)) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if ((r & 3) + 8 * (r >> 2) + 4 * hh >= lim) {
-              if (USE_ALPHA) {
-                rp[r] = -INFINITY;
-              } else {
-                sc[r] = -INFINITY;
+            if constexpr (n % 3 == 1 && n / 3 < LOADS) load(pl, n / 3);
+            if constexpr (USE_ALPHA) {
+              // near the chain's end, in the registers its last reads free:
+              // alpha^k of token l % 32 and two RoPE rows, then F^T =
+              // alpha^k alpha^q as one float32 outer product (outer32),
+              // independent of the chain
+              if constexpr (n == NK - QK_AHEAD - 2)
+                ak_row = *reinterpret_cast<const LDS_AS float*>(lds0 + opaque(ak_lane) + stage_off);
+              if constexpr (n >= NK - 2) {
+                constexpr int kk = n - (NK - 2);
+                rope_a[kk] = lds_read16(lds0 + ((rp_l ^ (32u * kk)) + stage_off));
               }
+              if constexpr (n == NK - 2) fac = outer32(ak_row, aq_col);
             }
-          }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        } else {
+#pragma unroll
+          for (int k = 0; k < LOADS; ++k) load(pl, k);
         }
-        // ---- PV of the previous stage, with the probabilities of this one
-        // computed between its products ----
+        // ---- softmax of this stage between the products of the previous
+        // stage's PV.  With the factors: S = S_c F, then the RoPE products
+        // accumulate onto it on the matrix core (S = S_c F + K^R q^R^T).
+        // Rows past the visible end (tail page, causal window, bad page) are
+        // then set to -inf.  S^T tile layout: lane holds head l32 and tokens
+        // r % 4 + 8 (r / 4) + 4 hh for its 16 registers r.
         float mx = -INFINITY, mc = 0.f;
-        bf16x8 pnew[2];
-        auto softmax_step = [&](int n) {
-          if (n == 0) {
+        auto softmax_step = [&](auto N) {
+          constexpr int n = decltype(N)::value;
+          constexpr int M = USE_ALPHA ? 3 : 0;  // steps taken by the factors and RoPE
+          if constexpr (USE_ALPHA && n == 0) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              if (USE_ALPHA) sc[r] = fmaf(sc[r], fac[r], rp[r]);
-              mx = fmaxf(mx, sc[r]);
-            }
-          } else if (n == 1) {
+            for (int r = 0; r < 16; ++r) sc[r] *= fac[r];
+            const uint32_t rp_l2 = opaque(rp_lane);
+            rope_a[2] = lds_read16(lds0 + ((rp_l2 ^ 64u) + stage_off));
+            rope_a[3] = lds_read16(lds0 + ((rp_l2 ^ 96u) + stage_off));
+          } else if constexpr (USE_ALPHA && n == 1) {
+            sc = mfma(rope_a[0], qrb[0], sc);
+            sc = mfma(rope_a[1], qrb[1], sc);
+          } else if constexpr (USE_ALPHA && n == 2) {
+            sc = mfma(rope_a[2], qrb[2], sc);
+            sc = mfma(rope_a[3], qrb[3], sc);
+          } else if constexpr (n == M) {
+            if (__builtin_expect(lim < ST, 0)) {
+              // register r holds token (r % 4) + 8 (r / 4) + 4 hh: compare the
+              // constant part against lim - 4 hh (no per-register lane values)
+              const int lim_l = lim - 4 * hh;
 #pragma unroll
-            for (int r = 8; r < 16; ++r) {
-              if (USE_ALPHA) sc[r] = fmaf(sc[r], fac[r], rp[r]);
-              mx = fmaxf(mx, sc[r]);
+              for (int r = 0; r < 16; ++r)
+                if ((r & 3) + 8 * (r >> 2) >= lim_l) sc[r] = -INFINITY;
             }
-          } else if (n == 2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+          } else if constexpr (n == M + 1) {
             mx = pair_max(mx);
             m_seen = fmaxf(m_seen, mx);
             if (m_ref == -INFINITY) m_ref = mx;  // first visible tokens of the split
             if ((mx - m_ref) * c2 > kMaxExp2) overflow = 1;
             mc = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-          } else if (n >= 3 && n < 3 + 8) {
+          } else if constexpr (n >= M + 2 && n < M + 2 + 8) {
             // P^T as the B operand of the two 16-token steps: registers 8 ks .. 8 ks + 7
-            const int r = 2 * (n - 3);
+            constexpr int r = 2 * (n - (M + 2));
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mc));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -mc));
             const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
             pnew[r >> 3][r & 7] = pr[0];
             pnew[r >> 3][(r & 7) + 1] = pr[1];
-            l_run += static_cast<float>(pr[0]) + static_cast<float>(pr[1]);
+            // the denominator is the sum of the same rounded values
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
           }
         };
         pv_stage(s - 1, pprev, softmax_step);
-        pprev[0] = pnew[0];
-        pprev[1] = pnew[1];
       }
       // did any head outgrow its reference?
       if (__builtin_amdgcn_ballot_w64(overflow != 0)) *flag = 1;
       asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage s + 1 has landed
       __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(*flag)) {
+      return __builtin_amdgcn_readfirstlane(*flag) != 0;
+    };
+    for (int s = 0; s <= n_st; s += 2) {
+      if (iteration(std::integral_constant<int, 0>{}, s, pA, pB)) {
+        again = true;
+        break;
+      }
+      if (s + 1 > n_st) break;
+      if (iteration(std::integral_constant<int, 1>{}, s + 1, pB, pA)) {
         again = true;
         break;
       }
@@ -606,7 +673,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   if (wave_active) {
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int ln = fresh_lane();
+    const int ln = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
     const size_t row_e = ((size_t)b * s_q + i) * heads + h0 + (ln & 31);
     // accumulator tile om: lane holds head l32 and latents 32 om + r % 4 +
     // 8 (r / 4) + 4 hh.  The two lanes of a head (l, l ^ 32) trade halves so
@@ -647,14 +714,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 
 template <bool USE_ALPHA>
 hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
-  const hipError_t e = set_lds_limit_once(
-      reinterpret_cast<const void*>(&decode_mfma_kernel<USE_ALPHA>), LDS_BYTES);
-  if (e != hipSuccess) return e;
   const int row_blocks = cdiv(d.s_q * d.heads, ROWS_PER_WG);
   const int n_work = d.batch * a.num_splits * row_blocks;
   const int per_xcd = cdiv(n_work, 8);
   dim3 grid(per_xcd * 8);
-  hipLaunchKernelGGL(decode_mfma_kernel<USE_ALPHA>, grid, dim3(64 * WAVES), LDS_BYTES, s,
+  hipLaunchKernelGGL(decode_mfma_kernel<USE_ALPHA>, grid, dim3(64 * WAVES), 0, s,
                      static_cast<const uint16_t*>(a.q_tilde), a.alpha_q,
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint16_t*>(a.kv),
                      a.alpha_k, a.block_table, a.seq_lens, static_cast<_Float16*>(a.o_part),
