@@ -60,30 +60,42 @@ def default_splits(wl, seq_lens, cus=256):
     Cost model, in units of one 32-token stage of one workgroup (about 2 us on
     MI355X for 128 query rows): a workgroup costs WG_FIXED (its prologue, which
     loads q~ and the first stages, and its epilogue, which writes the
-    partials) plus its stage count.  The decode kernel deals work item w =
-    (b P + p) R + r (R row blocks) to XCD w / ceil(n / 8), and each XCD's 32
-    CUs take their items in order as they free up (one workgroup per CU); the
-    combine costs its partial bytes, written and read back, at about 6 TB/s.
-    With WG_FIXED = 8 this reproduces the measured decode times of the
-    workloads within a few percent.  Equal lengths then get the count that
-    fills the CUs once; a ragged batch (a few long sequences) gets more."""
+    partials) plus its stage count.  The decode kernel deals its items the
+    way the kernel does: equal lengths (or more than 64 sequences) in index
+    order, XCD x taking the x-th eighth of the items; a ragged batch of up to
+    64 sequences longest sequence first, its (sequence, split) pairs dealt
+    round-robin over the XCDs, the row blocks of a pair together.  Each XCD's
+    32 CUs take their items in order as they free up (one workgroup per CU);
+    the combine costs its partial bytes, written and read back, at about
+    6 TB/s.  Equal lengths then get the count that fills the CUs once; a
+    ragged batch gets the count that best evens out its long sequences."""
     WG_FIXED, STAGE_US = 8.0, 2.0
     R = math.ceil(wl.s_q * wl.heads / 128)
     rows = wl.batch * wl.s_q * wl.heads
+    lens = [int(T) for T in seq_lens]
+    ragged = len(lens) <= 64 and len(set(lens)) > 1
+    order = sorted(range(len(lens)), key=lambda b: (-lens[b], b)) if ragged else range(len(lens))
     best = None
     for P in range(1, min(512, max(1, 8 * cus // (wl.batch * R))) + 1):
+        queues = [[] for _ in range(8)]
         items = []
-        for T in seq_lens:
-            T = int(T)
+        for b in order:
+            T = lens[b]
             L = split_len(max(T, 1), P)
             for p in range(P):
                 n = min(T, (p + 1) * L) - p * L
-                items += [WG_FIXED + math.ceil(n / 32) if n > 0 else 1.0] * R
-        per_xcd = math.ceil(len(items) / 8)
+                items.append([WG_FIXED + math.ceil(n / 32) if n > 0 else 1.0] * R)
+        if ragged:
+            for k, its in enumerate(items):
+                queues[k % 8] += its
+        else:
+            flat = [c for its in items for c in its]
+            per_xcd = math.ceil(len(flat) / 8)
+            queues = [flat[x * per_xcd:(x + 1) * per_xcd] for x in range(8)]
         makespan = 0.0
-        for x in range(8):
+        for q in queues:
             loads = [0.0] * (cus // 8)
-            for c in items[x * per_xcd:(x + 1) * per_xcd]:
+            for c in q:
                 heapq.heappush(loads, heapq.heappop(loads) + c)
             makespan = max(makespan, max(loads))
         t = makespan * STAGE_US + rows * P * wl.rank * 2 * 2 / 6e12 * 1e6

@@ -60,6 +60,7 @@
 // LDS banks.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "qkn_internal.h"
@@ -230,24 +231,61 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv,
     const float* __restrict__ alpha_k, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, _Float16* __restrict__ o_part,
-    float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int s_q, int heads,
+    float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int batch, int s_q, int heads,
     int groups, int max_pages, int num_pages, int num_splits, int row_blocks, int n_work,
     int per_xcd, float scale) {
   // a static allocation: its LDS address (0) is known when the kernel is
   // compiled, so stage offsets fold into the read instructions
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
-  // blocks are dealt to the 8 XCDs round-robin; give consecutive work items
-  // (the row blocks and splits of one sequence) to the same XCD and L2
-  const int wg = blockIdx.x;
-  const int work = (wg & 7) * per_xcd + (wg >> 3);
-  if (work >= n_work) return;
-  const int rb = work % row_blocks;
-  const int p = (work / row_blocks) % num_splits;
-  const int b = work / (row_blocks * num_splits);
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+
+  // The work item (sequence b, split p, row block rb) of this block.  Blocks
+  // are dealt to the 8 XCDs round-robin (block 8 j + x is the j-th of XCD x)
+  // and the CUs of an XCD take its blocks in order as they free up.
+  //  - Equal lengths, or a batch over 64: XCD x takes the consecutive items
+  //    x n/8 .. (x + 1) n/8 - 1, so that the row blocks and splits of one
+  //    sequence share an L2.
+  //  - Ragged lengths: the (sequence, split) pairs, longest sequence first,
+  //    are dealt round-robin over the XCDs, the row blocks of a pair staying
+  //    together (they read the same pages).  Each XCD then holds the same
+  //    mix of lengths and takes its longest items first, which keeps the
+  //    XCDs, and the CUs of each, within about one item of one another.
+  const int wg = blockIdx.x;
+  int b, p, rb;
+  {
+    bool ragged = false;
+    int rank = 0;  // place of sequence `lane` in the order (longest first, ties by index)
+    if (batch <= 64) {
+      const int tl = lane < batch ? seq_lens[lane] : 0;
+      const int t0 = __builtin_amdgcn_readfirstlane(tl);
+      ragged = __ballot(lane < batch && tl != t0) != 0;
+      if (ragged) {
+        for (int j = 0; j < batch; ++j) {
+          const int tj = __builtin_amdgcn_readlane(tl, j);
+          rank += (tj > tl || (tj == tl && j < lane)) ? 1 : 0;
+        }
+      }
+    }
+    if (ragged) {
+      const int pos = wg >> 3;
+      rb = pos % row_blocks;
+      const int k = (pos / row_blocks) * 8 + (wg & 7);  // pair k of the order
+      if (k >= batch * num_splits) return;
+      const int o = k / num_splits;
+      p = k - o * num_splits;
+      // the ranks are a permutation of 0 .. batch - 1: exactly one lane has rank o
+      b = static_cast<int>(__builtin_ctzll(__ballot(lane < batch && rank == o)));
+    } else {
+      if ((wg >> 3) >= per_xcd) return;
+      const int work = (wg & 7) * per_xcd + (wg >> 3);
+      if (work >= n_work) return;
+      rb = work % row_blocks;
+      p = (work / row_blocks) % num_splits;
+      b = work / (row_blocks * num_splits);
+    }
+  }
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int l32 = lane & 31;  // head within the wave
   const int hh = lane >> 5;   // which 8-wide half of a 16-long reduction step
@@ -717,12 +755,15 @@ hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t 
   const int row_blocks = cdiv(d.s_q * d.heads, ROWS_PER_WG);
   const int n_work = d.batch * a.num_splits * row_blocks;
   const int per_xcd = cdiv(n_work, 8);
-  dim3 grid(per_xcd * 8);
+  // enough blocks for either dealing of the work items (the kernel takes the
+  // longest-first one for a ragged batch of up to 64 sequences)
+  const int per_xcd_ragged = d.batch <= 64 ? cdiv(d.batch * a.num_splits, 8) * row_blocks : 0;
+  dim3 grid(8 * std::max(per_xcd, per_xcd_ragged));
   hipLaunchKernelGGL(decode_mfma_kernel<USE_ALPHA>, grid, dim3(64 * WAVES), 0, s,
                      static_cast<const uint16_t*>(a.q_tilde), a.alpha_q,
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint16_t*>(a.kv),
                      a.alpha_k, a.block_table, a.seq_lens, static_cast<_Float16*>(a.o_part),
-                     a.lse_part, a.err_flag, d.s_q,
+                     a.lse_part, a.err_flag, d.batch, d.s_q,
                      d.heads, d.groups, d.max_pages_per_seq, d.num_pages, a.num_splits, row_blocks,
                      n_work, per_xcd, d.softmax_scale);
   return hipGetLastError();

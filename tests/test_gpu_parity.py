@@ -454,6 +454,45 @@ def test_page_permutation_bitwise():
     assert torch.equal(a.o_latent, b.o_latent) and torch.equal(a.lse, b.lse)
 
 
+def test_work_dealing_ragged_batch_with_ties():
+    """A ragged batch of up to 64 sequences is dealt to the workgroups longest
+    sequence first, ties by index.  Every (sequence, split, row block) item
+    must be computed exactly once, and its result must not depend on which
+    workgroup draws it: 64 sequences of five distinct lengths (many ties, an
+    empty split at the shortest) are decoded, then decoded again in reverse
+    order, which breaks the ties the other way and hands the items to other
+    workgroups.  Put back in order, the partials match bit for bit, and no
+    sentinel survives in either run."""
+    wl = W.WORKLOADS["mtp"].replace(batch=64, seq_len=200, seq_len_range=None, num_splits=3)
+    inp = W.make_inputs(wl, seed=41)
+    lens = np.array([4, 64, 65, 130, 200], dtype=np.int32)[np.arange(64) * 7 % 5]
+    announce("work dealing: 64 ragged sequences with ties, forward and reversed")
+    r = DecodeRunner(wl, inp, num_splits=3)
+    r.fill_history()
+    r.prepare()
+    r.seq_lens.copy_(torch.from_numpy(lens).to("cuda"))
+
+    def run():
+        r.o_partial.fill_(float("nan"))
+        r.lse_partial.fill_(float("nan"))
+        r.err_flag.zero_()
+        r.decode()
+        torch.cuda.synchronize()
+        assert int(r.err_flag.item()) == 0
+        o, l = r.o_partial.clone(), r.lse_partial.clone()
+        assert not torch.isnan(o).any() and not torch.isnan(l).any()
+        return o, l
+
+    a_o, a_l = run()
+    perm = torch.arange(63, -1, -1, device="cuda")
+    for t in (r.block_table, r.seq_lens, r.q_tilde, r.alpha_q, r.q_rope_normed):
+        t.copy_(t[perm].clone())
+    b_o, b_l = run()
+    assert torch.equal(a_o, b_o[perm]) and torch.equal(a_l, b_l[perm])
+    # the shortest sequences leave their later splits empty
+    assert torch.all(torch.isneginf(a_l[torch.from_numpy(lens == 4).to("cuda")][..., 1:]))
+
+
 def test_deterministic():
     wl = P.small("grouped")
     inp = W.make_inputs(wl, seed=31)
