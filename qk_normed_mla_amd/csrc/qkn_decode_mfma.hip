@@ -254,11 +254,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   //    XCDs, and the CUs of each, within about one item of one another.
   const int wg = blockIdx.x;
   int b, p, rb;
+  int tl = 0;  // length of sequence `lane` (batch <= 64)
   {
     bool ragged = false;
     int rank = 0;  // place of sequence `lane` in the order (longest first, ties by index)
     if (batch <= 64) {
-      const int tl = lane < batch ? seq_lens[lane] : 0;
+      tl = lane < batch ? seq_lens[lane] : 0;
       const int t0 = __builtin_amdgcn_readfirstlane(tl);
       ragged = __ballot(lane < batch && tl != t0) != 0;
       if (ragged) {
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   int err = 0;
   bool restarted = false;
 
-  int T = seq_lens[b];
+  int T = batch <= 64 ? __builtin_amdgcn_readlane(tl, b) : seq_lens[b];
   if (T < 0 || T > max_pages * PAGE) {
     err = 1;
     T = min(max(T, 0), max_pages * PAGE);
@@ -314,6 +315,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   // row of this lane's head (an idle wave uses row 0 and discards its results)
   const size_t my_row = ((size_t)b * s_q + i) * heads + h0 + l32;
 
+  // The prologue's memory traffic overlaps: the first page of the split comes
+  // in by a scalar load, its two stages are issued as soon as it is in, and
+  // alpha^q, q~, q^R and the page-table window follow (vector loads; the
+  // page loads go first so that the HBM round trip starts early).  One wait
+  // for everything then precedes the first stage.  (The page loads are not
+  // visible to the compiler's own waits, so every vector load the compiler
+  // issued must be complete before the loop.)
+  const int first_pg = (first_page < max_pages && n_st > 0)
+                           ? block_table[(size_t)b * max_pages + first_page] : -1;
+  float aq;
+  // q~ and q^R as the B operand of QK: lane holds q[head l32][16 kk + 8 hh .. +8]
+  bf16x8 qb[R / 16];
+  bf16x8 qrb[DR / 16];
+  auto load_query = [&]() {
+    aq = USE_ALPHA ? alpha_q[my_row] : 1.f;
+    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + hh;
+#pragma unroll
+    for (int kk = 0; kk < R / 16; ++kk) qb[kk] = qt[2 * kk];
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + hh;
+#pragma unroll
+    for (int kk = 0; kk < DR / 16; ++kk) qrb[kk] = qr[2 * kk];
+  };
   // Page-table window: lane j of every wave holds the entry of split page
   // wbase + j (64 pages, 4096 tokens), so a stage finds its page with one
   // v_readlane instead of a memory round trip inside the loop.
@@ -323,25 +346,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const int j = first_page + base + lane;
     pwin = j < max_pages ? block_table[(size_t)b * max_pages + j] : -1;
   };
-  load_window(0);
-
-  // q~ and q^R as the B operand of QK: lane holds q[head l32][16 kk + 8 hh .. +8]
-  bf16x8 qb[R / 16];
-  bf16x8 qrb[DR / 16];
-  {
-    const bf16x8* qt = reinterpret_cast<const bf16x8*>(q_tilde + my_row * R) + hh;
-#pragma unroll
-    for (int kk = 0; kk < R / 16; ++kk) qb[kk] = qt[2 * kk];
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_rope + my_row * DR) + hh;
-#pragma unroll
-    for (int kk = 0; kk < DR / 16; ++kk) qrb[kk] = qr[2 * kk];
-  }
-  const float aq = USE_ALPHA ? alpha_q[my_row] : 1.f;
-  // query operands and page window in registers before any page load is
-  // issued (the page loads are not visible to the compiler's own waits)
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  // column operand of the alpha^k alpha^q product tile (see outer32)
-  const float aq_col = hh == 0 ? aq : 0.f;
 
   // ---- per-lane constants of the LDS traffic (stage offsets are added per
   // stage, or folded into the instructions' immediate offsets) ----
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   struct PagePlan {
     i32x4 rs, ra;  // KV rows of the page, alpha^k rows of the page
   };
-  auto plan_page = [&](int s) {  // s: the first stage of the page (even)
+  auto plan_page = [&](int s, auto FIRST) {  // s: the first stage of the page (even)
     const int rel = s >> 1;  // page of the split
     PagePlan pp;
     if (s >= n_st) {
@@ -402,14 +406,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
       pp.ra = buffer_rsrc(alpha_k, 0);
       return pp;
     }
-    if (rel < wbase || rel >= wbase + 64) {  // uniform; once per 64 pages
-      wbase = rel & ~63;
-      load_window(wbase);
-      // a wait the compiler sees, so that it adds none of its own at every
-      // later use of the window (which would also wait for the page loads)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    int pg;
+    if constexpr (decltype(FIRST)::value) {
+      pg = first_pg;  // the split's first page, from its own scalar load
+    } else {
+      if (rel < wbase || rel >= wbase + 64) {  // uniform; once per 64 pages
+        wbase = rel & ~63;
+        load_window(wbase);
+        // a wait the compiler sees, so that it adds none of its own at every
+        // later use of the window (which would also wait for the page loads)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      }
+      pg = __builtin_amdgcn_readlane(pwin, rel - wbase);
     }
-    int pg = __builtin_amdgcn_readlane(pwin, rel - wbase);
     pg = (pg >= 0 && pg < num_pages) ? pg : -1;
     const uint32_t ok = pg >= 0 ? 3u : 0u;  // validity of both stages of the page
     vmask = (vmask & ~(3u << (s & 3))) | (ok << (s & 3));
@@ -458,6 +467,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     }
   };
 
+  // column operand of the alpha^k alpha^q product tile (see outer32), formed
+  // where it is used (opaque keeps it there), so that no wait for alpha^q
+  // precedes the first page loads
+  auto aq_col = [&]() { return hh == 0 ? __uint_as_float(opaque(__float_as_uint(aq))) : 0.f; };
+
   f32x16 acc[R / 32];
   float m_ref = -INFINITY;   // reference of the exponent for this lane's head (logit units)
   float m_seen = -INFINITY;  // largest logit of this head seen so far
@@ -485,16 +499,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
 #pragma unroll
     for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
     l_run = 0.f;
-    PagePlan page = plan_page(0);
+    PagePlan page = plan_page(0, std::true_type{});
     {
       const StagePlan p0 = stage_plan(page, 0);
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) load(p0, k);
+    }
+    if (!restarted) {  // the first pass: the query side and the page window
+      load_query();
+      load_window(0);
+    }
+    // stage 0 has landed, and so has every vector load of the prologue; the
+    // loads of stage 1 go out now (fewer bytes ahead of the first stage, when
+    // every CU asks for its first pages at once), the loop waits for them
+    // at the end of its first iteration
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    {
       const StagePlan p1 = stage_plan(page, 1);
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) load(p1, k);
     }
-    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage 0 has landed
     __syncthreads();
     // probabilities of the previous stage / of this one, swapped every stage
     bf16x8 pA[2] = {}, pB[2];
@@ -545,7 +569,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
       const bool has_qk = s < n_st;
       // the loads of stage s + 2 go into the buffer of stage s - 2; an even
       // stage s + 2 starts a page and takes its plan, an odd one reuses it
-      if constexpr (decltype(HALF)::value == 0) page = plan_page(s + 2);
+      if constexpr (decltype(HALF)::value == 0) page = plan_page(s + 2, std::false_type{});
       const StagePlan pl = stage_plan(page, s + 2);
       const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
       const int tok0 = lo + s * ST;
@@ -616,7 +640,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
                 constexpr int kk = n - (NK - 2);
                 rope_a[kk] = lds_read16(lds0 + ((rp_l ^ (32u * kk)) + stage_off));
               }
-              if constexpr (n == NK - 2) fac = outer32(ak_row, aq_col);
+              if constexpr (n == NK - 2) fac = outer32(ak_row, aq_col());
             }
             __builtin_amdgcn_sched_barrier(0);
           });
