@@ -402,17 +402,97 @@ def decode_on_image(wl, q_img, kv, alpha_k, block_table, seq_lens, num_splits,
     return res
 
 
+def sparse_split_bounds(K: int, num_splits: int, stage: int = 32):
+    """List entries per split of a sparse decode: ceil(K / P) rounded up to whole
+    32-entry stages, as contiguous runs [lo, hi) of the K-entry list."""
+    per = -(-int(K) // int(num_splits))
+    L = stage * (-(-per // stage))
+    return [(min(p * L, K), min((p + 1) * L, K)) for p in range(num_splits)]
+
+
+def sparse_decode_on_image(wl, q_img, kv, alpha_k, block_table, seq_lens, indices,
+                           num_splits, rows=None):
+    """Selected-token decode over the stored state ([GQLA] section 2, "GQLA
+    Disperso": fine-grained sparse attention kept on the MQA-absorbed path).
+
+    Query token (b, i) attends only to the cache tokens listed in
+    indices[b, i, :] (logical positions, shared by every head and group; -1
+    marks an unused entry).  The logits are those of :func:`decode_on_image`
+    for the listed tokens; the softmax runs over the listed tokens only, taken
+    as listed (a position listed twice counts twice).  An entry that is not -1
+    and falls outside the visible tokens 0 .. T - s_q + i, or whose page entry
+    is out of range, is ignored and reported.  Split p covers the list entries
+    sparse_split_bounds(K, P)[p]; a split with no valid entry gives lse_p =
+    -inf and o_p = 0.  Returns (results per (b, i, h) as in decode_on_image,
+    whether any entry was reported)."""
+    dt = wl.cache_dtype
+    r, P, H, G, sq = wl.rank, wl.page_size, wl.heads, wl.groups, wl.s_q
+    indices = np.asarray(indices)
+    B, _, K = indices.shape
+    num_pages = kv.shape[0]
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(sq) for h in range(H)]
+    by_bi = {}
+    for (b, i, h) in rows:
+        by_bi.setdefault((b, i), []).append(h)
+    qt = words_to_f64(q_img["q_tilde"], dt)
+    qr = words_to_f64(q_img["qr_hat"], dt)
+    aq = np.asarray(q_img["alpha_q"], dtype=np.float64)
+    err = False
+    res = {}
+    for (b, i), hs in by_bi.items():
+        hs = np.asarray(hs)
+        T = int(seq_lens[b])
+        n_vis = visible_count(T, sq, i)
+        g_of = group_of(hs, H, G)
+        o_part = np.zeros((len(hs), num_splits, r))
+        lse_part = np.full((len(hs), num_splits), NEG_INF)
+        for p, (lo, hi) in enumerate(sparse_split_bounds(K, num_splits)):
+            t = indices[b, i, lo:hi].astype(np.int64)
+            used = t != -1
+            vis = used & (t >= 0) & (t < n_vis)
+            page = np.full(t.shape, -1, dtype=np.int64)
+            page[vis] = block_table[b, t[vis] // P]
+            ok = vis & (page >= 0) & (page < num_pages)
+            err = err or bool(np.any(used & ~ok))
+            if not np.any(ok):
+                continue
+            pg, sl = page[ok], t[ok] % P
+            C = words_to_f64(kv[pg, sl, :r], dt)
+            KR = words_to_f64(kv[pg, sl, r:], dt)
+            AK = np.asarray(alpha_k[pg, sl, :], dtype=np.float64)
+            for g in range(G):
+                sel = np.nonzero(g_of == g)[0]
+                if len(sel) == 0:
+                    continue
+                logits = absorbed_logits(wl, qt[b, i, hs[sel]], aq[b, i, hs[sel]],
+                                         qr[b, i, hs[sel]], C, AK, KR, g)
+                pr, lse = _softmax_stats(logits)
+                o_part[sel, p] = pr @ C
+                lse_part[sel, p] = lse
+        o_lat, lse = combine(o_part, lse_part)
+        for k, h in enumerate(hs):
+            res[(b, i, int(h))] = {"o_part": o_part[k], "lse_part": lse_part[k],
+                                   "o_lat": o_lat[k], "lse": lse[k]}
+    return res, err
+
+
 def combine(o_part, lse_part):
     """Merge split partials ([..., P, r], [..., P]) by log-sum-exp weights:
     M = max_p lse_p, lse = M + ln sum_p e^{lse_p - M}, o = sum_p e^{lse_p - lse} o_p.
-    Empty splits (lse_p = -inf) get weight 0."""
+    Empty splits (lse_p = -inf) get weight 0; when every split is empty (a
+    sparse decode whose list holds no valid entry) the result is the empty
+    sum: o = 0, lse = -inf."""
     lse_part = np.asarray(lse_part, dtype=np.float64)
     o_part = np.asarray(o_part, dtype=np.float64)
     M = np.max(lse_part, axis=-1, keepdims=True)
+    empty = np.isneginf(M)
+    M = np.where(empty, 0.0, M)
     w = np.exp(lse_part - M)
     s = np.sum(w, axis=-1, keepdims=True)
-    lse = (M + np.log(s))[..., 0]
-    o = np.sum((w / s)[..., None] * o_part, axis=-2)
+    s1 = np.where(empty, 1.0, s)
+    lse = np.where(empty, NEG_INF, M + np.log(s1))[..., 0]
+    o = np.sum((w / s1)[..., None] * o_part, axis=-2)
     return o, lse
 
 

@@ -506,6 +506,152 @@ def check_no_alpha_is_plain_mla():
     assert rel_err(got, ref) < 1e-5
 
 
+# ---------------------------------------------------------------------------
+# sparse (selected-token) decode
+# ---------------------------------------------------------------------------
+
+def _visible_lists(wl, inp, K):
+    """Per (b, i): every visible position in order, padded with -1 to K entries."""
+    idx = np.full((wl.batch, wl.s_q, K), -1, dtype=np.int32)
+    for b, T in enumerate(inp["seq_lens"]):
+        for i in range(wl.s_q):
+            n = O.visible_count(int(T), wl.s_q, i)
+            idx[b, i, :n] = np.arange(n)
+    return idx
+
+
+def check_sparse_split_bounds():
+    # runs of whole 32-entry stages that cover [0, K) in order
+    for K in (1, 31, 32, 33, 100, 2048, 2049):
+        for Pn in (1, 2, 3, 8, 64):
+            bounds = O.sparse_split_bounds(K, Pn)
+            assert bounds[0][0] == 0 and bounds[-1][1] == K and len(bounds) == Pn
+            for (a, b), (c, _) in zip(bounds, bounds[1:]):
+                assert b == c and a <= b
+            for (a, b) in bounds:
+                assert a % 32 == 0 or a == K
+            assert max(b - a for a, b in bounds) <= -(-K // Pn) + 31
+
+
+def check_sparse_all_visible_equals_dense(name):
+    """Listing every visible token gives the dense decode's merged result (the
+    split structure differs, the merged softmax does not)."""
+    wl = small(name)
+    inp = W.make_inputs(wl, seed=33)
+    img = O.full_cache_image(wl, inp)
+    qi = O.query_image(wl, inp)
+    K = int(np.max(inp["seq_lens"])) + 5
+    idx = _visible_lists(wl, inp, K)
+    dense = O.decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                              inp["seq_lens"], num_splits=2)
+    for Pn in (1, 3):
+        sp, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                           inp["seq_lens"], idx, Pn)
+        assert not err
+        for k, v in dense.items():
+            assert np.allclose(sp[k]["o_lat"], v["o_lat"], rtol=1e-12, atol=1e-13)
+            assert abs(sp[k]["lse"] - v["lse"]) < 1e-12
+
+
+def check_sparse_subset_against_explicit():
+    """A subset S of the visible tokens, against the explicit float64 path:
+    restricting its softmax to S gives o^lat = sum_S p_t c_t / sum_S p_t and
+    lse = lse_all + ln sum_S p_t.  With an fp32 cache the stored state differs
+    from the inputs only by float32 rounding (tolerance as for the dense
+    decode).  Also: order, -1 padding and split count leave the result as is;
+    a list with one valid entry gives that token's latent exactly."""
+    wl = small("mtp").replace(cache_dtype="f32")
+    inp = W.make_inputs(wl, seed=34)
+    img = O.full_cache_image(wl, inp)
+    qi = O.query_image(wl, inp)
+    rng = np.random.default_rng(35)
+    K = 96
+    idx = np.full((wl.batch, wl.s_q, K), -1, dtype=np.int32)
+    subsets = {}
+    for b, T in enumerate(inp["seq_lens"]):
+        for i in range(wl.s_q):
+            n = O.visible_count(int(T), wl.s_q, i)
+            m = min(n, int(rng.integers(1, 60)))
+            S = rng.choice(n, size=m, replace=False)
+            subsets[(b, i)] = np.sort(S)
+            slots = np.sort(rng.choice(K, size=m, replace=False))
+            idx[b, i, slots] = S
+    sp, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                       inp["seq_lens"], idx, 3)
+    assert not err
+    for (b, i), S in subsets.items():
+        e = O.explicit_rows(wl, inp, b, i)
+        C = np.asarray(inp["c"][inp["tok_offsets"][b] + S], dtype=np.float64)
+        w = e["p"][:, S]
+        want = (w @ C) / w.sum(axis=1, keepdims=True)
+        want_lse = e["lse"] + np.log(w.sum(axis=1))
+        got = np.stack([sp[(b, i, h)]["o_lat"] for h in range(wl.heads)])
+        lse = np.array([sp[(b, i, h)]["lse"] for h in range(wl.heads)])
+        assert rel_err(got, want) < 2e-5, rel_err(got, want)
+        assert np.max(np.abs(lse - want_lse)) < 2e-5
+    # order, padding and split count do not matter
+    perm = idx[..., ::-1].copy()
+    pad = np.concatenate([np.full(idx.shape[:2] + (40,), -1, np.int32), idx], axis=2)
+    for alt, Pn in ((perm, 3), (pad, 1), (idx, 5)):
+        sp2, _ = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                          inp["seq_lens"], alt, Pn)
+        for k, v in sp.items():
+            assert np.allclose(sp2[k]["o_lat"], v["o_lat"], rtol=1e-12, atol=1e-13)
+            assert abs(sp2[k]["lse"] - v["lse"]) < 1e-12
+    # one valid entry: o^lat is that latent as stored, lse its logit
+    one = np.full((wl.batch, wl.s_q, 40), -1, dtype=np.int32)
+    one[:, :, 17] = 2
+    sp1, _ = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                      inp["seq_lens"], one, 2)
+    for b in range(wl.batch):
+        e = O.explicit_rows(wl, inp, b, 0)
+        page = inp["block_table"][b, 0]
+        c2 = O.words_to_f64(img["kv"][page, 2, :wl.rank], "f32")
+        for h in range(wl.heads):
+            assert np.array_equal(sp1[(b, 0, h)]["o_lat"], c2)
+            assert abs(sp1[(b, 0, h)]["lse"] - (e["lse"][h] + np.log(e["p"][h, 2]))) < 2e-5
+
+
+def check_sparse_invalid_entries():
+    """Entries past the visible end, below -1, or on an out-of-range page entry
+    are reported and ignored; a list of -1 only is the empty sum (o = 0,
+    lse = -inf) and is not an error."""
+    wl = small("dsv3")
+    inp = W.make_inputs(wl, seed=36)
+    img = O.full_cache_image(wl, inp)
+    qi = O.query_image(wl, inp)
+    base = np.full((wl.batch, 1, 64), -1, dtype=np.int32)
+    base[:, 0, :5] = [0, 9, 33, 64, 101]
+    ref, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                        inp["seq_lens"], base, 2)
+    assert not err
+    bad = base.copy()
+    bad[:, 0, 20] = int(inp["seq_lens"][0]) + 3   # past the visible end
+    bad[:, 0, 40] = -7
+    got, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                        inp["seq_lens"], bad, 2)
+    assert err
+    for k, v in ref.items():
+        assert np.array_equal(got[k]["o_lat"], v["o_lat"]) and got[k]["lse"] == v["lse"]
+    bt = inp["block_table"].copy()
+    bt[:, 1] = img["kv"].shape[0] + 4               # page of positions 64 .. 127 out of range
+    got, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], bt,
+                                        inp["seq_lens"], base, 2)
+    assert err
+    drop = base.copy()
+    drop[:, 0, 3:5] = -1
+    want, _ = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                       inp["seq_lens"], drop, 2)
+    for k, v in want.items():
+        assert np.array_equal(got[k]["o_lat"], v["o_lat"])
+    empty = np.full((wl.batch, 1, 50), -1, dtype=np.int32)
+    got, err = O.sparse_decode_on_image(wl, qi, img["kv"], img["alpha_k"], inp["block_table"],
+                                        inp["seq_lens"], empty, 3)
+    assert not err
+    for v in got.values():
+        assert not np.any(v["o_lat"]) and np.isneginf(v["lse"])
+
+
 def check_intensity_golden(golden):
     """The per-token arithmetic intensity of the absorbed decode path at s_q = 1,
     128 heads, r = 512, d_R = 64 against the value the GQLA page states."""

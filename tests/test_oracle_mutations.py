@@ -129,6 +129,26 @@ def _explicit_unnormalised_key(wl, inp, b, i, heads=None):
         O.rmsnorm = saved
 
 
+def _sparse_padding_as_token0(wl, q_img, kv, alpha_k, block_table, seq_lens, indices,
+                              num_splits, rows=None):
+    # the -1 marker read as position 0 instead of an unused entry
+    idx = np.where(np.asarray(indices) == -1, 0, indices)
+    return _orig["sparse_decode_on_image"](wl, q_img, kv, alpha_k, block_table, seq_lens, idx,
+                                           num_splits, rows)
+
+
+def _sparse_positions_off_by_one(wl, q_img, kv, alpha_k, block_table, seq_lens, indices,
+                                 num_splits, rows=None):
+    idx = np.asarray(indices).copy()
+    idx[idx >= 0] += 1
+    return _orig["sparse_decode_on_image"](wl, q_img, kv, alpha_k, block_table, seq_lens, idx,
+                                           num_splits, rows)
+
+
+def _sparse_bounds_unstaged(K, num_splits, stage=32):
+    return _orig["sparse_split_bounds"](K, num_splits, 1)
+
+
 MUTATIONS = {
     "absorb drops gamma_k": ("absorb_query", _absorb_without_gamma_k,
                              [lambda: P.check_explicit_equals_absorbed("grouped")]),
@@ -161,6 +181,13 @@ MUTATIONS = {
                                      [lambda: P.check_explicit_equals_absorbed("dsv3")]),
     "cache slot index wrong": ("cache_image", _cache_image_wrong_slot,
                                [P.check_cache_image_layout]),
+    "sparse -1 marker read as position 0": ("sparse_decode_on_image", _sparse_padding_as_token0,
+                                            [P.check_sparse_subset_against_explicit,
+                                             P.check_sparse_invalid_entries]),
+    "sparse positions off by one": ("sparse_decode_on_image", _sparse_positions_off_by_one,
+                                    [P.check_sparse_subset_against_explicit]),
+    "sparse splits not whole stages": ("sparse_split_bounds", _sparse_bounds_unstaged,
+                                       [P.check_sparse_split_bounds]),
     "explicit path skips the key norm": ("explicit_rows", _explicit_unnormalised_key,
                                          [P.check_textbook_reduction,
                                           lambda: P.check_explicit_equals_absorbed("dsv3")]),

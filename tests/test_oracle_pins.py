@@ -106,3 +106,20 @@ def test_intensity_golden():
     with open(os.path.join(GOLDEN, "gqla_absorbed_intensity.json")) as f:
         golden = json.load(f)
     P.check_intensity_golden(golden)
+
+
+def test_sparse_split_bounds():
+    P.check_sparse_split_bounds()
+
+
+@pytest.mark.parametrize("name", ["mtp", "grouped"])
+def test_sparse_all_visible_equals_dense(name):
+    P.check_sparse_all_visible_equals_dense(name)
+
+
+def test_sparse_subset_against_explicit():
+    P.check_sparse_subset_against_explicit()
+
+
+def test_sparse_invalid_entries():
+    P.check_sparse_invalid_entries()
