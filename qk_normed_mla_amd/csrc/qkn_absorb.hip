@@ -215,7 +215,7 @@ struct QueryRows {
           const int j = lane + 64 * k;
           cs[k] = 1.f;
           sn[k] = 0.f;
-          if (j < half && theta != 0.f) rope_cos_sin(pos[u], j, rope_dim, theta, &cs[k], &sn[k]);
+          if (j < half && theta != 0.f) rope_cos_sin<false>(pos[u], j, rope_dim, theta, &cs[k], &sn[k]);
         }
         angle_tok = tok[u];
       }
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void absorb_rows(
   const int half = rope_dim / 2;
   for (int j = threadIdx.x; j < half; j += 256) {
     float c = 1.f, s = 0.f;
-    if (theta != 0.f) rope_cos_sin(q_pos[tok], j, rope_dim, theta, &c, &s);
+    if (theta != 0.f) rope_cos_sin<std::is_same<OutT, float>::value>(q_pos[tok], j, rope_dim, theta, &c, &s);
     cs[j] = c;
     sn[j] = s;
   }

@@ -156,10 +156,11 @@ int qkn_mla_decode_kernel_kind(const qkn_mla_dims* dims, int32_t num_splits, uin
   return qkn::mfma_decode_supported(*dims) ? 1 : 0;
 }
 
-int qkn_mla_absorb_query(const qkn_mla_dims* dims, const float* q, const float* q_rope,
-                         const int32_t* q_pos, const float* w_k, const float* gamma_q,
-                         const float* gamma_k, const float* gamma_qr, void* q_tilde,
-                         float* alpha_q, void* q_rope_normed, void* stream) {
+namespace {
+int check_absorb_args(const qkn_mla_dims* dims, const float* q, const float* q_rope,
+                      const int32_t* q_pos, const float* w_k, const float* gamma_q,
+                      const float* gamma_k, const float* gamma_qr, const void* q_tilde,
+                      const float* alpha_q, const void* q_rope_normed) {
   int st = check_dims(dims);
   if (st != QKN_OK) return st;
   const bool rope = dims->rope_dim > 0;
@@ -171,6 +172,35 @@ int qkn_mla_absorb_query(const qkn_mla_dims* dims, const float* q, const float* 
     if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
   if (rope && (!aligned16(q_rope) || !aligned16(gamma_qr) || !aligned16(q_rope_normed)))
     return QKN_ERR_ALIGNMENT;
+  return QKN_OK;
+}
+
+// n_tokens > 0 here
+int check_append_args(const qkn_mla_dims* dims, const float* c_new, const float* k_rope_new,
+                      const int32_t* seq_idx, const int32_t* pos, const int32_t* block_table,
+                      const float* w_k, const float* gamma_kr, const void* kv_cache,
+                      const float* alpha_k_cache) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  const bool rope = dims->rope_dim > 0;
+  if (!c_new || !seq_idx || !pos || !block_table || !w_k || !kv_cache || !alpha_k_cache)
+    return QKN_ERR_INVALID_ARG;
+  if (rope && (!k_rope_new || !gamma_kr)) return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {c_new, seq_idx, pos, block_table, w_k, kv_cache, alpha_k_cache};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  if (rope && (!aligned16(k_rope_new) || !aligned16(gamma_kr))) return QKN_ERR_ALIGNMENT;
+  return QKN_OK;
+}
+}  // namespace
+
+int qkn_mla_absorb_query(const qkn_mla_dims* dims, const float* q, const float* q_rope,
+                         const int32_t* q_pos, const float* w_k, const float* gamma_q,
+                         const float* gamma_k, const float* gamma_qr, void* q_tilde,
+                         float* alpha_q, void* q_rope_normed, void* stream) {
+  const int st = check_absorb_args(dims, q, q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr,
+                                   q_tilde, alpha_q, q_rope_normed);
+  if (st != QKN_OK) return st;
   return hip_status(qkn::launch_absorb_query(*dims, q, q_rope, q_pos, w_k, gamma_q, gamma_k,
                                              gamma_qr, q_tilde, alpha_q, q_rope_normed,
                                              static_cast<hipStream_t>(stream)));
@@ -184,14 +214,9 @@ int qkn_mla_append(const qkn_mla_dims* dims, int32_t n_tokens, const float* c_ne
   if (st != QKN_OK) return st;
   if (n_tokens < 0) return QKN_ERR_INVALID_ARG;
   if (n_tokens == 0) return QKN_OK;
-  const bool rope = dims->rope_dim > 0;
-  if (!c_new || !seq_idx || !pos || !block_table || !w_k || !kv_cache || !alpha_k_cache)
-    return QKN_ERR_INVALID_ARG;
-  if (rope && (!k_rope_new || !gamma_kr)) return QKN_ERR_INVALID_ARG;
-  const void* ptrs[] = {c_new, seq_idx, pos, block_table, w_k, kv_cache, alpha_k_cache};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
-  if (rope && (!aligned16(k_rope_new) || !aligned16(gamma_kr))) return QKN_ERR_ALIGNMENT;
+  st = check_append_args(dims, c_new, k_rope_new, seq_idx, pos, block_table, w_k, gamma_kr,
+                         kv_cache, alpha_k_cache);
+  if (st != QKN_OK) return st;
   return hip_status(qkn::launch_append(*dims, n_tokens, c_new, k_rope_new, seq_idx, pos,
                                        block_table, w_k, gamma_kr, kv_cache, alpha_k_cache,
                                        err_flag, static_cast<hipStream_t>(stream)));

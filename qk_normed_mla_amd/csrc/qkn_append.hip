@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
       for (int jj = lane; jj < half; jj += 64) {
         const float x1 = xn[jj], x2 = xn[jj + half];
         float c = 1.f, s = 0.f;
-        if (theta != 0.f) rope_cos_sin(xpos, jj, rope_dim, theta, &c, &s);
+        if (theta != 0.f) rope_cos_sin<std::is_same<CacheT, float>::value>(xpos, jj, rope_dim, theta, &c, &s);
         Elem<CacheT>::store(out, jj, x1 * c - x2 * s);
         Elem<CacheT>::store(out, jj + half, x2 * c + x1 * s);
       }
@@ -161,8 +161,6 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(
     alpha_k[(size_t)sr * groups + g] = 1.0f / sqrtf(tot / (float)head_dim + eps);
   }
 }
-
-constexpr int kBulkMinTokens = 4096;  // from here on alpha^k is one matrix product per group
 
 // The stores of the bulk path (bf16 cache): one wave per token for the slot,
 // the latent (16-byte stores of 8 bf16 words) and the RoPE key, with the
@@ -222,7 +220,7 @@ __global__ __launch_bounds__(256) void append_store_bulk(
   for (int jj = lane; jj < half; jj += 64) {
     const float x1 = xn[jj], x2 = xn[jj + half];
     float c = 1.f, s = 0.f;
-    if (theta != 0.f) rope_cos_sin(p, jj, rope_dim, theta, &c, &s);
+    if (theta != 0.f) rope_cos_sin<false>(p, jj, rope_dim, theta, &c, &s);
     out[jj] = f32_to_bf16(x1 * c - x2 * s);
     out[jj + half] = f32_to_bf16(x2 * c + x1 * s);
   }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qkn_mla.h"
 
 namespace qkn {
@@ -40,27 +42,44 @@ template <> struct Elem<uint16_t> {
 // ----------------------------------------------------------------------------
 // RoPE on the RMS-normed RoPE block (NeoX halves): the angle pos * omega_j,
 // omega_j = theta^(-2 j / d_R), is formed and reduced in double precision (at
-// positions of 2^18 a float angle would already be off by ~1e-2 rad), and
-// its cosine and sine are taken in double on the reduced angle.  omega_j is w^j with w = theta^(-2/d_R),
+// positions of 2^18 a float angle would already be off by ~1e-2 rad).  The
+// cosine and sine of the reduced angle |r| <= pi are taken in double when the
+// result is stored in float32 (PRECISE), else in float (sincosf on r rounded
+// to float: ~3e-7 absolute, far below the bf16 step of the stored key or
+// query, at a small fraction of the double routine's cost).  omega_j is w^j with w = theta^(-2/d_R),
 // raised by repeated squaring (at most 8 double products for j < 256; the
 // relative error stays ~1e-14), and the reduction subtracts k * 2 pi with 2 pi
 // in two double parts, which leaves the reduced angle good to ~1e-15 rad.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cos_sin(int pos, int j, int rope_dim, float theta,
-                                             float* c, float* s) {
+__device__ __forceinline__ double rope_omega(int j, int rope_dim, float theta) {
   const double w = exp2(-2.0 / (double)rope_dim * log2((double)theta));
   double omega = 1.0, b = w;
   for (int e = j; e != 0; e >>= 1) {
     if (e & 1) omega *= b;
     b *= b;
   }
+  return omega;
+}
+
+template <bool PRECISE>
+__device__ __forceinline__ void rope_cos_sin_at(int pos, double omega, float* c, float* s) {
   const double ang = (double)pos * omega;
   const double k = rint(ang * 0.15915494309189533577);          // ang / (2 pi)
   const double r = fma(-k, 2.44929359829470635445e-16, fma(-k, 6.28318530717958623200, ang));
-  double sd, cd;
-  sincos(r, &sd, &cd);  // |r| <= pi: the short path
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
+  if constexpr (PRECISE) {
+    double sd, cd;
+    sincos(r, &sd, &cd);  // |r| <= pi: the short path
+    *c = static_cast<float>(cd);
+    *s = static_cast<float>(sd);
+  } else {
+    sincosf(static_cast<float>(r), s, c);
+  }
+}
+
+template <bool PRECISE>
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, int rope_dim, float theta,
+                                             float* c, float* s) {
+  rope_cos_sin_at<PRECISE>(pos, rope_omega(j, rope_dim, theta), c, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -120,6 +139,9 @@ hipError_t launch_append(const qkn_mla_dims& d, int32_t n_tokens, const float* c
                          const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
                          const int32_t* block_table, const float* w_k, const float* gamma_kr,
                          void* kv_cache, float* alpha_k_cache, int32_t* err_flag, hipStream_t s);
+
+// From this many tokens in one call the append takes the bulk route.
+constexpr int kBulkMinTokens = 4096;
 
 // Element type of the split-KV partials for a cache of element type CacheT:
 // half for a bf16 cache (stored as uint16_t words), float32 for a float32 one.

@@ -44,6 +44,22 @@ def test_append_cache_image(name):
     _check_append_image(wl, inp)
 
 
+# per-step appends at other shapes: head dims 32, 64 and 256, ranks 128 to
+# 384, up to 80 tokens in one call and KV groups
+APPEND_SHAPES = [("dsv3", dict(head_dim=32, rank=128)), ("dsv3", dict(head_dim=64, rank=256)),
+                 ("grouped", dict(rank=384)), ("mtp", dict(batch=20)),
+                 ("grouped", dict(batch=40, seq_len=100)),
+                 ("dsv3", dict(head_dim=256, rank=256))]
+
+
+@pytest.mark.parametrize("name,kw", APPEND_SHAPES)
+def test_append_cache_image_shapes(name, kw):
+    wl = P.small(name, **kw)
+    inp = W.make_inputs(wl, seed=26, extra_pages=2)
+    announce(f"append {name} {kw} tokens={wl.batch * wl.s_q}")
+    _check_append_image(wl, inp)
+
+
 # thousands of tokens in one call: alpha^k as one matrix product per group
 BULK = [("dsv3", dict(batch=8, seq_len=600)), ("grouped", dict(batch=4, seq_len=1100)),
         ("mtp", dict(batch=12, seq_len=500, seq_len_range=(300, 500))),
@@ -71,6 +87,11 @@ def _check_append_image(wl, inp):
     r.fill_history()
     r.append_new()
     torch.cuda.synchronize()
+    _verify_append_image(wl, inp, r)
+
+
+def _verify_append_image(wl, inp, r):
+    """The runner's cache image against the oracle's (every token appended)."""
     assert int(r.err_flag.item()) == 0
     got = r.kv_words()
     ak = r.alpha_k.cpu().numpy()
@@ -162,6 +183,11 @@ def _check_absorb(wl, case):
     r = DecodeRunner(wl, inp)
     r.absorb()
     torch.cuda.synchronize()
+    _verify_absorb(wl, inp, r)
+
+
+def _verify_absorb(wl, inp, r):
+    """The runner's query side against the oracle's."""
     ref = O.query_image(wl, inp)
     aq = r.alpha_q.cpu().numpy()
     assert np.max(np.abs(aq / ref["alpha_q"] - 1)) < 1e-5
