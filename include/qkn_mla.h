@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 5
+#define QKN_MLA_ABI_VERSION 6
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -253,6 +253,41 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
  */
 QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream);
+
+/*
+ * qkn_mla_decode_sparse -- selected-token decode (the partials of a split-KV
+ * decode over listed cache tokens only).
+ *   Source: GQLA summary, section 2, "GQLA Disperso": fine-grained sparse
+ *   attention over the latent cache stays on the MQA-absorbed path, whose
+ *   decode-logit equation (QK-Normed MLA summary, "Metodologia") it keeps.
+ *
+ *   Query token (b, i) attends to the cache tokens listed in
+ *   indices[b][i][0 .. index_len) (logical positions within sequence b,
+ *   shared by every head and group; -1 marks an unused entry).  Logits, the
+ *   softmax over the listed tokens (taken as listed: a position listed twice
+ *   counts twice), o_p and lse_p are those of qkn_mla_decode, and the partials
+ *   have its layout, so qkn_mla_combine (or qkn_mla_combine_project) merges
+ *   them.  Split p covers list entries p L .. p L + L - 1, L = index_len / P
+ *   rounded up to a multiple of 32.  A split with no valid entry, or a list
+ *   with none, gives lse_p = -inf and o_p = 0 (combine then gives o = 0,
+ *   lse = -inf).
+ *   indices [B, s_q, index_len] int32 (16-byte aligned; may be null when
+ *   index_len == 0); the other arguments as for qkn_mla_decode.
+ *   err_flag (nullable): an entry that is not -1 and lies outside 0 .. T_b -
+ *   s_q + i, or whose page entry is out of range, is skipped and
+ *   QKN_FLAG_INDEX is ORed in (as is an out-of-range seq_lens[b]).
+ *   Returns QKN_ERR_UNSUPPORTED unless the matrix-core decode takes the dims
+ *   with heads a multiple of 128, the cache is under 4 GiB, and a split holds
+ *   at most 2048 list entries (raise num_splits for longer lists); and for
+ *   QKN_DECODE_FORCE_GENERIC.  QKN_DECODE_NO_ALPHA is accepted.
+ */
+QKN_API int qkn_mla_decode_sparse(const qkn_mla_dims* dims, const void* q_tilde,
+                          const float* alpha_q, const void* q_rope_normed,
+                          const void* kv_cache, const float* alpha_k_cache,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* indices, int32_t index_len, int32_t num_splits,
+                          uint32_t flags, void* o_partial, float* lse_partial,
+                          int32_t* err_flag, void* stream);
 
 /*
  * qkn_mla_decode_attend -- qkn_mla_decode followed by qkn_mla_combine, with

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 QKN_OK = 0
 QKN_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -96,6 +96,9 @@ def library() -> ctypes.CDLL:
         lib.qkn_mla_decode.restype = ctypes.c_int
         lib.qkn_mla_decode.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
                                        P, P, P, P]
+        lib.qkn_mla_decode_sparse.restype = ctypes.c_int
+        lib.qkn_mla_decode_sparse.argtypes = [D, P, P, P, P, P, P, P, P, _c_int32, _c_int32,
+                                              ctypes.c_uint32, P, P, P, P]
         lib.qkn_mla_decode_attend.restype = ctypes.c_int
         lib.qkn_mla_decode_attend.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
                                               P, ctypes.c_size_t, P, P, P, P]
@@ -117,7 +120,8 @@ EXPORTED_SYMBOLS = (
     "qkn_mla_abi_version", "qkn_status_string", "qkn_mla_check_dims",
     "qkn_mla_partial_dtype", "qkn_mla_decode_workspace_bytes",
     "qkn_mla_decode_kernel_kind", "qkn_mla_absorb_query", "qkn_mla_append",
-    "qkn_mla_decode", "qkn_mla_decode_attend", "qkn_mla_decode_attend_noalloc",
+    "qkn_mla_decode", "qkn_mla_decode_sparse", "qkn_mla_decode_attend",
+    "qkn_mla_decode_attend_noalloc",
     "qkn_mla_combine", "qkn_mla_combine_project",
 )
 
@@ -274,6 +278,35 @@ def qkn_mla_decode(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_
         _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
         ctypes.c_void_p(_stream_ptr(stream)))
     _check("qkn_mla_decode", st)
+
+
+def qkn_mla_decode_sparse(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,
+                          block_table, seq_lens, indices, num_splits: int, flags: int, o_partial,
+                          lse_partial, err_flag=None, stream=None):
+    """Selected-token decode: ``indices`` [B, s_q, K] int32 (logical positions,
+    -1 unused) on the device; partials as for :func:`qkn_mla_decode`."""
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    P = int(num_splits)
+    K = int(indices.shape[-1]) if indices is not None else 0
+    st = library().qkn_mla_decode_sparse(
+        ctypes.byref(d),
+        _ptr(q_tilde, "q_tilde", ct, rows * d.rank),
+        _ptr(alpha_q, "alpha_q", f32, rows),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(alpha_k_cache, "alpha_k_cache", f32, d.num_pages * PAGE_SIZE * d.groups),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", i32, d.batch),
+        _ptr(indices, "indices", i32, d.batch * d.s_q * K, allow_none=K == 0),
+        K, P, int(flags),
+        _ptr(o_partial, "o_partial", partial_torch_dtype(d), rows * P * d.rank),
+        _ptr(lse_partial, "lse_partial", f32, rows * P),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_decode_sparse", st)
 
 
 def qkn_mla_decode_attend(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,

@@ -238,6 +238,28 @@ int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const float* a
   return hip_status(launch_decode(kind, *dims, a, static_cast<hipStream_t>(stream)));
 }
 
+int qkn_mla_decode_sparse(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
+                          const void* q_rope_normed, const void* kv_cache,
+                          const float* alpha_k_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* indices, int32_t index_len,
+                          int32_t num_splits, uint32_t flags, void* o_partial,
+                          float* lse_partial, int32_t* err_flag, void* stream) {
+  if (flags & QKN_DECODE_FORCE_GENERIC) return QKN_ERR_UNSUPPORTED;
+  const int kind = check_decode_args(dims, q_tilde, alpha_q, q_rope_normed, kv_cache,
+                                     alpha_k_cache, block_table, seq_lens, num_splits, flags);
+  if (kind < 0) return kind;
+  if (index_len < 0) return QKN_ERR_INVALID_ARG;
+  if (!o_partial || !lse_partial || (index_len > 0 && !indices)) return QKN_ERR_INVALID_ARG;
+  if (!aligned16(o_partial) || !aligned16(lse_partial)) return QKN_ERR_ALIGNMENT;
+  if (index_len > 0 && !aligned16(indices)) return QKN_ERR_ALIGNMENT;
+  const int chk = qkn::sparse_decode_check(*dims, index_len, num_splits);
+  if (chk != 0) return chk == -1 ? QKN_ERR_INVALID_ARG : QKN_ERR_UNSUPPORTED;
+  qkn::DecodeArgs a{q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache, block_table,
+                    seq_lens, o_partial, lse_partial, err_flag, num_splits,
+                    (flags & QKN_DECODE_NO_ALPHA) == 0, indices, index_len};
+  return hip_status(qkn::launch_decode_sparse(*dims, a, static_cast<hipStream_t>(stream)));
+}
+
 int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
                           const void* q_rope_normed, const void* kv_cache,
                           const float* alpha_k_cache, const int32_t* block_table,

@@ -92,6 +92,10 @@ constexpr int ALPHA_BYTES = ST * kMaxGroups * 4;  // 1024
 constexpr int STAGE_BYTES = CONTENT_BYTES + ROPE_BYTES + ALPHA_BYTES;  // 37888
 constexpr int FLAG_OFFSET = NSTAGE * STAGE_BYTES; // the workgroup's restart flag
 constexpr int LDS_BYTES = FLAG_OFFSET + 16;       // 151568
+// selected-token decode: the cache rows of a split's list entries, as a table
+// in LDS after the flag (at most this many entries per split)
+constexpr int kSelMaxPerSplit = 2048;
+constexpr int SEL_TABLE_BYTES = 4 * kSelMaxPerSplit;
 constexpr int WAVES = 4;
 constexpr int HEADS_PER_WAVE = 32;
 constexpr int ROWS_PER_WG = WAVES * HEADS_PER_WAVE;  // 128
@@ -225,18 +229,25 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool USE_ALPHA>
+// SPARSE: the selected-token variant.  Query token (b, i) attends to the cache
+// tokens listed in sel[b][i][0 .. sel_len) (logical positions, -1 = unused
+// entry); split p takes list entries p L .. p L + L - 1, L = sel_len / P
+// rounded up to whole 32-entry stages.  A workgroup's rows are then one query
+// token (heads a multiple of 128, checked by the host), so its waves share the
+// list.  Stage rows are gathered by cache row instead of by page.
+template <bool USE_ALPHA, bool SPARSE>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     const uint16_t* __restrict__ q_tilde, const float* __restrict__ alpha_q,
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv,
     const float* __restrict__ alpha_k, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, _Float16* __restrict__ o_part,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel, int sel_len,
+    _Float16* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ err_flag, int batch, int s_q, int heads,
     int groups, int max_pages, int num_pages, int num_splits, int row_blocks, int n_work,
     int per_xcd, float scale) {
   // a static allocation: its LDS address (0) is known when the kernel is
   // compiled, so stage offsets fold into the read instructions
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES + (SPARSE ? SEL_TABLE_BYTES : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   {
     bool ragged = false;
     int rank = 0;  // place of sequence `lane` in the order (longest first, ties by index)
-    if (batch <= 64) {
+    if (!SPARSE && batch <= 64) {
       tl = lane < batch ? seq_lens[lane] : 0;
       const int t0 = __builtin_amdgcn_readfirstlane(tl);
       ragged = __ballot(lane < batch && tl != t0) != 0;
@@ -293,14 +304,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   int err = 0;
   bool restarted = false;
 
-  int T = batch <= 64 ? __builtin_amdgcn_readlane(tl, b) : seq_lens[b];
+  int T = (!SPARSE && batch <= 64) ? __builtin_amdgcn_readlane(tl, b) : seq_lens[b];
   if (T < 0 || T > max_pages * PAGE) {
     err = 1;
     T = min(max(T, 0), max_pages * PAGE);
   }
-  const int L = split_len(max(T, 1), num_splits);
+  // split p: tokens lo .. hi - 1 of the sequence (list entries lo .. hi - 1 when SPARSE)
+  const int L = SPARSE ? ST * cdiv(cdiv(max(sel_len, 1), num_splits), ST)
+                       : split_len(max(T, 1), num_splits);
   const int lo = p * L;
-  const int hi = min(lo + L, T);
+  const int hi = min(lo + L, SPARSE ? sel_len : T);
   const int first_page = lo / PAGE;  // lo is a multiple of the page size
   const int n_st = hi > lo ? (hi - lo + ST - 1) / ST : 0;
 
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   // for everything then precedes the first stage.  (The page loads are not
   // visible to the compiler's own waits, so every vector load the compiler
   // issued must be complete before the loop.)
-  const int first_pg = (first_page < max_pages && n_st > 0)
+  const int first_pg = (!SPARSE && first_page < max_pages && n_st > 0)
                            ? block_table[(size_t)b * max_pages + first_page] : -1;
   float aq;
   // q~ and q^R as the B operand of QK: lane holds q[head l32][16 kk + 8 hh .. +8]
@@ -432,10 +445,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     return pp;
   };
   struct StagePlan {
-    i32x4 rs, ra;    // the page's descriptors
+    i32x4 rs, ra;    // the page's descriptors (SPARSE: the whole cache's)
     uint32_t buf;    // LDS address of the stage buffer
     uint32_t half;   // which half of the page (0, 1)
     uint32_t l16;    // 16 * lane, taken as new for this stage (see opaque)
+    // SPARSE: lane l holds the byte offset of the stage's entry l % 32 in the
+    // cache (a zero-reading offset for an unused or invalid entry) and its
+    // cache row (-1 for none); vm has bit l set for a valid entry l
+    uint32_t off;
+    int row;
+    uint32_t vm;
   };
   auto stage_plan = [&](const PagePlan& pp, int s) {
     StagePlan pl;
@@ -447,7 +466,53 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     pl.l16 = opaque(lane16);
     return pl;
   };
+  // SPARSE: descriptors over the whole cache (its size fits 32-bit offsets,
+  // checked by the host) and the entries' cache rows in LDS
+  const uint32_t kv_bytes = static_cast<uint32_t>(num_pages) * PAGE * ROW_BYTES;
+  const uint32_t ak_bytes = static_cast<uint32_t>(num_pages) * PAGE * groups * 4;
+  const LDS_AS int* sel_rows = (const LDS_AS int*)((LDS_AS uint8_t*)smem + LDS_BYTES);
+  auto gather_plan = [&](int s) {
+    StagePlan pl;
+    pl.rs = buffer_rsrc(kv, kv_bytes);
+    pl.ra = buffer_rsrc(alpha_k, USE_ALPHA ? ak_bytes : 0);
+    pl.buf = lds_base + (s & (NSTAGE - 1)) * STAGE_BYTES;
+    asm volatile("" : "+s"(pl.buf));
+    pl.half = 0;
+    pl.l16 = opaque(lane16);
+    pl.row = s < n_st ? sel_rows[s * ST + (lane & 31)] : -1;
+    pl.off = pl.row >= 0 ? static_cast<uint32_t>(pl.row) * ROW_BYTES : kv_bytes;
+    pl.vm = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(pl.row >= 0));
+    return pl;
+  };
   auto load = [&](const StagePlan& pl, int k) {
+    if constexpr (SPARSE) {
+      if (k < ST / WAVES) {
+        // content token t = w + 4k from its own cache row
+        const int t = w + WAVES * k;
+        const uint32_t voff = (pl.l16 ^ static_cast<uint32_t>(swz(t) << 4)) +
+                              static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pl.off), t));
+        if (k == 0) {
+          dma16<true>(pl.buf + t * 1024, voff, pl.rs);
+        } else {
+          dma16<false>(pl.buf + t * 1024, voff, pl.rs);
+        }
+      } else if (k == ST / WAVES) {
+        // RoPE key of token 8w + lane / 8 from its row
+        const int tr = 8 * w + (lane >> 3);
+        const uint32_t row_off = static_cast<uint32_t>(__shfl(static_cast<int>(pl.off), tr));
+        const uint32_t voff = row_off == kv_bytes ? kv_bytes
+                              : row_off + static_cast<uint32_t>(R * 2 + (((lane & 7) ^ swz_rope(tr)) << 4));
+        dma16<false>(pl.buf + CONTENT_BYTES + w * 1024, voff, pl.rs);
+      } else {
+        // alpha^k slot i = 8Gw + lane: token i % 32, group i / 32
+        const int si = 8 * groups * w + lane;
+        const int row = __shfl(pl.row, si & 31);
+        const uint32_t voff = row >= 0 ? static_cast<uint32_t>((row * groups + (si >> 5)) * 4) : ak_bytes;
+        if (dma_a_lane)
+          dma4_first(pl.buf + CONTENT_BYTES + ROPE_BYTES + 32 * groups * w, voff, pl.ra);
+      }
+      return;
+    }
     if (k < ST / WAVES) {
       // content token t = w + 4k at t * ROW_BYTES; the lane's chunk is lane ^ f(t)
       const int t = w + WAVES * k;
@@ -493,19 +558,60 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
       *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)smem + 3 * STAGE_BYTES + 16 * e) = z;
   }
 
+  if constexpr (SPARSE) {
+    // The cache row of every list entry of the split (-1: unused or invalid),
+    // into LDS: the list entries first, then the query loads (their latency
+    // overlaps the page-table lookups), then the lookups.  An entry that is
+    // not -1 and lies outside the visible tokens 0 .. T - s_q + i, or whose
+    // page entry is out of range, is reported.
+    constexpr int PER = kSelMaxPerSplit / (64 * WAVES);
+    const int n_e = hi > lo ? hi - lo : 0;
+    const int vis = T - s_q + i + 1;
+    const int32_t* srow = sel + ((size_t)b * s_q + i) * sel_len + lo;
+    int tv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 64 * WAVES * u;
+      tv[u] = e < n_e ? srow[e] : -1;
+    }
+    load_query();
+    LDS_AS int* rows_w = (LDS_AS int*)((LDS_AS uint8_t*)smem + LDS_BYTES);
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 64 * WAVES * u;
+      if (e < n_st * ST) {
+        const int t = tv[u];
+        int row = -1;
+        if (t != -1) {
+          const int pg = (t >= 0 && t < vis) ? block_table[(size_t)b * max_pages + t / PAGE] : -1;
+          if (pg >= 0 && pg < num_pages) row = pg * PAGE + t % PAGE;
+          else bad = true;
+        }
+        rows_w[e] = row;
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(bad)) err = 1;
+    __syncthreads();
+  }
+  // masks of valid entries of stages s and s + 1 at iteration s (SPARSE)
+  uint32_t vm_cur = 0, vm_next = 0;
+
   bool again;
   do {
     again = false;
 #pragma unroll
     for (int om = 0; om < R / 32; ++om) acc[om] = f32x16{};
     l_run = 0.f;
-    PagePlan page = plan_page(0, std::true_type{});
+    PagePlan page;
+    if constexpr (!SPARSE) page = plan_page(0, std::true_type{});
     {
-      const StagePlan p0 = stage_plan(page, 0);
+      const StagePlan p0 = SPARSE ? gather_plan(0) : stage_plan(page, 0);
+      vm_cur = p0.vm;
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) load(p0, k);
     }
-    if (!restarted) {  // the first pass: the query side and the page window
+    if (!SPARSE && !restarted) {  // the first pass: the query side and the page window
       load_query();
       load_window(0);
     }
@@ -515,7 +621,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
     // at the end of its first iteration
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     {
-      const StagePlan p1 = stage_plan(page, 1);
+      const StagePlan p1 = SPARSE ? gather_plan(1) : stage_plan(page, 1);
+      vm_next = p1.vm;
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) load(p1, k);
     }
@@ -569,15 +676,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
       const bool has_qk = s < n_st;
       // the loads of stage s + 2 go into the buffer of stage s - 2; an even
       // stage s + 2 starts a page and takes its plan, an odd one reuses it
-      if constexpr (decltype(HALF)::value == 0) page = plan_page(s + 2, std::false_type{});
-      const StagePlan pl = stage_plan(page, s + 2);
+      if constexpr (!SPARSE && decltype(HALF)::value == 0) page = plan_page(s + 2, std::false_type{});
+      const StagePlan pl = SPARSE ? gather_plan(s + 2) : stage_plan(page, s + 2);
       const uint32_t stage_off = (s & (NSTAGE - 1)) * STAGE_BYTES;
       const int tok0 = lo + s * ST;
-      const bool page_ok = (vmask >> (s & 3)) & 1u;
-      if (has_qk && !page_ok) err = 1;
+      const bool page_ok = SPARSE || ((vmask >> (s & 3)) & 1u);
+      if (!SPARSE && has_qk && !page_ok) err = 1;
       // rows r of this stage with r < lim are visible to this wave; past the
-      // last stage none (the softmax steps then only produce zeros)
-      const int lim = (has_qk && page_ok) ? hi_w - tok0 : 0;
+      // last stage none (the softmax steps then only produce zeros).  SPARSE:
+      // the valid entries of the stage instead (none past the last stage).
+      const int lim = SPARSE ? (has_qk ? ST : 0) : (has_qk && page_ok) ? hi_w - tok0 : 0;
+      const uint32_t vm_s = has_qk ? vm_cur : 0u;
+      vm_cur = vm_next;
+      vm_next = pl.vm;
       int overflow = 0;
 
       if (!wave_active) {
@@ -671,6 +782,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
             sc = mfma(rope_a[2], qrb[2], sc);
             sc = mfma(rope_a[3], qrb[3], sc);
           } else if constexpr (n == M) {
+            if constexpr (SPARSE) {
+              if (vm_s != 0xffffffffu) {
+                // register r holds token (r % 4) + 8 (r / 4) + 4 hh
+                const uint32_t vl = vm_s >> (4 * hh);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  if (!((vl >> ((r & 3) + 8 * (r >> 2))) & 1u)) sc[r] = -INFINITY;
+              }
+            }
             if (__builtin_expect(lim < ST, 0)) {
               // register r holds token (r % 4) + 8 (r / 4) + 4 hh: compare the
               // constant part against lim - 4 hh (no per-register lane values)
@@ -774,19 +894,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(
   if (restarted && err_flag && tid == 0) atomicOr(err_flag, QKN_FLAG_RESTART);
 }
 
-template <bool USE_ALPHA>
+template <bool USE_ALPHA, bool SPARSE>
 hipError_t launch_typed(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
   const int row_blocks = cdiv(d.s_q * d.heads, ROWS_PER_WG);
   const int n_work = d.batch * a.num_splits * row_blocks;
   const int per_xcd = cdiv(n_work, 8);
   // enough blocks for either dealing of the work items (the kernel takes the
   // longest-first one for a ragged batch of up to 64 sequences)
-  const int per_xcd_ragged = d.batch <= 64 ? cdiv(d.batch * a.num_splits, 8) * row_blocks : 0;
+  const int per_xcd_ragged =
+      (!SPARSE && d.batch <= 64) ? cdiv(d.batch * a.num_splits, 8) * row_blocks : 0;
   dim3 grid(8 * std::max(per_xcd, per_xcd_ragged));
-  hipLaunchKernelGGL(decode_mfma_kernel<USE_ALPHA>, grid, dim3(64 * WAVES), 0, s,
+  hipLaunchKernelGGL((decode_mfma_kernel<USE_ALPHA, SPARSE>), grid, dim3(64 * WAVES), 0, s,
                      static_cast<const uint16_t*>(a.q_tilde), a.alpha_q,
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint16_t*>(a.kv),
-                     a.alpha_k, a.block_table, a.seq_lens, static_cast<_Float16*>(a.o_part),
+                     a.alpha_k, a.block_table, a.seq_lens, a.sel, a.sel_len,
+                     static_cast<_Float16*>(a.o_part),
                      a.lse_part, a.err_flag, d.batch, d.s_q,
                      d.heads, d.groups, d.max_pages_per_seq, d.num_pages, a.num_splits, row_blocks,
                      n_work, per_xcd, d.softmax_scale);
@@ -801,7 +923,19 @@ bool mfma_decode_supported(const qkn_mla_dims& d) {
 }
 
 hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
-  return a.use_alpha ? launch_typed<true>(d, a, s) : launch_typed<false>(d, a, s);
+  return a.use_alpha ? launch_typed<true, false>(d, a, s) : launch_typed<false, false>(d, a, s);
+}
+
+int sparse_decode_check(const qkn_mla_dims& d, int sel_len, int num_splits) {
+  if (!mfma_decode_supported(d) || d.heads % ROWS_PER_WG != 0) return -2;
+  if ((uint64_t)d.num_pages * PAGE * ROW_BYTES + ROW_BYTES >= (1ull << 32)) return -2;
+  if (sel_len < 0) return -1;
+  const int L = ST * cdiv(cdiv(std::max(sel_len, 1), num_splits), ST);
+  return L <= kSelMaxPerSplit ? 0 : -2;
+}
+
+hipError_t launch_decode_sparse(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s) {
+  return a.use_alpha ? launch_typed<true, true>(d, a, s) : launch_typed<false, true>(d, a, s);
 }
 
 }  // namespace qkn

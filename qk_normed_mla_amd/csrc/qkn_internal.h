@@ -169,11 +169,19 @@ struct DecodeArgs {
   int32_t* err_flag;
   int num_splits;
   bool use_alpha;
+  const int32_t* sel = nullptr;  // selected-token decode: [B, s_q, sel_len] positions
+  int sel_len = 0;
 };
 
 hipError_t launch_decode_generic(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
 bool mfma_decode_supported(const qkn_mla_dims& d);
 hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
+// Selected-token decode on the matrix cores: 0 when it takes these dims, list
+// length and split count, -1 for a bad argument, -2 for unsupported dims
+// (heads not a multiple of 128, a cache of 4 GiB or more, or more than 2048
+// list entries per split).
+int sparse_decode_check(const qkn_mla_dims& d, int sel_len, int num_splits);
+hipError_t launch_decode_sparse(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);

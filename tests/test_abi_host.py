@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 14, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 5
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 6
     for st in (0, -1, -2, -3, -4, -5):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -233,3 +233,30 @@ def test_noalloc_rejects_requests_beyond_its_scratch():
     assert call(d, 8, o_lat=P((1 << 20) + 4)) == -3
     assert call(good_dims(groups=3), 8) == -1
     assert "static scratch" in Q.status_string(Q.QKN_ERR_SCRATCH)
+
+
+def _call_sparse(d, ptr, idx_ptr, K, num_splits=1, flags=0):
+    P = ctypes.c_void_p
+    return Q.library().qkn_mla_decode_sparse(ctypes.byref(d), P(ptr), P(ptr), P(ptr), P(ptr),
+                                             P(ptr), P(ptr), P(ptr), idx_ptr, K, num_splits,
+                                             flags, P(ptr), P(ptr), None, None)
+
+
+def test_sparse_decode_rejections():
+    """The selected-token decode checks its arguments before any launch: the
+    dense decode's checks, the list pointer and length, and the dims it takes
+    (heads a multiple of 128, a cache under 4 GiB, at most 2048 entries per
+    split, no forced vector-ALU kernel)."""
+    P = ctypes.c_void_p
+    d = good_dims()
+    assert _call_sparse(d, 0x1000, None, 16) == -1                   # no list, entries > 0
+    assert _call_sparse(d, 0x1000, P(0x1000), -1) == -1              # negative length
+    assert _call_sparse(d, 0x1000, P(0x1004), 16) == -3              # misaligned list
+    assert _call_sparse(d, 0x1008, P(0x1000), 16) == -3              # misaligned operands
+    assert _call_sparse(d, 0x1000, P(0x1000), 16, num_splits=0) == -1
+    assert _call_sparse(d, 0x1000, P(0x1000), 4096, num_splits=1) == -2   # 4096 entries in a split
+    assert _call_sparse(d, 0x1000, P(0x1000), 16, flags=Q.QKN_DECODE_FORCE_GENERIC) == -2
+    assert _call_sparse(good_dims(heads=64), 0x1000, P(0x1000), 16) == -2  # two tokens per workgroup
+    assert _call_sparse(good_dims(cache_dtype="f32"), 0x1000, P(0x1000), 16) == -2
+    big = good_dims(num_pages=60000)                                 # 4.4 GB of cache rows
+    assert _call_sparse(big, 0x1000, P(0x1000), 16) == -2

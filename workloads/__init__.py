@@ -89,7 +89,14 @@ WORKLOADS = {
                     rope_dim=64, seq_len=16384, seq_len_range=(1024, 16384),
                     cache_dtype="bf16", latent_log_sigma=0.5, num_splits=4,
                     shuffled_pages=True),
+    # selected-token decode: 2048 listed tokens per query out of 16384
+    "sparse": Workload("sparse", batch=32, s_q=1, heads=128, groups=1, rank=512, head_dim=128,
+                       rope_dim=64, seq_len=16384, cache_dtype="bf16", latent_log_sigma=0.5,
+                       num_splits=2, shuffled_pages=True),
 }
+
+# entries per query list of the selected-token workload
+SPARSE_LIST_LEN = 2048
 
 # Order in which the workloads are listed by the project (index 0 is the tiny
 # correctness case).
@@ -168,6 +175,29 @@ def make_inputs(wl: Workload, seed: int = 0, *, extra_pages: int = 0) -> dict:
             k += 1
     out["block_table"] = bt
     out["num_pages"] = num_pages
+    return out
+
+
+def make_selection(wl: Workload, seq_lens, list_len: int, seed: int, fill: float = 1.0,
+                   shuffle: bool = True) -> np.ndarray:
+    """Token lists for a selected-token decode: int32 [B, s_q, list_len].  For
+    query token i of sequence b, min(visible, round(fill * list_len)) distinct
+    positions drawn uniformly from its visible tokens 0 .. T_b - s_q + i, in
+    random entries of the list (shuffle) or in order at its start; every
+    other entry is -1."""
+    rng = np.random.default_rng(seed)
+    B, sq = len(seq_lens), wl.s_q
+    out = np.full((B, sq, list_len), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(sq):
+            vis = int(seq_lens[b]) - sq + i + 1
+            m = min(vis, int(round(fill * list_len)))
+            pos = np.sort(rng.choice(vis, size=m, replace=False)).astype(np.int32)
+            if shuffle:
+                slots = np.sort(rng.choice(list_len, size=m, replace=False))
+                out[b, i, slots] = rng.permutation(pos)
+            else:
+                out[b, i, :m] = pos
     return out
 
 
