@@ -17,7 +17,9 @@ time of exactly K timed steps.  ``roofline`` rates its decode kernel alone (HIP
 events on its stream) against the peak of its bound: bf16 matrix-core FLOP/s
 when the workload's arithmetic intensity is past the ridge, else 8 TB/s of HBM.
 ``workloads`` carries the same figures for the other bf16 workloads (dsv3,
-grouped, long); ``qknorm_sweep`` the cost of the inverse-RMS factors over a
+grouped, long); ``sparse`` the selected-token decode (2048 listed tokens per
+query out of 16384, its listed rows as the algorithmic bytes);
+``qknorm_sweep`` the cost of the inverse-RMS factors over a
 batch-1 context sweep from 4k to 256k tokens; ``cpu_baseline`` the float64 CPU
 oracle timed on a bounded sample on the host's cores (and on one core).
 
@@ -400,6 +402,61 @@ def measure(Q, W, torch, timer, wl, inp, splits, *, steps, warmup, overhead=True
     return res
 
 
+def measure_sparse(Q, W, torch, timer, splits=8):
+    """Selected-token decode: 32 sequences of 16384 tokens (shuffled pages),
+    each query listing 2048 of its tokens at random; the decode kernel alone
+    and decode + combine, over rotating cache replicas.  Algorithmic bytes:
+    the listed rows (latent, RoPE key and alpha^k of each)."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS["sparse"].replace(num_splits=splits)
+    log("sparse: generating inputs")
+    inp = W.make_inputs(wl, seed=0)
+    K = W.SPARSE_LIST_LEN
+    sel = W.make_selection(wl, inp["seq_lens"], K, seed=1)
+    n_listed = int(np.sum(sel >= 0))
+    row_bytes = (wl.rank + wl.rope_dim) * 2 + 4 * wl.groups
+    nbytes = n_listed * row_bytes
+    flops = n_listed * wl.heads * (4 * wl.rank + 2 * wl.rope_dim)
+    r = DecodeRunner(wl, inp, num_splits=splits)
+    r.fill_history()
+    r.prepare()
+    idx = torch.from_numpy(sel).to("cuda")
+    torch.cuda.synchronize()
+    cache_bytes = r.kv.numel() * r.kv.element_size() + r.alpha_k.numel() * 4
+    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / cache_bytes) + 1)
+    kvs = [r.kv] + [r.kv.clone() for _ in range(n_rep - 1)]
+    aks = [r.alpha_k] + [r.alpha_k.clone() for _ in range(n_rep - 1)]
+
+    def dec(k):
+        Q.qkn_mla_decode_sparse(r.dims, r.q_tilde, r.alpha_q, r.q_rope_normed, kvs[k % n_rep],
+                                aks[k % n_rep], r.block_table, r.seq_lens, idx, splits, 0,
+                                r.o_partial, r.lse_partial, r.err_flag)
+
+    def attn(k):
+        dec(k)
+        r.combine()
+
+    r.err_flag.zero_()
+    attn(0)
+    torch.cuda.synchronize()
+    if int(r.err_flag.item()) != 0:
+        raise RuntimeError("the sparse decode flagged its inputs")
+    n_dec = max(40, 4 * n_rep)
+    graphs = [timer.capture(f, n_dec) for f in (dec, attn)]
+    timer.warm(graphs[0])
+    dec_ms, attn_ms = [t / n_dec for t in timer.timed(graphs, reps=15)]
+    log(f"sparse: B={wl.batch} T={wl.seq_len} K={K} splits={splits} listed bytes "
+        f"{nbytes / 1e6:.1f} MB: decode kernel {dec_ms * 1e3:.1f} us, decode+combine "
+        f"{attn_ms * 1e3:.1f} us")
+    return {"workload": "sparse", "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
+            "list_len": K, "num_splits": splits, "listed_bytes": nbytes, "flops": flops,
+            "decode_kernel_us": round(dec_ms * 1e3, 2),
+            "decode_combine_us": round(attn_ms * 1e3, 2),
+            "decode_gbs": round(nbytes / (dec_ms * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def qknorm_sweep(Q, W, torch, timer, lengths=(4096, 8192, 16384, 32768, 65536, 131072, 262144)):
     """Batch-1 decode + combine (128 heads, r = 512, d_R = 64, latent scales
     log-normal sigma 0.5) with and without the inverse-RMS factors over a
@@ -564,6 +621,9 @@ def main():
         for name in ("dsv3", "grouped", "long", "mtp"):
             if name != args.workload:
                 others.append(run(name, False)[2]["summary"])
+    sparse = None
+    if not args.only:
+        sparse = measure_sparse(Q, W, torch, timer)
     sweep = None
     if not args.only and not args.no_sweep:
         log("batch-1 QK-norm overhead sweep")
@@ -602,6 +662,7 @@ def main():
                   | {"cache": wl.cache_dtype},
         "roofline": roof,
         "workloads": [hs] + others,
+        "sparse": sparse,
         "qknorm_sweep": sweep,
         "cpu_baseline": cpu,
     }
