@@ -390,6 +390,9 @@ def measure(Q, W, torch, timer, wl, inp, splits, *, steps, warmup, overhead=True
         "decode_combine_hbm_frac": round(nbytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "qknorm_overhead_pct": None if (ov is None or restarted["no_alpha"]) else ov,
         "restarted": restarted,
+        # HBM bytes per decode launch from the committed counter runs (null
+        # when they were taken on another kernel source)
+        "decode_hbm_traffic": load_traffic(wl.name),
     }
     if ov is not None and restarted["no_alpha"]:
         out["qknorm_overhead_note"] = ("not comparable: without the inverse-RMS factors the "
