@@ -477,6 +477,85 @@ def sparse_decode_on_image(wl, q_img, kv, alpha_k, block_table, seq_lens, indice
     return res, err
 
 
+# ----------------------------------------------------------------------------
+# chunked prefill on the explicit path ([QKN] Planteamiento del Problema: keys
+# k = c W^K_g are materialised and RMS-normed after the projection; Metodologia
+# item 4: the RoPE block is normed on its own).  A chunk of s_q new query
+# tokens per sequence attends causally to the whole cache, the chunk included.
+# ----------------------------------------------------------------------------
+
+def prefill_query_image(wl, inp) -> dict:
+    """The explicit path's query side as stored: q^ = gamma_q * q / RMS(q) per
+    head, and the normed, rotated RoPE query (as in :func:`query_image`), both
+    in the cache dtype."""
+    B, sq = wl.batch, wl.s_q
+    pos = np.asarray(inp["seq_lens"], dtype=np.int64)[:, None] - sq + np.arange(sq)[None, :]
+    q_hat = rmsnorm(inp["q"], inp["gamma_q"], wl.eps)
+    qr_hat = rope(rmsnorm(inp["q_rope"], inp["gamma_qr"], wl.eps), pos[..., None], wl.rope_theta)
+    return {"q_hat": stored_bits(q_hat, wl.cache_dtype),
+            "qr_hat": stored_bits(qr_hat, wl.cache_dtype)}
+
+
+def expand_image(wl, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k, max_T) -> dict:
+    """Keys and values of the explicit path materialised from the stored cache.
+    For token t < T_b of sequence b and group g, with c_t the stored latent:
+    k^_{t,g} = gamma_k,g * (c_t W^K_g) * alpha^k_{t,g} (the stored inverse RMS of
+    that same projection, so k^ = RMSNorm(c_t W^K_g)) and v_{t,g} = c_t W^V_g.
+    Returns the exact float64 values and their storage words, [B, max_T, G, d];
+    rows t >= T_b are zero."""
+    dt = wl.cache_dtype
+    B, G, d, r, P = len(seq_lens), wl.groups, wl.head_dim, wl.rank, wl.page_size
+    k_hat = np.zeros((B, max_T, G, d))
+    v = np.zeros((B, max_T, G, d))
+    for b in range(B):
+        T = int(seq_lens[b])
+        t = np.arange(T)
+        page, sl = block_table[b, t // P], t % P
+        C = words_to_f64(kv[page, sl, :r], dt)
+        AK = np.asarray(alpha_k[page, sl, :], dtype=np.float64)
+        for g in range(G):
+            K = C @ np.asarray(w_k[g], dtype=np.float64)
+            k_hat[b, :T, g] = K * np.asarray(gamma_k[g], dtype=np.float64)[None, :] * AK[:, g:g + 1]
+            v[b, :T, g] = C @ np.asarray(w_v[g], dtype=np.float64)
+    return {"k_hat": k_hat, "v": v, "k_hat_words": stored_bits(k_hat, dt),
+            "v_words": stored_bits(v, dt)}
+
+
+def prefill_on_images(wl, q_img, e_img, kv, block_table, seq_lens, rows=None) -> dict:
+    """Attention of the explicit path over stored images: query token i of
+    sequence b, head h (group g), over the keys t <= T_b - s_q + i:
+    l_t = scale * (q^ . k^_{t,g} + q^R . k^R_t), p = softmax(l),
+    o = sum_t p_t v_{t,g}, lse = ln sum_t e^{l_t}.  The inputs are the stored
+    words of q^, q^R (query image), k^, v (expanded image) and k^R (cache).
+    ``rows`` optionally restricts to a list of (b, i, h).  Returns
+    {(b, i, h): {"o": [d], "lse": float}}."""
+    dt = wl.cache_dtype
+    r, P, H, G, sq = wl.rank, wl.page_size, wl.heads, wl.groups, wl.s_q
+    B = len(seq_lens)
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(sq) for h in range(H)]
+    by_bi = {}
+    for (b, i, h) in rows:
+        by_bi.setdefault((b, i), []).append(h)
+    qh = words_to_f64(q_img["q_hat"], dt)
+    qr = words_to_f64(q_img["qr_hat"], dt)
+    kh = words_to_f64(e_img["k_hat_words"], dt)
+    vv = words_to_f64(e_img["v_words"], dt)
+    res = {}
+    for (b, i), hs in by_bi.items():
+        hs = np.asarray(hs)
+        T = int(seq_lens[b])
+        n = visible_count(T, sq, i)
+        t = np.arange(n)
+        KR = words_to_f64(kv[block_table[b, t // P], t % P, r:], dt)
+        for h in hs:
+            g = int(group_of(h, H, G))
+            logits = wl.softmax_scale * (kh[b, :n, g] @ qh[b, i, h] + KR @ qr[b, i, h])
+            pr, lse = _softmax_stats(logits[None, :])
+            res[(b, i, int(h))] = {"o": (pr @ vv[b, :n, g])[0], "lse": float(lse[0])}
+    return res
+
+
 def combine(o_part, lse_part):
     """Merge split partials ([..., P, r], [..., P]) by log-sum-exp weights:
     M = max_p lse_p, lse = M + ln sum_p e^{lse_p - M}, o = sum_p e^{lse_p - lse} o_p.

@@ -652,6 +652,75 @@ def check_sparse_invalid_entries():
         assert not np.any(v["o_lat"]) and np.isneginf(v["lse"])
 
 
+# ---------------------------------------------------------------------------
+# chunked prefill on the explicit path
+# ---------------------------------------------------------------------------
+
+def _prefill_images(wl, inp):
+    img = O.full_cache_image(wl, inp)
+    max_T = wl.max_pages_per_seq * wl.page_size
+    e = O.expand_image(wl, img["kv"], img["alpha_k"], inp["block_table"], inp["seq_lens"],
+                       inp["w_k"], inp["w_v"], inp["gamma_k"], max_T)
+    return img, O.prefill_query_image(wl, inp), e
+
+
+def check_expanded_keys_unit_rms():
+    """Every materialised key divided by gamma_k has mean square
+    m / (m + eps), m the mean square of its projection (the RMS of the
+    stored latent's projection, through the stored alpha^k), and the rows
+    past each sequence are zero."""
+    wl = small("grouped")
+    inp = W.make_inputs(wl, seed=37)
+    img, _, e = _prefill_images(wl, inp)
+    for b, T in enumerate(inp["seq_lens"]):
+        T = int(T)
+        t = np.arange(T)
+        page, sl = inp["block_table"][b, t // 64], t % 64
+        C = O.words_to_f64(img["kv"][page, sl, :wl.rank], wl.cache_dtype)
+        for g in range(wl.groups):
+            K = C @ inp["w_k"][g].astype(np.float64)
+            m = np.mean(K * K, axis=1)
+            got = np.mean((e["k_hat"][b, :T, g] / inp["gamma_k"][g][None, :]) ** 2, axis=1)
+            assert np.allclose(got, m / (m + wl.eps), rtol=2e-6), np.max(np.abs(got / (m / (m + wl.eps)) - 1))
+        assert not np.any(e["k_hat"][b, T:]) and not np.any(e["v"][b, T:])
+
+
+def check_prefill_matches_explicit_f32():
+    """With an fp32 cache the stored images differ from the inputs only by
+    float32 rounding, so the prefill over them must agree with the explicit
+    float64 path (values, latent-free) to ~1e-6; s_q > 1 exercises the causal
+    window of every chunk token, G = 4 the per-group keys and values."""
+    for name, kw in (("mtp", dict(s_q=6)), ("grouped", dict(s_q=3))):
+        wl = small(name, **kw).replace(cache_dtype="f32")
+        inp = W.make_inputs(wl, seed=38)
+        img, qi, e = _prefill_images(wl, inp)
+        res = O.prefill_on_images(wl, qi, e, img["kv"], inp["block_table"], inp["seq_lens"])
+        for b in range(wl.batch):
+            for i in range(wl.s_q):
+                ex = O.explicit_rows(wl, inp, b, i)
+                got = np.stack([res[(b, i, h)]["o"] for h in range(wl.heads)])
+                lse = np.array([res[(b, i, h)]["lse"] for h in range(wl.heads)])
+                assert rel_err(got, ex["o"]) < 2e-5, rel_err(got, ex["o"])
+                assert np.max(np.abs(lse - ex["lse"])) < 2e-5
+
+
+def check_prefill_bf16_within_tolerance():
+    """The bf16 images alone (before any kernel) stay inside the 1e-2
+    end-to-end budget against the explicit float64 path."""
+    wl = small("dsv3", batch=1, seq_len=300, s_q=8)
+    inp = W.make_inputs(wl, seed=39)
+    img, qi, e = _prefill_images(wl, inp)
+    res = O.prefill_on_images(wl, qi, e, img["kv"], inp["block_table"], inp["seq_lens"])
+    worst = 0.0
+    for i in range(wl.s_q):
+        ex = O.explicit_rows(wl, inp, 0, i)
+        got = np.stack([res[(0, i, h)]["o"] for h in range(wl.heads)])
+        rowerr = np.max(np.abs(got - ex["o"]), axis=1) / np.max(np.abs(ex["o"]), axis=1)
+        worst = max(worst, float(np.max(rowerr)))
+    assert worst < 7.5e-3, worst
+    return worst
+
+
 def check_intensity_golden(golden):
     """The per-token arithmetic intensity of the absorbed decode path at s_q = 1,
     128 heads, r = 512, d_R = 64 against the value the GQLA page states."""

@@ -149,6 +149,21 @@ def _sparse_bounds_unstaged(K, num_splits, stage=32):
     return _orig["sparse_split_bounds"](K, num_splits, 1)
 
 
+def _expand_values_with_w_k(wl, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k, max_T):
+    return _orig["expand_image"](wl, kv, alpha_k, block_table, seq_lens, w_k, w_k, gamma_k, max_T)
+
+
+def _expand_without_gamma_k(wl, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k, max_T):
+    return _orig["expand_image"](wl, kv, alpha_k, block_table, seq_lens, w_k, w_v,
+                                 np.ones_like(gamma_k), max_T)
+
+
+def _prefill_window_one_longer(wl, q_img, e_img, kv, block_table, seq_lens, rows=None):
+    # every query sees one token past its causal end
+    return _orig["prefill_on_images"](wl, q_img, e_img, kv, block_table,
+                                      np.asarray(seq_lens) + 1, rows)
+
+
 MUTATIONS = {
     "absorb drops gamma_k": ("absorb_query", _absorb_without_gamma_k,
                              [lambda: P.check_explicit_equals_absorbed("grouped")]),
@@ -188,6 +203,13 @@ MUTATIONS = {
                                     [P.check_sparse_subset_against_explicit]),
     "sparse splits not whole stages": ("sparse_split_bounds", _sparse_bounds_unstaged,
                                        [P.check_sparse_split_bounds]),
+    "prefill values projected with W^K": ("expand_image", _expand_values_with_w_k,
+                                          [P.check_prefill_matches_explicit_f32]),
+    "prefill keys without gamma_k": ("expand_image", _expand_without_gamma_k,
+                                     [P.check_expanded_keys_unit_rms,
+                                      P.check_prefill_matches_explicit_f32]),
+    "prefill causal window one token long": ("prefill_on_images", _prefill_window_one_longer,
+                                             [P.check_prefill_matches_explicit_f32]),
     "explicit path skips the key norm": ("explicit_rows", _explicit_unnormalised_key,
                                          [P.check_textbook_reduction,
                                           lambda: P.check_explicit_equals_absorbed("dsv3")]),

@@ -123,3 +123,15 @@ def test_sparse_subset_against_explicit():
 
 def test_sparse_invalid_entries():
     P.check_sparse_invalid_entries()
+
+
+def test_expanded_keys_unit_rms():
+    P.check_expanded_keys_unit_rms()
+
+
+def test_prefill_matches_explicit_f32():
+    P.check_prefill_matches_explicit_f32()
+
+
+def test_prefill_bf16_within_tolerance():
+    P.check_prefill_bf16_within_tolerance()
