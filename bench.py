@@ -18,7 +18,8 @@ events on its stream) against the peak of its bound: bf16 matrix-core FLOP/s
 when the workload's arithmetic intensity is past the ridge, else 8 TB/s of HBM.
 ``workloads`` carries the same figures for the other bf16 workloads (dsv3,
 grouped, long); ``sparse`` the selected-token decode (2048 listed tokens per
-query out of 16384, its listed rows as the algorithmic bytes);
+query out of 16384, its listed rows as the algorithmic bytes); ``prefill`` the
+chunked prefill on the explicit path (a 512-token chunk over 8192 tokens);
 ``qknorm_sweep`` the cost of the inverse-RMS factors over a
 batch-1 context sweep from 4k to 256k tokens; ``cpu_baseline`` the float64 CPU
 oracle timed on a bounded sample on the host's cores (and on one core).
@@ -460,6 +461,43 @@ def measure_sparse(Q, W, torch, timer, splits=8):
             "decode_hbm_frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def measure_prefill(Q, W, torch, timer):
+    """Chunked prefill on the explicit path: 2 sequences of 8192 tokens whose
+    last 512 are the chunk; the query side, the materialised keys and values of
+    the whole cache, and the causal attention, each timed back to back.  FLOPs:
+    the attention's q^.k^ + q^R.k^R and P.V products over each query's visible
+    keys, and the expansion's two products over every cached token."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS["prefill"]
+    log("prefill: generating inputs")
+    inp = W.make_inputs(wl, seed=0)
+    r = DecodeRunner(wl, inp)
+    r.fill_history()
+    r.append_new()
+    r.alloc_prefill()
+    torch.cuda.synchronize()
+    vis = sum(int(T) - wl.s_q + i + 1 for T in inp["seq_lens"] for i in range(wl.s_q))
+    att_flops = vis * wl.heads * 2 * (2 * wl.head_dim + wl.rope_dim)
+    exp_flops = int(np.sum(inp["seq_lens"])) * wl.groups * 2 * (2 * wl.rank * wl.head_dim)
+    n = 20
+    graphs = [timer.capture(lambda k: r.prefill_query(), n),
+              timer.capture(lambda k: r.prefill_expand(), n),
+              timer.capture(lambda k: r.prefill_attend(), n)]
+    timer.warm(graphs[2])
+    q_ms, e_ms, a_ms = [t / n for t in timer.timed(graphs, reps=9)]
+    log(f"prefill: B={wl.batch} chunk={wl.s_q} T={wl.seq_len}: query {q_ms * 1e3:.1f} us, "
+        f"expand {e_ms * 1e3:.1f} us, attend {a_ms * 1e3:.1f} us "
+        f"({att_flops / (a_ms * 1e-3) / 1e12:.0f} TFLOP/s)")
+    return {"workload": "prefill", "batch": wl.batch, "chunk": wl.s_q, "seq_len": wl.seq_len,
+            "heads": wl.heads, "query_us": round(q_ms * 1e3, 2), "expand_us": round(e_ms * 1e3, 2),
+            "attend_us": round(a_ms * 1e3, 2), "attend_flops": att_flops,
+            "attend_tflops": round(att_flops / (a_ms * 1e-3) / 1e12, 1),
+            "attend_mfma_frac": round(att_flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "expand_flops": exp_flops,
+            "expand_tflops": round(exp_flops / (e_ms * 1e-3) / 1e12, 1)}
+
+
 def qknorm_sweep(Q, W, torch, timer, lengths=(4096, 8192, 16384, 32768, 65536, 131072, 262144)):
     """Batch-1 decode + combine (128 heads, r = 512, d_R = 64, latent scales
     log-normal sigma 0.5) with and without the inverse-RMS factors over a
@@ -624,9 +662,10 @@ def main():
         for name in ("dsv3", "grouped", "long", "mtp"):
             if name != args.workload:
                 others.append(run(name, False)[2]["summary"])
-    sparse = None
+    sparse = prefill = None
     if not args.only:
         sparse = measure_sparse(Q, W, torch, timer)
+        prefill = measure_prefill(Q, W, torch, timer)
     sweep = None
     if not args.only and not args.no_sweep:
         log("batch-1 QK-norm overhead sweep")
@@ -666,6 +705,7 @@ def main():
         "roofline": roof,
         "workloads": [hs] + others,
         "sparse": sparse,
+        "prefill": prefill,
         "qknorm_sweep": sweep,
         "cpu_baseline": cpu,
     }

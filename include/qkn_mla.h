@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 6
+#define QKN_MLA_ABI_VERSION 7
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -253,6 +253,68 @@ QKN_API int qkn_mla_decode(const qkn_mla_dims* dims, const void* q_tilde, const 
  */
 QKN_API int qkn_mla_combine(const qkn_mla_dims* dims, int32_t num_splits, const void* o_partial,
                     const float* lse_partial, float* o_latent, float* lse, void* stream);
+
+/*
+ * Chunked prefill on the explicit path: three calls.
+ *   Source: QK-Normed MLA summary, "Planteamiento del Problema" (the explicit
+ *   path materialises k = c W^K_g and applies the RMSNorm after the
+ *   projection) and "Metodologia" item 4 (the RoPE block is normed on its
+ *   own).  A chunk of dims->s_q new query tokens per sequence attends
+ *   causally to the whole cache, the chunk included (its tokens appended
+ *   first with qkn_mla_append): query i of sequence b sits at position
+ *   T_b - s_q + i and sees the tokens t <= T_b - s_q + i.
+ *   Supported for a bf16 cache with r = 512, d = 128, d_R = 64 and a multiple
+ *   of 32 heads per group (QKN_ERR_UNSUPPORTED otherwise).  max_T below is
+ *   dims->max_pages_per_seq * 64.  The materialised q_hat, k_hat and v are IEEE
+ *   half (fp16): the norm bounds |q_hat_j| by sqrt(d) |gamma_q,j| and |k_hat_j|
+ *   likewise, and half keeps three more bits than bf16.
+ *
+ * qkn_mla_prefill_query: q_hat[b,i,h,:] = gamma_q * q / RMS(q) (fp16) and
+ *   q_rope_normed as qkn_mla_absorb_query writes it.
+ *   q [B, s_q, H, d], q_rope [B, s_q, H, d_R] float32; q_pos [B, s_q] int32;
+ *   out: q_hat [B, s_q, H, d] fp16, q_rope_normed [B, s_q, H, d_R] bf16.
+ */
+QKN_API int qkn_mla_prefill_query(const qkn_mla_dims* dims, const float* q, const float* q_rope,
+                          const int32_t* q_pos, const float* gamma_q, const float* gamma_qr,
+                          void* q_hat, void* q_rope_normed, void* stream);
+
+/*
+ * qkn_mla_prefill_expand: keys and values of every cached token t < T_b of
+ *   every sequence and group, from the stored latent c_t:
+ *     k_hat[b,t,g,:] = gamma_k[g] * (c_t W^K_g) * alpha_k_cache[t,g]   (fp16)
+ *     v[b,t,g,:]     = c_t W^V_g                                        (fp16)
+ *   (alpha^k is 1/RMS of the same projection, so k_hat = RMSNorm(c_t W^K_g)),
+ *   as matrix products on the matrix cores with every product exact and
+ *   float32 sums.  Rows t >= T_b are written as zeros.
+ *   out: k_hat, v [B, max_T, G, d] fp16.  w_k, w_v [G, r, d], gamma_k [G, d]
+ *   float32.  err_flag (nullable): a token on an out-of-range page entry is
+ *   written as zeros and QKN_FLAG_INDEX is ORed in; a value beyond the half
+ *   range (stored as +-inf) ORs QKN_FLAG_PARTIAL_RANGE.
+ */
+QKN_API int qkn_mla_prefill_expand(const qkn_mla_dims* dims, const void* kv_cache,
+                           const float* alpha_k_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, const float* w_k, const float* w_v,
+                           const float* gamma_k, void* k_hat, void* v, int32_t* err_flag,
+                           void* stream);
+
+/*
+ * qkn_mla_prefill_attend: for query i of sequence b and head h (group g),
+ *   over the keys t <= T_b - s_q + i:
+ *     l_t = softmax_scale * (q_hat . k_hat[b,t,g] + q_rope_normed . k^R_t),
+ *     o[b,i,h,:] = sum_t softmax(l)_t v[b,t,g,:],  lse[b,i,h] = ln sum_t e^{l_t},
+ *   with k^R_t the stored RoPE key of the paged cache.  Flash attention on
+ *   the matrix cores: fp16 content and value operands, bf16 RoPE operands,
+ *   float32 accumulation, probabilities rounded to fp16 for the P.V product
+ *   and normalised by the sum of the same rounded values.
+ *   out: o [B, s_q, H, d], lse [B, s_q, H] float32.
+ *   err_flag (nullable): T_b < s_q, T_b beyond the page table, or a bad page
+ *   entry ORs QKN_FLAG_INDEX (bad pages read as zero RoPE keys).
+ */
+QKN_API int qkn_mla_prefill_attend(const qkn_mla_dims* dims, const void* q_hat,
+                           const void* q_rope_normed, const void* k_hat, const void* v,
+                           const void* kv_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, float* o, float* lse, int32_t* err_flag,
+                           void* stream);
 
 /*
  * qkn_mla_decode_sparse -- selected-token decode (the partials of a split-KV

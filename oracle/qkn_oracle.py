@@ -78,14 +78,19 @@ def stored_value(x64, dtype: str) -> np.ndarray:
         return x32
     if dtype == "bf16":
         return bf16_bits_to_f32(f32_to_bf16_bits(x32))
+    if dtype == "f16":
+        return x32.astype(np.float16).astype(np.float32)   # IEEE half, nearest-even
     raise ValueError(dtype)
 
 
 def stored_bits(x64, dtype: str) -> np.ndarray:
-    """Raw storage words: uint16 patterns for bf16, float32 for f32."""
+    """Raw storage words: uint16 patterns for bf16 and f16 (IEEE half, nearest
+    even), float32 for f32."""
     x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if dtype == "f32":
         return x32
+    if dtype == "f16":
+        return x32.astype(np.float16).view(np.uint16)
     return f32_to_bf16_bits(x32)
 
 
@@ -341,6 +346,8 @@ def query_image(wl, inp) -> dict:
 def words_to_f64(words, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(words).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(words, dtype=np.uint16).view(np.float16).astype(np.float64)
     return np.asarray(words, dtype=np.float64)
 
 
@@ -484,15 +491,22 @@ def sparse_decode_on_image(wl, q_img, kv, alpha_k, block_table, seq_lens, indice
 # tokens per sequence attends causally to the whole cache, the chunk included.
 # ----------------------------------------------------------------------------
 
+def prefill_dtype(wl) -> str:
+    """Storage of the prefill's materialised q^, k^ and v: IEEE half with a bf16
+    cache (the norm bounds |q^_j| by sqrt(d) |gamma_q,j| and |k^_j| likewise,
+    and half keeps 3 more bits than bf16), float32 with a float32 cache."""
+    return "f16" if wl.cache_dtype == "bf16" else "f32"
+
+
 def prefill_query_image(wl, inp) -> dict:
     """The explicit path's query side as stored: q^ = gamma_q * q / RMS(q) per
-    head, and the normed, rotated RoPE query (as in :func:`query_image`), both
-    in the cache dtype."""
+    head (in :func:`prefill_dtype`), and the normed, rotated RoPE query in the
+    cache dtype (as in :func:`query_image`)."""
     B, sq = wl.batch, wl.s_q
     pos = np.asarray(inp["seq_lens"], dtype=np.int64)[:, None] - sq + np.arange(sq)[None, :]
     q_hat = rmsnorm(inp["q"], inp["gamma_q"], wl.eps)
     qr_hat = rope(rmsnorm(inp["q_rope"], inp["gamma_qr"], wl.eps), pos[..., None], wl.rope_theta)
-    return {"q_hat": stored_bits(q_hat, wl.cache_dtype),
+    return {"q_hat": stored_bits(q_hat, prefill_dtype(wl)),
             "qr_hat": stored_bits(qr_hat, wl.cache_dtype)}
 
 
@@ -501,8 +515,8 @@ def expand_image(wl, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k, max_
     For token t < T_b of sequence b and group g, with c_t the stored latent:
     k^_{t,g} = gamma_k,g * (c_t W^K_g) * alpha^k_{t,g} (the stored inverse RMS of
     that same projection, so k^ = RMSNorm(c_t W^K_g)) and v_{t,g} = c_t W^V_g.
-    Returns the exact float64 values and their storage words, [B, max_T, G, d];
-    rows t >= T_b are zero."""
+    Returns the exact float64 values and their storage words (in
+    :func:`prefill_dtype`), [B, max_T, G, d]; rows t >= T_b are zero."""
     dt = wl.cache_dtype
     B, G, d, r, P = len(seq_lens), wl.groups, wl.head_dim, wl.rank, wl.page_size
     k_hat = np.zeros((B, max_T, G, d))
@@ -517,8 +531,9 @@ def expand_image(wl, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k, max_
             K = C @ np.asarray(w_k[g], dtype=np.float64)
             k_hat[b, :T, g] = K * np.asarray(gamma_k[g], dtype=np.float64)[None, :] * AK[:, g:g + 1]
             v[b, :T, g] = C @ np.asarray(w_v[g], dtype=np.float64)
-    return {"k_hat": k_hat, "v": v, "k_hat_words": stored_bits(k_hat, dt),
-            "v_words": stored_bits(v, dt)}
+    pd = prefill_dtype(wl)
+    return {"k_hat": k_hat, "v": v, "k_hat_words": stored_bits(k_hat, pd),
+            "v_words": stored_bits(v, pd)}
 
 
 def prefill_on_images(wl, q_img, e_img, kv, block_table, seq_lens, rows=None) -> dict:
@@ -537,10 +552,11 @@ def prefill_on_images(wl, q_img, e_img, kv, block_table, seq_lens, rows=None) ->
     by_bi = {}
     for (b, i, h) in rows:
         by_bi.setdefault((b, i), []).append(h)
-    qh = words_to_f64(q_img["q_hat"], dt)
+    pd = prefill_dtype(wl)
+    qh = words_to_f64(q_img["q_hat"], pd)
     qr = words_to_f64(q_img["qr_hat"], dt)
-    kh = words_to_f64(e_img["k_hat_words"], dt)
-    vv = words_to_f64(e_img["v_words"], dt)
+    kh = words_to_f64(e_img["k_hat_words"], pd)
+    vv = words_to_f64(e_img["v_words"], pd)
     res = {}
     for (b, i), hs in by_bi.items():
         hs = np.asarray(hs)

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 QKN_OK = 0
 QKN_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -96,6 +96,12 @@ def library() -> ctypes.CDLL:
         lib.qkn_mla_decode.restype = ctypes.c_int
         lib.qkn_mla_decode.argtypes = [D, P, P, P, P, P, P, P, _c_int32, ctypes.c_uint32,
                                        P, P, P, P]
+        lib.qkn_mla_prefill_query.restype = ctypes.c_int
+        lib.qkn_mla_prefill_query.argtypes = [D, P, P, P, P, P, P, P, P]
+        lib.qkn_mla_prefill_expand.restype = ctypes.c_int
+        lib.qkn_mla_prefill_expand.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
+        lib.qkn_mla_prefill_attend.restype = ctypes.c_int
+        lib.qkn_mla_prefill_attend.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
         lib.qkn_mla_decode_sparse.restype = ctypes.c_int
         lib.qkn_mla_decode_sparse.argtypes = [D, P, P, P, P, P, P, P, P, _c_int32, _c_int32,
                                               ctypes.c_uint32, P, P, P, P]
@@ -123,6 +129,7 @@ EXPORTED_SYMBOLS = (
     "qkn_mla_decode", "qkn_mla_decode_sparse", "qkn_mla_decode_attend",
     "qkn_mla_decode_attend_noalloc",
     "qkn_mla_combine", "qkn_mla_combine_project",
+    "qkn_mla_prefill_query", "qkn_mla_prefill_expand", "qkn_mla_prefill_attend",
 )
 
 
@@ -278,6 +285,70 @@ def qkn_mla_decode(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_
         _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
         ctypes.c_void_p(_stream_ptr(stream)))
     _check("qkn_mla_decode", st)
+
+
+def qkn_mla_prefill_query(dims: Dims, q, q_rope, q_pos, gamma_q, gamma_qr, q_hat, q_rope_normed,
+                          stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    st = library().qkn_mla_prefill_query(
+        ctypes.byref(d),
+        _ptr(q, "q", f32, rows * d.head_dim),
+        _ptr(q_rope, "q_rope", f32, rows * d.rope_dim),
+        _ptr(q_pos, "q_pos", i32, d.batch * d.s_q),
+        _ptr(gamma_q, "gamma_q", f32, d.head_dim),
+        _ptr(gamma_qr, "gamma_qr", f32, d.rope_dim),
+        _ptr(q_hat, "q_hat", torch.float16, rows * d.head_dim),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_prefill_query", st)
+
+
+def qkn_mla_prefill_expand(dims: Dims, kv_cache, alpha_k_cache, block_table, seq_lens, w_k, w_v,
+                           gamma_k, k_hat, v, err_flag=None, stream=None):
+    d = dims
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    n_kv = d.batch * d.max_pages_per_seq * PAGE_SIZE * d.groups * d.head_dim
+    st = library().qkn_mla_prefill_expand(
+        ctypes.byref(d),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(alpha_k_cache, "alpha_k_cache", f32, d.num_pages * PAGE_SIZE * d.groups),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", i32, d.batch),
+        _ptr(w_k, "w_k", f32, d.groups * d.rank * d.head_dim),
+        _ptr(w_v, "w_v", f32, d.groups * d.rank * d.head_dim),
+        _ptr(gamma_k, "gamma_k", f32, d.groups * d.head_dim),
+        _ptr(k_hat, "k_hat", torch.float16, n_kv),
+        _ptr(v, "v", torch.float16, n_kv),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_prefill_expand", st)
+
+
+def qkn_mla_prefill_attend(dims: Dims, q_hat, q_rope_normed, k_hat, v, kv_cache, block_table,
+                           seq_lens, o, lse, err_flag=None, stream=None):
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ct = cache_torch_dtype(d)
+    f32, i32 = torch.float32, torch.int32
+    n_kv = d.batch * d.max_pages_per_seq * PAGE_SIZE * d.groups * d.head_dim
+    st = library().qkn_mla_prefill_attend(
+        ctypes.byref(d),
+        _ptr(q_hat, "q_hat", torch.float16, rows * d.head_dim),
+        _ptr(q_rope_normed, "q_rope_normed", ct, rows * d.rope_dim),
+        _ptr(k_hat, "k_hat", torch.float16, n_kv),
+        _ptr(v, "v", torch.float16, n_kv),
+        _ptr(kv_cache, "kv_cache", ct, d.num_pages * PAGE_SIZE * (d.rank + d.rope_dim)),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", i32, d.batch),
+        _ptr(o, "o", f32, rows * d.head_dim),
+        _ptr(lse, "lse", f32, rows),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_prefill_attend", st)
 
 
 def qkn_mla_decode_sparse(dims: Dims, q_tilde, alpha_q, q_rope_normed, kv_cache, alpha_k_cache,

@@ -260,6 +260,58 @@ int qkn_mla_decode_sparse(const qkn_mla_dims* dims, const void* q_tilde, const f
   return hip_status(qkn::launch_decode_sparse(*dims, a, static_cast<hipStream_t>(stream)));
 }
 
+int qkn_mla_prefill_query(const qkn_mla_dims* dims, const float* q, const float* q_rope,
+                          const int32_t* q_pos, const float* gamma_q, const float* gamma_qr,
+                          void* q_hat, void* q_rope_normed, void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (!qkn::prefill_supported(*dims)) return QKN_ERR_UNSUPPORTED;
+  if (!q || !q_rope || !q_pos || !gamma_q || !gamma_qr || !q_hat || !q_rope_normed)
+    return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, q_rope, q_pos, gamma_q, gamma_qr, q_hat, q_rope_normed};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_prefill_query(*dims, q, q_rope, q_pos, gamma_q, gamma_qr, q_hat,
+                                              q_rope_normed, static_cast<hipStream_t>(stream)));
+}
+
+int qkn_mla_prefill_expand(const qkn_mla_dims* dims, const void* kv_cache,
+                           const float* alpha_k_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, const float* w_k, const float* w_v,
+                           const float* gamma_k, void* k_hat, void* v, int32_t* err_flag,
+                           void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (!qkn::prefill_supported(*dims)) return QKN_ERR_UNSUPPORTED;
+  if (!kv_cache || !alpha_k_cache || !block_table || !seq_lens || !w_k || !w_v || !gamma_k ||
+      !k_hat || !v)
+    return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {kv_cache, alpha_k_cache, block_table, seq_lens, w_k, w_v, gamma_k, k_hat, v};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_prefill_expand(*dims, kv_cache, alpha_k_cache, block_table,
+                                               seq_lens, w_k, w_v, gamma_k, k_hat, v, err_flag,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int qkn_mla_prefill_attend(const qkn_mla_dims* dims, const void* q_hat, const void* q_rope_normed,
+                           const void* k_hat, const void* v, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, float* o,
+                           float* lse, int32_t* err_flag, void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (!qkn::prefill_supported(*dims)) return QKN_ERR_UNSUPPORTED;
+  if (!q_hat || !q_rope_normed || !k_hat || !v || !kv_cache || !block_table || !seq_lens || !o ||
+      !lse)
+    return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_hat, q_rope_normed, k_hat, v, kv_cache, block_table, seq_lens, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_prefill_attend(*dims, q_hat, q_rope_normed, k_hat, v, kv_cache,
+                                               block_table, seq_lens, o, lse, err_flag,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int qkn_mla_decode_attend(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
                           const void* q_rope_normed, const void* kv_cache,
                           const float* alpha_k_cache, const int32_t* block_table,

@@ -181,6 +181,21 @@ hipError_t launch_decode_mfma(const qkn_mla_dims& d, const DecodeArgs& a, hipStr
 // (heads not a multiple of 128, a cache of 4 GiB or more, or more than 2048
 // list entries per split).
 int sparse_decode_check(const qkn_mla_dims& d, int sel_len, int num_splits);
+
+// Chunked prefill on the explicit path (bf16 cache, r = 512, d = 128, d_R = 64,
+// a multiple of 32 heads per group).
+bool prefill_supported(const qkn_mla_dims& d);
+hipError_t launch_prefill_query(const qkn_mla_dims& d, const float* q, const float* q_rope,
+                                const int32_t* q_pos, const float* gamma_q, const float* gamma_qr,
+                                void* q_hat, void* q_rope_normed, hipStream_t s);
+hipError_t launch_prefill_expand(const qkn_mla_dims& d, const void* kv, const float* alpha_k,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const float* w_k, const float* w_v, const float* gamma_k,
+                                 void* k_hat, void* v, int32_t* err_flag, hipStream_t s);
+hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const void* q_rope_normed,
+                                 const void* k_hat, const void* v, const void* kv,
+                                 const int32_t* block_table, const int32_t* seq_lens, float* o,
+                                 float* lse, int32_t* err_flag, hipStream_t s);
 hipError_t launch_decode_sparse(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,

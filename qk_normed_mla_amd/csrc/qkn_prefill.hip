@@ -1,0 +1,529 @@
+// Chunked prefill on the explicit path (QK-Normed MLA summary, "Planteamiento
+// del Problema": keys k = c W^K_g are materialised and RMS-normed after the
+// projection; "Metodologia" item 4: the RoPE block is normed on its own).  A
+// chunk of s_q new query tokens per sequence attends causally to its whole
+// cache, the chunk included (its tokens appended first).  Three kernels:
+//   prefill_query:  q^ = gamma_q * q / RMS(q) per head (IEEE half), and the
+//                   normed, rotated RoPE query (bf16, as the absorb call's).
+//   prefill_expand: for every cached token and KV group, k^ = gamma_k *
+//                   (c W^K_g) * alpha^k (the stored inverse RMS of that same
+//                   projection of the stored latent) and v = c W^V_g, as IEEE
+//                   half, matrix products on the matrix cores.
+// The materialised q^, k^ and v are half, not bf16: the norm bounds |q^_j| by
+// sqrt(d) |gamma_q,j| and |k^_j| likewise, and half's three more bits keep the
+// explicit path inside the end-to-end tolerance; a value beyond the half range
+// is reported (QKN_FLAG_PARTIAL_RANGE).
+//   prefill_attend: flash attention of the chunk over the materialised keys
+//                   and values, l = scale * (q^ . k^ + q^R . k^R), online
+//                   softmax, o = sum p v.
+#include <math.h>
+
+#include <algorithm>
+
+#include "qkn_internal.h"
+
+namespace qkn {
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// query side: one wave per query row (b, i, h)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_query_kernel(
+    const float* __restrict__ q, const float* __restrict__ q_rope, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_qr,
+    _Float16* __restrict__ q_hat, uint16_t* __restrict__ qr_out, int rows, int heads,
+    int head_dim, int rope_dim, float eps, float theta) {
+  const int lane = threadIdx.x & 63;
+  const int half = rope_dim / 2;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+    float x[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = lane + 64 * k;
+      x[k] = j < head_dim ? q[(size_t)row * head_dim + j] : 0.f;
+      ss = fmaf(x[k], x[k], ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)head_dim + eps);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = lane + 64 * k;
+      if (j < head_dim) q_hat[(size_t)row * head_dim + j] = static_cast<_Float16>(x[k] * inv * gamma_q[j]);
+    }
+    if (rope_dim == 0) continue;
+    const float x1 = lane < half ? q_rope[(size_t)row * rope_dim + lane] : 0.f;
+    const float x2 = lane < half ? q_rope[(size_t)row * rope_dim + lane + half] : 0.f;
+    const float sr = wave_sum(fmaf(x1, x1, x2 * x2));
+    const float ir = 1.0f / sqrtf(sr / (float)rope_dim + eps);
+    if (lane < half) {
+      float c = 1.f, s = 0.f;
+      if (theta != 0.f) rope_cos_sin<false>(q_pos[row / heads], lane, rope_dim, theta, &c, &s);
+      const float y1 = x1 * ir * gamma_qr[lane], y2 = x2 * ir * gamma_qr[lane + half];
+      qr_out[(size_t)row * rope_dim + lane] = f32_to_bf16(y1 * c - y2 * s);
+      qr_out[(size_t)row * rope_dim + lane + half] = f32_to_bf16(y2 * c + y1 * s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// keys and values: K = C W^K_g, V = C W^V_g for 256 tokens of one sequence and
+// group per block (blockIdx.z: 0 keys, 1 values).  Wave w owns tokens 32 w ..
+// 32 w + 31 (the A rows: the stored bf16 latent words, exact operands) and all
+// d / 32 column tiles.  W passes through LDS in chunks of KC rows split into
+// three bf16 words (hi + mid + lo, exact to 2^-24), read with
+// ds_read_b64_tr_b16; every product is exact and the sums are float32.
+// ---------------------------------------------------------------------------
+constexpr int EX_WAVES = 8;
+constexpr int EX_TOK = 32 * EX_WAVES;
+constexpr int EX_CHUNK = 8192;  // W values per staged chunk
+constexpr int EX_PAD = 16;      // bf16 of padding per staged row
+constexpr int ex_chunk_rows(int d) { return EX_CHUNK / d < 128 ? EX_CHUNK / d : 128; }
+
+__device__ __forceinline__ void split3(float4 v, bf16x4& hi, bf16x4& mid, bf16x4& lo) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  hi = __builtin_convertvector(x, bf16x4);
+  const f32x4 h = __builtin_convertvector(hi, f32x4);
+  f32x4 r1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r1[j] = x[j] - h[j];
+  mid = __builtin_convertvector(r1, bf16x4);
+  const f32x4 m = __builtin_convertvector(mid, f32x4);
+  f32x4 r2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r2[j] = r1[j] - m[j];
+  lo = __builtin_convertvector(r2, bf16x4);
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(const_cast<__bf16*>(p)));
+}
+
+template <int NT>
+__global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
+    const uint16_t* __restrict__ kv, const float* __restrict__ alpha_k,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const float* __restrict__ w_k, const float* __restrict__ w_v,
+    const float* __restrict__ gamma_k, _Float16* __restrict__ k_hat, _Float16* __restrict__ v_out,
+    int32_t* __restrict__ err_flag, int groups, int rank, int rope_dim, int max_pages,
+    int num_pages, int max_T) {
+  constexpr int D = NT * 32;
+  constexpr int KC = ex_chunk_rows(D);
+  constexpr int PER = KC * D / 4 / (64 * EX_WAVES);  // float4 of a chunk per thread
+  constexpr int SPC = KC / 16;                       // 16-row steps per chunk
+  constexpr int WROW = D + EX_PAD;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __bf16* W0 = reinterpret_cast<__bf16*>(smem);
+  __bf16* W1 = W0 + KC * WROW;
+  __bf16* W2 = W1 + KC * WROW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, G = (lane >> 4) & 1;
+  const int b = blockIdx.y / groups, g = blockIdx.y % groups;
+  const bool values = blockIdx.z == 1;
+  const float* wg = (values ? w_v : w_k) + (size_t)g * rank * D;
+  int T = seq_lens[b];
+  T = min(max(T, 0), max_pages * QKN_MLA_PAGE_SIZE);
+  const int t = blockIdx.x * EX_TOK + 32 * wave + l32;  // token of this lane's A row
+  int row = -1;                                          // its cache row
+  if (t < T) {
+    const int pg = block_table[(size_t)b * max_pages + t / QKN_MLA_PAGE_SIZE];
+    if (pg >= 0 && pg < num_pages) row = pg * QKN_MLA_PAGE_SIZE + t % QKN_MLA_PAGE_SIZE;
+    else if (err_flag && hh == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
+  }
+  const uint16_t* crow = kv + (size_t)(row >= 0 ? row : 0) * (rank + rope_dim);
+
+  // the next chunk: W rows k0 .. k0 + KC - 1 and this lane's latents of its
+  // SPC steps in the order of the transposed read (4 hh + 0..3, 8 + 4 hh + 0..3)
+  float4 wv[PER];
+  uint2 av[SPC][2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * 64 * EX_WAVES;
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(k0 + e / (D / 4)) * D + 4 * (e % (D / 4)));
+    }
+#pragma unroll
+    for (int st = 0; st < SPC; ++st) {
+      const uint16_t* ap = crow + k0 + 16 * st + 4 * hh;
+      av[st][0] = row >= 0 ? *reinterpret_cast<const uint2*>(ap) : make_uint2(0u, 0u);
+      av[st][1] = row >= 0 ? *reinterpret_cast<const uint2*>(ap + 8) : make_uint2(0u, 0u);
+    }
+  };
+  load(0);
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) acc[ct] = f32x16{};
+  const int tr_off = (4 * hh + (l16 >> 2)) * WROW + 16 * G + 4 * (l16 & 3);
+  for (int k0 = 0; k0 < rank; k0 += KC) {
+    __syncthreads();  // every read of the previous chunk done
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * 64 * EX_WAVES;
+      bf16x4 hi, mid, lo;
+      split3(wv[u], hi, mid, lo);
+      const int at = (e / (D / 4)) * WROW + 4 * (e % (D / 4));
+      *reinterpret_cast<bf16x4*>(W0 + at) = hi;
+      *reinterpret_cast<bf16x4*>(W1 + at) = mid;
+      *reinterpret_cast<bf16x4*>(W2 + at) = lo;
+    }
+    bf16x8 a[SPC];
+#pragma unroll
+    for (int st = 0; st < SPC; ++st) {
+      const uint4 w4 = {av[st][0].x, av[st][0].y, av[st][1].x, av[st][1].y};
+      a[st] = __builtin_bit_cast(bf16x8, w4);  // the stored words of c_t
+    }
+    if (k0 + KC < rank) load(k0 + KC);  // in flight during this chunk's products
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < SPC; ++st) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int off = tr_off + 16 * st * WROW + 32 * ct;
+        const bf16x8 b0 = __builtin_shufflevector(tr_read(W0 + off), tr_read(W0 + off + 8 * WROW),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 b1 = __builtin_shufflevector(tr_read(W1 + off), tr_read(W1 + off + 8 * WROW),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 b2 = __builtin_shufflevector(tr_read(W2 + off), tr_read(W2 + off + 8 * WROW),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        acc[ct] = mfma(a[st], b0, acc[ct]);
+        acc[ct] = mfma(a[st], b1, acc[ct]);
+        acc[ct] = mfma(a[st], b2, acc[ct]);
+      }
+    }
+  }
+
+  // D[i][j]: lane holds column 32 ct + l32 of tokens i = r % 4 + 8 (r / 4) + 4 hh
+  // of the wave; keys are scaled by gamma_k[j] alpha^k of the token.  Tokens
+  // past the sequence (or on a bad page) are written as zeros.
+  _Float16* out = values ? v_out : k_hat;
+  const float* gk = gamma_k + (size_t)g * D;
+  float big = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = (r & 3) + 8 * (r >> 2) + 4 * hh;
+    const int tt = blockIdx.x * EX_TOK + 32 * wave + i;
+    if (tt >= max_T) continue;
+    const int row_i = __shfl(row, i);  // lane i holds token i's cache row
+    float s = 0.f;
+    if (row_i >= 0) s = values ? 1.f : alpha_k[(size_t)row_i * groups + g];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int j = 32 * ct + l32;
+      const float x = row_i >= 0 ? acc[ct][r] * s * (values ? 1.f : gk[j]) : 0.f;
+      big = fmaxf(big, fabsf(x));
+      out[(((size_t)b * max_T + tt) * groups + g) * D + j] = static_cast<_Float16>(x);
+    }
+  }
+  // a value the half rounds to +-inf
+  if (big >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
+}
+
+// ---------------------------------------------------------------------------
+// attention: one workgroup per (sequence, 4 consecutive chunk tokens, 32 heads
+// of one group); wave w takes query token i0 + w with the 32 heads as its
+// rows (lane l % 32).  Keys stream in tiles of 32 (k^ 8 KB, k^R 4 KB, v 8 KB)
+// through two LDS buffers: the next tile's loads are in flight during the
+// current tile's products.  Per tile and wave:
+//   S^T[32 keys x 32 heads] = K^ q^^T + K^R q^R^T (12 products; A a 16-byte
+//     key row read per lane, B the queries in registers),
+//   online softmax in base 2 (running max per head, the accumulator rescaled
+//     when it rises; probabilities to the products rounded to bf16 and the
+//     normaliser summed from the same rounded values),
+//   O^T[128 x 32 heads] += V^T P^T (8 products; V^T read with
+//     ds_read_b64_tr_b16 from the row-major tile).
+// Rows of 256 bytes store chunk c of key t at chunk c ^ (t mod 16) (RoPE rows:
+// c ^ (t mod 8)), so the column reads of 32 rows spread over the banks.
+// ---------------------------------------------------------------------------
+constexpr int AT_D = 128, AT_DR = 64, AT_R = 512;
+constexpr int AT_KEYS = 32;
+constexpr int AT_K_BYTES = AT_KEYS * AT_D * 2;    // 8192
+constexpr int AT_R_BYTES = AT_KEYS * AT_DR * 2;   // 4096
+constexpr int AT_TILE = 2 * AT_K_BYTES + AT_R_BYTES;  // 20480
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(256, 1) void prefill_attend_kernel(
+    const _Float16* __restrict__ q_hat, const uint16_t* __restrict__ q_rope,
+    const _Float16* __restrict__ k_hat, const _Float16* __restrict__ v_in,
+    const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ o, float* __restrict__ lse,
+    int32_t* __restrict__ err_flag, int s_q, int heads, int groups, int max_pages, int num_pages,
+    int max_T, int token_groups, int head_blocks, float scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * AT_TILE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int hb = blockIdx.x % head_blocks;
+  const int tg = (blockIdx.x / head_blocks) % token_groups;
+  const int b = blockIdx.x / (head_blocks * token_groups);
+  const int h0 = 32 * hb;
+  const int g = h0 / (heads / groups);
+  const int i = 4 * tg + w;  // this wave's chunk token
+  const bool active = i < s_q;
+  int T = seq_lens[b];
+  int err = 0;
+  if (T < s_q || T > max_pages * QKN_MLA_PAGE_SIZE) {
+    err = 1;
+    T = min(max(T, s_q), max_pages * QKN_MLA_PAGE_SIZE);
+  }
+  const int vis = active ? T - s_q + i + 1 : 0;                        // keys of this wave
+  const int vis_max = T - s_q + min(4 * tg + 3, s_q - 1) + 1;          // keys of the block
+  const int n_tiles = (vis_max + AT_KEYS - 1) / AT_KEYS;
+
+  // queries as the B operand: lane holds head l32, entries 16 kk + 8 hh .. + 7
+  const size_t qrow = ((size_t)b * s_q + (active ? i : 0)) * heads + h0 + l32;
+  f16x8 qb[AT_D / 16];
+  bf16x8 qrb[AT_DR / 16];
+#pragma unroll
+  for (int kk = 0; kk < AT_D / 16; ++kk)
+    qb[kk] = *reinterpret_cast<const f16x8*>(q_hat + qrow * AT_D + 16 * kk + 8 * hh);
+#pragma unroll
+  for (int kk = 0; kk < AT_DR / 16; ++kk)
+    qrb[kk] = *reinterpret_cast<const bf16x8*>(q_rope + qrow * AT_DR + 16 * kk + 8 * hh);
+
+  // tile loads: thread e < 512 of K^ / V takes row e / 16, chunk e % 16 (two
+  // each); thread e < 256 of K^R row e / 8, chunk e % 8
+  uint4 nk[2], nv[2], nr;
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
+      const int t = kt * AT_KEYS + rr;
+      const size_t at = (((size_t)b * max_T + t) * groups + g) * AT_D + 8 * c;
+      nk[u] = t < vis_max ? *reinterpret_cast<const uint4*>(k_hat + at) : make_uint4(0u, 0u, 0u, 0u);
+      nv[u] = t < vis_max ? *reinterpret_cast<const uint4*>(v_in + at) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int rr = tid >> 3, c = tid & 7;
+    const int t = kt * AT_KEYS + rr;
+    nr = make_uint4(0u, 0u, 0u, 0u);
+    if (t < vis_max) {
+      const int pg = block_table[(size_t)b * max_pages + t / QKN_MLA_PAGE_SIZE];
+      if (pg >= 0 && pg < num_pages) {
+        const size_t row = (size_t)pg * QKN_MLA_PAGE_SIZE + t % QKN_MLA_PAGE_SIZE;
+        nr = *reinterpret_cast<const uint4*>(kv + row * (AT_R + AT_DR) + AT_R + 8 * c);
+      } else {
+        err = 1;
+      }
+    }
+  };
+  auto stash = [&](int kt) {
+    uint8_t* buf = smem + (kt & 1) * AT_TILE;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
+      const int at = rr * 256 + ((c ^ (rr & 15)) << 4);
+      *reinterpret_cast<uint4*>(buf + at) = nk[u];
+      *reinterpret_cast<uint4*>(buf + AT_K_BYTES + AT_R_BYTES + at) = nv[u];
+    }
+    const int rr = tid >> 3, c = tid & 7;
+    *reinterpret_cast<uint4*>(buf + AT_K_BYTES + rr * 128 + ((c ^ (rr & 7)) << 4)) = nr;
+  };
+
+  // per-lane read offsets.  QK: key row l32, chunk 2 kk + hh.  PV (V^T, the
+  // transposed read of the decode's P.C): within a 16-lane group G16, row
+  // t0 = 4 hh + l16 / 4 (and t0 + 8), chunk 4 om + 2 G16 + (l16 % 4) / 2,
+  // byte 8 (l16 % 2); rows + 16 ks.
+  const int l16 = lane & 15, G16 = (lane >> 4) & 1;
+  const int t0 = 4 * hh + (l16 >> 2), c_lo = 2 * G16 + ((l16 & 3) >> 1);
+  const uint32_t pv0 = static_cast<uint32_t>(t0 * 256 + 8 * (l16 & 1) + ((c_lo ^ (t0 & 15)) << 4));
+  const uint32_t pv1 =
+      static_cast<uint32_t>((t0 + 8) * 256 + 8 * (l16 & 1) + ((c_lo ^ ((t0 + 8) & 15)) << 4));
+
+  f32x16 acc[AT_D / 32];
+#pragma unroll
+  for (int om = 0; om < AT_D / 32; ++om) acc[om] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = scale * kLog2e;
+  const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+
+  if (n_tiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    if (kt + 1 < n_tiles) fetch(kt + 1);  // in flight during this tile's products
+    const LDS_AS uint8_t* buf = (const LDS_AS uint8_t*)smem + (kt & 1) * AT_TILE;
+    if (active && kt * AT_KEYS < vis) {
+      // ---- S^T = K^ q^^T + K^R q^R^T ----
+      f32x16 sc = {};
+#pragma unroll
+      for (int kk = 0; kk < AT_D / 16; ++kk) {
+        const f16x8 a = *reinterpret_cast<const LDS_AS f16x8*>(
+            buf + l32 * 256 + (((2 * kk + hh) ^ (l32 & 15)) << 4));
+        sc = mfma(a, qb[kk], sc);
+      }
+#pragma unroll
+      for (int kk = 0; kk < AT_DR / 16; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(
+            buf + AT_K_BYTES + l32 * 128 + (((2 * kk + hh) ^ (l32 & 7)) << 4));
+        sc = mfma(a, qrb[kk], sc);
+      }
+      // ---- mask, running max, rescale ----
+      // register r holds key kt * 32 + r % 4 + 8 (r / 4) + 4 hh
+      const int lim = vis - kt * AT_KEYS - 4 * hh;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if ((r & 3) + 8 * (r >> 2) >= lim) sc[r] = -INFINITY;
+        mx = fmaxf(mx, sc[r]);
+      }
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new > m_run && m_run != -INFINITY) {
+        const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+        l_run *= al;
+#pragma unroll
+        for (int om = 0; om < AT_D / 32; ++om)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[om][r] *= al;
+      }
+      m_run = m_new;
+      const float mc = m_run == -INFINITY ? 0.f : m_run * c2;
+      f16x8 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -mc));
+        const f16x2 pr = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+        pb[r >> 3][r & 7] = pr[0];
+        pb[r >> 3][(r & 7) + 1] = pr[1];
+        l_run = __builtin_amdgcn_fdot2(pr, ones, l_run, false);
+      }
+      // ---- O^T += V^T P^T ----
+      const LDS_AS uint8_t* vb = buf + AT_K_BYTES + AT_R_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int om = 0; om < AT_D / 32; ++om) {
+          const uint32_t off = 4096u * ks;
+          // the transposed read moves 16-bit words; the words are halves here
+          const f16x4 lo4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(vb + ((pv0 ^ (64u * om)) + off))));
+          const f16x4 hi4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(vb + ((pv1 ^ (64u * om)) + off))));
+          const f16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[om] = mfma(a, pb[ks], acc[om]);
+        }
+      }
+    }
+    // the next tile goes to the other buffer, which every wave finished
+    // reading before the previous barrier
+    if (kt + 1 < n_tiles) stash(kt + 1);
+    __syncthreads();
+  }
+
+  // ---- o = acc / l (lane: head l32, entries 32 om + r % 4 + 8 (r / 4) + 4 hh) ----
+  if (active) {
+    const float l_tot = pair_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const size_t orow = ((size_t)b * s_q + i) * heads + h0 + l32;
+#pragma unroll
+    for (int om = 0; om < AT_D / 32; ++om) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 x = {acc[om][4 * qd] * inv, acc[om][4 * qd + 1] * inv,
+                         acc[om][4 * qd + 2] * inv, acc[om][4 * qd + 3] * inv};
+        *reinterpret_cast<f32x4*>(o + orow * AT_D + 32 * om + 8 * qd + 4 * hh) = x;
+      }
+    }
+    if (hh == 0)
+      lse[orow] = l_tot > 0.f ? m_run * scale + log2f(l_tot) * kLn2 : -INFINITY;
+  }
+  if (err && err_flag && lane == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
+}
+
+template <int NT>
+hipError_t launch_expand_nt(const qkn_mla_dims& d, const void* kv, const float* alpha_k,
+                            const int32_t* block_table, const int32_t* seq_lens, const float* w_k,
+                            const float* w_v, const float* gamma_k, void* k_hat, void* v,
+                            int32_t* err_flag, hipStream_t s) {
+  constexpr int D = NT * 32;
+  constexpr int KC = ex_chunk_rows(D);
+  const int lds = 3 * KC * (D + EX_PAD) * 2;
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&prefill_expand_kernel<NT>), lds);
+  if (e != hipSuccess) return e;
+  const int max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
+  hipLaunchKernelGGL(prefill_expand_kernel<NT>, dim3(cdiv(max_T, EX_TOK), d.batch * d.groups, 2),
+                     dim3(64 * EX_WAVES), lds, s, static_cast<const uint16_t*>(kv), alpha_k,
+                     block_table, seq_lens, w_k, w_v, gamma_k, static_cast<_Float16*>(k_hat),
+                     static_cast<_Float16*>(v), err_flag, d.groups, d.rank, d.rope_dim,
+                     d.max_pages_per_seq, d.num_pages, max_T);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(const qkn_mla_dims& d) {
+  return d.cache_dtype == QKN_BF16 && d.head_dim == AT_D && d.rope_dim == AT_DR && d.rank == AT_R &&
+         (d.heads / d.groups) % 32 == 0;
+}
+
+hipError_t launch_prefill_query(const qkn_mla_dims& d, const float* q, const float* q_rope,
+                                const int32_t* q_pos, const float* gamma_q, const float* gamma_qr,
+                                void* q_hat, void* q_rope_normed, hipStream_t s) {
+  const int rows = d.batch * d.s_q * d.heads;
+  const int blocks = std::min(cdiv(rows, 4), 4096);
+  hipLaunchKernelGGL(prefill_query_kernel, dim3(blocks), dim3(256), 0, s, q, q_rope, q_pos, gamma_q,
+                     gamma_qr, static_cast<_Float16*>(q_hat), static_cast<uint16_t*>(q_rope_normed),
+                     rows, d.heads, d.head_dim, d.rope_dim, d.eps, d.rope_theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_expand(const qkn_mla_dims& d, const void* kv, const float* alpha_k,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const float* w_k, const float* w_v, const float* gamma_k,
+                                 void* k_hat, void* v, int32_t* err_flag, hipStream_t s) {
+  return launch_expand_nt<AT_D / 32>(d, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k,
+                                     k_hat, v, err_flag, s);
+}
+
+hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const void* q_rope_normed,
+                                 const void* k_hat, const void* v, const void* kv,
+                                 const int32_t* block_table, const int32_t* seq_lens, float* o,
+                                 float* lse, int32_t* err_flag, hipStream_t s) {
+  const int token_groups = cdiv(d.s_q, 4);
+  const int head_blocks = d.heads / 32;
+  const int max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
+  hipLaunchKernelGGL(prefill_attend_kernel, dim3(d.batch * token_groups * head_blocks), dim3(256), 0,
+                     s, static_cast<const _Float16*>(q_hat),
+                     static_cast<const uint16_t*>(q_rope_normed), static_cast<const _Float16*>(k_hat),
+                     static_cast<const _Float16*>(v), static_cast<const uint16_t*>(kv), block_table,
+                     seq_lens, o, lse, err_flag, d.s_q, d.heads, d.groups, d.max_pages_per_seq,
+                     d.num_pages, max_T, token_groups, head_blocks, d.softmax_scale);
+  return hipGetLastError();
+}
+
+}  // namespace qkn

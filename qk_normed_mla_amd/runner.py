@@ -18,7 +18,8 @@ import torch
 
 from . import (QKN_BF16, PAGE_SIZE, Dims, alloc_decode_workspace, cache_torch_dtype, dims_for,
                partial_torch_dtype, qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine,
-               qkn_mla_combine_project, qkn_mla_decode, qkn_mla_decode_attend)
+               qkn_mla_combine_project, qkn_mla_decode, qkn_mla_decode_attend,
+               qkn_mla_prefill_attend, qkn_mla_prefill_expand, qkn_mla_prefill_query)
 
 
 def _dev(x, device, dtype=None):
@@ -177,6 +178,34 @@ class DecodeRunner:
         self.decode(flags)
         self.combine()
 
+    # -- chunked prefill on the explicit path (s_q = the chunk length) ----------
+    def alloc_prefill(self):
+        """Buffers of the prefill calls: q^ (half), the materialised keys and
+        values [B, max_T, G, d] (half) and the output o, lse."""
+        wl, dev = self.wl, self.device
+        B, sq, H = wl.batch, wl.s_q, wl.heads
+        max_T = self.dims.max_pages_per_seq * PAGE_SIZE
+        self.q_hat = torch.empty((B, sq, H, wl.head_dim), dtype=torch.float16, device=dev)
+        self.k_hat = torch.empty((B, max_T, wl.groups, wl.head_dim), dtype=torch.float16,
+                                 device=dev)
+        self.v_exp = torch.empty_like(self.k_hat)
+        self.o_prefill = torch.empty((B, sq, H, wl.head_dim), dtype=torch.float32, device=dev)
+        self.lse_prefill = torch.empty((B, sq, H), dtype=torch.float32, device=dev)
+
+    def prefill_query(self, stream=None):
+        qkn_mla_prefill_query(self.dims, self.q, self.q_rope, self.q_pos, self.gamma_q,
+                              self.gamma_qr, self.q_hat, self.q_rope_normed, stream)
+
+    def prefill_expand(self, stream=None):
+        qkn_mla_prefill_expand(self.dims, self.kv, self.alpha_k, self.block_table, self.seq_lens,
+                               self.w_k, self.w_v, self.gamma_k, self.k_hat, self.v_exp,
+                               self.err_flag, stream)
+
+    def prefill_attend(self, stream=None):
+        qkn_mla_prefill_attend(self.dims, self.q_hat, self.q_rope_normed, self.k_hat, self.v_exp,
+                               self.kv, self.block_table, self.seq_lens, self.o_prefill,
+                               self.lse_prefill, self.err_flag, stream)
+
     # -- host copies -------------------------------------------------------------
     def kv_words(self) -> np.ndarray:
         """Cache as raw storage words (uint16 for bf16, float32 for f32)."""
@@ -185,6 +214,6 @@ class DecodeRunner:
         return self.kv.cpu().numpy()
 
     def words(self, t: torch.Tensor) -> np.ndarray:
-        if t.dtype == torch.bfloat16:
+        if t.dtype in (torch.bfloat16, torch.float16):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()

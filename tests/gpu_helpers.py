@@ -39,7 +39,7 @@ from qk_normed_mla_amd.runner import DecodeRunner
 # The vector-ALU kernel keeps probabilities and partials (for a float32 cache)
 # in float32: the same form with u = 2^-24.
 TOL_E2E = {"f32": 1e-4, "bf16": 1e-2}
-U_PROB = {1: 2.0 ** -8, 0: 2.0 ** -24}      # probability rounding, by kernel kind
+U_PROB = {1: 2.0 ** -8, 0: 2.0 ** -24, 2: 2.0 ** -11}  # probability rounding: bf16, float32, half
 U_PART = {"f32": 0.0, "bf16": 2.0 ** -11}   # storage of the split partials
 # a float32 cache keeps float32 partials: the vector-ALU kernel's row-relative bar
 TOL_KERNEL_GENERIC = 1e-5
@@ -79,7 +79,8 @@ def row_err(got, ref):
 
 
 def ulp_distance_bf16(a_words, b_words):
-    """Distance in representable bf16 steps between two arrays of words."""
+    """Distance in representable steps between two arrays of 16-bit
+    sign-magnitude words (bf16, or IEEE half: the same ordering holds)."""
     def ordered(w):
         w = np.asarray(w, dtype=np.uint16).astype(np.int32)
         return np.where(w & 0x8000, -(w & 0x7FFF), w)
@@ -88,9 +89,9 @@ def ulp_distance_bf16(a_words, b_words):
 
 def upload_words(words, like: torch.Tensor) -> torch.Tensor:
     """Host storage words -> a device tensor of ``like``'s dtype and shape."""
-    if like.dtype == torch.bfloat16:
+    if like.dtype in (torch.bfloat16, torch.float16):
         t = torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).to(like.device)
-        return t.view(torch.bfloat16).reshape(like.shape)
+        return t.view(like.dtype).reshape(like.shape)
     return torch.from_numpy(np.ascontiguousarray(words, dtype=np.float32)).to(like.device).reshape(like.shape)
 
 

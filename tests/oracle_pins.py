@@ -62,6 +62,22 @@ def check_bf16_against_torch():
     assert np.array_equal(back, ref_back)
 
 
+def check_f16_against_torch():
+    """The half storage words against torch's float32 -> float16 cast (IEEE
+    round to nearest even), ties, subnormals, overflow to inf and signed zero."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(100000).astype(np.float32) * np.float32(5.0)
+    tiny = rng.standard_normal(1000).astype(np.float32) * np.float32(1e-6)   # subnormal halves
+    ties = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0, 65504.0,
+                     65519.0, 65520.0, 1e6, -0.0, 0.0, -1e-9], dtype=np.float32)
+    for v in (x, tiny, ties):
+        got = O.stored_bits(v.astype(np.float64), "f16")
+        want = torch.from_numpy(v).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want)
+        back = O.words_to_f64(got, "f16")
+        assert np.array_equal(back, torch.from_numpy(v).to(torch.float16).double().numpy())
+
+
 def check_rmsnorm_against_torch():
     rng = np.random.default_rng(2)
     for eps in (1e-6, 0.5, 3.0):

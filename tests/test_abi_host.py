@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 17, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 6
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 7
     for st in (0, -1, -2, -3, -4, -5):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -260,3 +260,23 @@ def test_sparse_decode_rejections():
     assert _call_sparse(good_dims(cache_dtype="f32"), 0x1000, P(0x1000), 16) == -2
     big = good_dims(num_pages=60000)                                 # 4.4 GB of cache rows
     assert _call_sparse(big, 0x1000, P(0x1000), 16) == -2
+
+
+def test_prefill_rejections():
+    """The prefill calls check their arguments before any launch: the dims they
+    take (bf16 cache, r = 512, d = 128, d_R = 64, a multiple of 32 heads per
+    group), null pointers and misalignment."""
+    lib = Q.library()
+    P = ctypes.c_void_p
+    a = [P(0x1000)] * 11
+    d = good_dims(s_q=64)
+    for bad in (good_dims(cache_dtype="f32"), good_dims(head_dim=64), good_dims(heads=48, groups=1)):
+        assert lib.qkn_mla_prefill_query(ctypes.byref(bad), *a[:7], None) == -2
+        assert lib.qkn_mla_prefill_expand(ctypes.byref(bad), *a[:9], None, None) == -2
+        assert lib.qkn_mla_prefill_attend(ctypes.byref(bad), *a[:9], None, None) == -2
+    assert lib.qkn_mla_prefill_query(ctypes.byref(d), None, *a[:6], None) == -1
+    assert lib.qkn_mla_prefill_expand(ctypes.byref(d), *a[:8], None, None, None) == -1
+    assert lib.qkn_mla_prefill_attend(ctypes.byref(d), *a[:8], None, None, None) == -1
+    assert lib.qkn_mla_prefill_query(ctypes.byref(d), P(0x1004), *a[:6], None) == -3
+    assert lib.qkn_mla_prefill_expand(ctypes.byref(d), P(0x1008), *a[:8], None, None) == -3
+    assert lib.qkn_mla_prefill_attend(ctypes.byref(d), *a[:8], P(0x1004), None, None) == -3

@@ -14,6 +14,10 @@ def test_bf16_rounding_matches_torch():
     P.check_bf16_against_torch()
 
 
+def test_f16_rounding_matches_torch():
+    P.check_f16_against_torch()
+
+
 def test_rmsnorm_matches_torch():
     P.check_rmsnorm_against_torch()
 

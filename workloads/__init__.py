@@ -93,6 +93,10 @@ WORKLOADS = {
     "sparse": Workload("sparse", batch=32, s_q=1, heads=128, groups=1, rank=512, head_dim=128,
                        rope_dim=64, seq_len=16384, cache_dtype="bf16", latent_log_sigma=0.5,
                        num_splits=2, shuffled_pages=True),
+    # chunked prefill on the explicit path: a 512-token chunk per sequence
+    "prefill": Workload("prefill", batch=2, s_q=512, heads=128, groups=1, rank=512, head_dim=128,
+                        rope_dim=64, seq_len=8192, cache_dtype="bf16", latent_log_sigma=0.5,
+                        num_splits=1),
 }
 
 # entries per query list of the selected-token workload
