@@ -572,6 +572,110 @@ def prefill_on_images(wl, q_img, e_img, kv, block_table, seq_lens, rows=None) ->
     return res
 
 
+def gqa_row_len(wl) -> int:
+    """Words per token of the GQA-path cache: every group's key and value (d
+    each) and the one shared RoPE key (d_R)."""
+    return 2 * wl.groups * wl.head_dim + wl.rope_dim
+
+
+def gqa_cache_image(wl, inp, seq_ids, positions, rows, kvg_init) -> dict:
+    """Cache of the GQA path ([GQLA] section 2: the latent expanded into g groups
+    of keys and values, stored per group, plus the shared RoPE key) under
+    QK-norm ([QKN] Planteamiento: the key is normed after its up-projection, so
+    the stored key is the normed one).  For each appended token, with c_t its
+    latent as the latent cache stores it (the reading alpha^k takes, so that
+    both paths are functions of one stored latent):
+      k^_{t,g} = gamma_k,g * k / RMS(k),  k = c_t W^K_g;   v_{t,g} = c_t W^V_g;
+    the RoPE key as :func:`cache_image` stores it.  Row of slot
+    (page, t % page): group g's key at [2dg, 2dg + d), its value at
+    [2dg + d, 2d(g + 1)), in :func:`prefill_dtype`; the RoPE key at
+    [2dG, 2dG + d_R) in the cache dtype.  Slots not appended keep ``kvg_init``.
+    Returns {"kvg": words, "k_hat": [n, G, d], "v": [n, G, d]} (the exact
+    values of the appended rows, float64)."""
+    dt, pd = wl.cache_dtype, prefill_dtype(wl)
+    G, d, P = wl.groups, wl.head_dim, wl.page_size
+    kvg = np.array(kvg_init, copy=True)
+    bt = inp["block_table"]
+    c_store = stored_value(np.asarray(inp["c"][rows], dtype=np.float64), dt).astype(np.float64)
+    kr_rows = np.asarray(inp["k_rope"][rows], dtype=np.float64)
+    kr_hat = rope(rmsnorm(kr_rows, inp["gamma_kr"], wl.eps), np.asarray(positions), wl.rope_theta)
+    page = bt[np.asarray(seq_ids), np.asarray(positions) // P]
+    slot = np.asarray(positions) % P
+    k_hat = np.zeros((len(c_store), G, d))
+    v = np.zeros((len(c_store), G, d))
+    for g in range(G):
+        k_hat[:, g] = rmsnorm(c_store @ np.asarray(inp["w_k"][g], dtype=np.float64),
+                              inp["gamma_k"][g], wl.eps)
+        v[:, g] = c_store @ np.asarray(inp["w_v"][g], dtype=np.float64)
+        kvg[page, slot, 2 * d * g:2 * d * g + d] = stored_bits(k_hat[:, g], pd)
+        kvg[page, slot, 2 * d * g + d:2 * d * (g + 1)] = stored_bits(v[:, g], pd)
+    kvg[page, slot, 2 * d * G:] = stored_bits(kr_hat, dt)
+    return {"kvg": kvg, "k_hat": k_hat, "v": v}
+
+
+def gqa_empty_image(wl, num_pages: int, fill_word=None) -> np.ndarray:
+    """Initial (never written) GQA-path cache words, the sentinel of tests."""
+    shape = (num_pages, wl.page_size, gqa_row_len(wl))
+    if wl.cache_dtype == "bf16":
+        return np.full(shape, 0x7E01 if fill_word is None else fill_word, dtype=np.uint16)
+    return np.full(shape, np.nan if fill_word is None else fill_word, dtype=np.float32)
+
+
+def gqa_full_image(wl, inp, kvg_init=None) -> dict:
+    """GQA-path cache after appending every token of every sequence."""
+    if kvg_init is None:
+        kvg_init = gqa_empty_image(wl, inp["num_pages"])
+    seq = np.repeat(np.arange(len(inp["seq_lens"]), dtype=np.int64), inp["seq_lens"])
+    pos = np.concatenate([np.arange(int(T)) for T in inp["seq_lens"]])
+    return gqa_cache_image(wl, inp, seq, pos, np.arange(len(seq)), kvg_init)
+
+
+def gqa_decode_on_image(wl, q_img, kvg, block_table, seq_lens, num_splits, rows=None) -> dict:
+    """Split-KV decode of the GQA path over its stored cache: standard grouped
+    attention with no latent expansion per step ([GQLA] section 2).  For query
+    row (b, i, h) of group g and split p (the decode's whole-page split rule),
+    over the visible tokens of the split:
+      l_t = scale * (q^ . k^_{t,g} + q^R . k^R_t),
+      o_p = sum_t softmax(l)_t v_{t,g},  lse_p = ln sum_t e^{l_t};
+    an empty split gives lse_p = -inf, o_p = 0.  q^, q^R are the stored words of
+    :func:`prefill_query_image`.  Returns partials and the combined result per
+    (b, i, h)."""
+    dt, pd = wl.cache_dtype, prefill_dtype(wl)
+    P, H, G, sq, d = wl.page_size, wl.heads, wl.groups, wl.s_q, wl.head_dim
+    B = len(seq_lens)
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(sq) for h in range(H)]
+    by_bi = {}
+    for (b, i, h) in rows:
+        by_bi.setdefault((b, i), []).append(h)
+    qh = words_to_f64(q_img["q_hat"], pd)
+    qr = words_to_f64(q_img["qr_hat"], dt)
+    res = {}
+    for (b, i), hs in by_bi.items():
+        T = int(seq_lens[b])
+        t = np.arange(T)
+        page, slot = block_table[b, t // P], t % P
+        KR = words_to_f64(kvg[page, slot, 2 * d * G:], dt)
+        n_vis = visible_count(T, sq, i)
+        for h in hs:
+            g = int(group_of(h, H, G))
+            K = words_to_f64(kvg[page, slot, 2 * d * g:2 * d * g + d], pd)
+            V = words_to_f64(kvg[page, slot, 2 * d * g + d:2 * d * (g + 1)], pd)
+            logits = wl.softmax_scale * (K @ qh[b, i, h] + KR @ qr[b, i, h])
+            o_part = np.zeros((num_splits, d))
+            lse_part = np.full(num_splits, NEG_INF)
+            for p, (lo, hi) in enumerate(split_bounds(T, num_splits, P)):
+                hi = min(hi, n_vis)
+                if hi <= lo:
+                    continue
+                pr, lse = _softmax_stats(logits[None, lo:hi])
+                o_part[p] = (pr @ V[lo:hi])[0]
+                lse_part[p] = lse[0]
+            o, lse = combine(o_part, lse_part)
+            res[(b, i, int(h))] = {"o_part": o_part, "lse_part": lse_part, "o": o, "lse": float(lse)}
+    return res
+
+
 def combine(o_part, lse_part):
     """Merge split partials ([..., P, r], [..., P]) by log-sum-exp weights:
     M = max_p lse_p, lse = M + ln sum_p e^{lse_p - M}, o = sum_p e^{lse_p - lse} o_p.

@@ -737,6 +737,118 @@ def check_prefill_bf16_within_tolerance():
     return worst
 
 
+# ---------------------------------------------------------------------------
+# the GQA path of GQLA with QK-norm (per-group normed keys and values cached)
+# ---------------------------------------------------------------------------
+
+def check_gqa_image_against_torch():
+    """Every row of the GQA-path cache against torch in float64: group g's key
+    is torch's rms_norm of the stored latent's projection by W^K_g (weight
+    gamma_k,g), its value the projection by W^V_g, at the offsets the layout
+    states; the RoPE key words equal the latent cache's; slots never written
+    keep the sentinel."""
+    wl = small("grouped", batch=2, seq_len=90).replace(cache_dtype="f32")
+    inp = W.make_inputs(wl, seed=41)
+    gi = O.gqa_full_image(wl, inp)
+    kvg = gi["kvg"]
+    d, G = wl.head_dim, wl.groups
+    assert kvg.shape[-1] == 2 * G * d + wl.rope_dim
+    lat = O.full_cache_image(wl, inp)["kv"]
+    written = np.zeros(kvg.shape[:2], dtype=bool)
+    for b, T in enumerate(inp["seq_lens"]):
+        T = int(T)
+        o = inp["tok_offsets"]
+        c = torch.from_numpy(np.asarray(inp["c"][o[b]:o[b + 1]], dtype=np.float32)).double()
+        t = np.arange(T)
+        page, sl = inp["block_table"][b, t // 64], t % 64
+        written[page, sl] = True
+        for g in range(G):
+            k = torch.nn.functional.rms_norm(c @ torch.from_numpy(np.asarray(inp["w_k"][g], np.float64)),
+                                             (d,), torch.from_numpy(np.asarray(inp["gamma_k"][g], np.float64)),
+                                             wl.eps).numpy()
+            v = (c @ torch.from_numpy(np.asarray(inp["w_v"][g], np.float64))).numpy()
+            assert np.allclose(kvg[page, sl, 2 * d * g:2 * d * g + d], k, rtol=2e-7, atol=1e-30)
+            assert np.allclose(kvg[page, sl, 2 * d * g + d:2 * d * (g + 1)], v, rtol=2e-7, atol=1e-6)
+        assert np.array_equal(kvg[page, sl, 2 * d * G:], lat[page, sl, wl.rank:])
+    assert np.all(np.isnan(kvg[~written]))
+
+
+def _gqa_explicit_worst(wl, inp, num_splits):
+    gi = O.gqa_full_image(wl, inp)
+    qi = O.prefill_query_image(wl, inp)
+    res = O.gqa_decode_on_image(wl, qi, gi["kvg"], inp["block_table"], inp["seq_lens"], num_splits)
+    worst, worst_lse = 0.0, 0.0
+    for b in range(wl.batch):
+        for i in range(wl.s_q):
+            ex = O.explicit_rows(wl, inp, b, i)
+            got = np.stack([res[(b, i, h)]["o"] for h in range(wl.heads)])
+            lse = np.array([res[(b, i, h)]["lse"] for h in range(wl.heads)])
+            rowerr = np.max(np.abs(got - ex["o"]), axis=1) / np.max(np.abs(ex["o"]), axis=1)
+            worst = max(worst, float(np.max(rowerr)))
+            worst_lse = max(worst_lse, float(np.max(np.abs(lse - ex["lse"]))))
+    return worst, worst_lse
+
+
+def check_gqa_matches_explicit_f32():
+    """With an fp32 cache the GQA-path decode over its stored cache equals the
+    explicit float64 path to float32 rounding: s_q = 4 (every query's causal
+    window, ragged lengths, shuffled pages) and G = 4 (per-group keys and
+    values), 3 splits."""
+    for name, kw in (("mtp", dict(s_q=4)), ("grouped", dict(s_q=3))):
+        wl = small(name, **kw).replace(cache_dtype="f32")
+        inp = W.make_inputs(wl, seed=42)
+        worst, worst_lse = _gqa_explicit_worst(wl, inp, 3)
+        assert worst < 2e-5 and worst_lse < 2e-5, (name, worst, worst_lse)
+
+
+def check_gqa_equals_absorbed_f32():
+    """The two algebraically equivalent paths of GQLA over the same weights:
+    the GQA-path decode equals the absorbed decode followed by the value
+    up-projection (float32 images of both caches)."""
+    wl = small("grouped", s_q=2).replace(cache_dtype="f32")
+    inp = W.make_inputs(wl, seed=43)
+    gi = O.gqa_full_image(wl, inp)
+    res = O.gqa_decode_on_image(wl, O.prefill_query_image(wl, inp), gi["kvg"], inp["block_table"],
+                                inp["seq_lens"], 2)
+    img = O.full_cache_image(wl, inp)
+    ab = O.decode_on_image(wl, O.query_image(wl, inp), img["kv"], img["alpha_k"], inp["block_table"],
+                           inp["seq_lens"], 2)
+    for b in range(wl.batch):
+        for i in range(wl.s_q):
+            hs = list(range(wl.heads))
+            o_ab = O.value_up_projection(wl, np.stack([ab[(b, i, h)]["o_lat"] for h in hs]),
+                                         inp["w_v"], hs)
+            o_gq = np.stack([res[(b, i, h)]["o"] for h in hs])
+            assert rel_err(o_gq, o_ab) < 2e-5, rel_err(o_gq, o_ab)
+
+
+def check_gqa_split_invariance():
+    """Splitting the keys (whole pages) and merging the partials gives the
+    unsplit result; a split past the visible tokens is empty (lse -inf)."""
+    wl = small("mtp", s_q=4)
+    inp = W.make_inputs(wl, seed=44)
+    gi = O.gqa_full_image(wl, inp)
+    qi = O.prefill_query_image(wl, inp)
+    one = O.gqa_decode_on_image(wl, qi, gi["kvg"], inp["block_table"], inp["seq_lens"], 1)
+    many = O.gqa_decode_on_image(wl, qi, gi["kvg"], inp["block_table"], inp["seq_lens"], 5)
+    for key, v in one.items():
+        assert rel_err(many[key]["o"], v["o"]) < 1e-12 and abs(many[key]["lse"] - v["lse"]) < 1e-12
+        T = int(inp["seq_lens"][key[0]])
+        for p, (lo, hi) in enumerate(O.split_bounds(T, 5)):
+            if hi <= lo:
+                assert many[key]["lse_part"][p] == -np.inf and not np.any(many[key]["o_part"][p])
+
+
+def check_gqa_bf16_within_tolerance():
+    """The bf16 GQA-path images alone (half keys and values, bf16 RoPE parts)
+    stay inside the 1e-2 end-to-end budget against the explicit float64 path."""
+    wl = small("dsv3", batch=2, seq_len=300, s_q=4)
+    inp = W.make_inputs(wl, seed=45)
+    worst, worst_lse = _gqa_explicit_worst(wl, inp, 2)
+    assert worst < 7.5e-3 and worst_lse < 1e-2, (worst, worst_lse)
+    return worst
+
+
 def check_intensity_golden(golden):
     """The per-token arithmetic intensity of the absorbed decode path at s_q = 1,
     128 heads, r = 512, d_R = 64 against the value the GQLA page states."""

@@ -164,6 +164,41 @@ def _prefill_window_one_longer(wl, q_img, e_img, kv, block_table, seq_lens, rows
                                       np.asarray(seq_lens) + 1, rows)
 
 
+def _gqa_values_with_w_k(wl, inp, seq_ids, positions, rows, kvg_init):
+    return _orig["gqa_cache_image"](wl, dict(inp, w_v=inp["w_k"]), seq_ids, positions, rows, kvg_init)
+
+
+def _gqa_keys_not_normed(wl, inp, seq_ids, positions, rows, kvg_init):
+    # the key stored as gamma_k * (c W^K_g), the RMS division forgotten
+    out = _orig["gqa_cache_image"](wl, inp, seq_ids, positions, rows, kvg_init)
+    d, P = wl.head_dim, wl.page_size
+    c = O.stored_value(np.asarray(inp["c"][rows], dtype=np.float64), wl.cache_dtype).astype(np.float64)
+    page = inp["block_table"][np.asarray(seq_ids), np.asarray(positions) // P]
+    slot = np.asarray(positions) % P
+    for g in range(wl.groups):
+        k = (c @ np.asarray(inp["w_k"][g], dtype=np.float64)) * np.asarray(inp["gamma_k"][g])
+        out["kvg"][page, slot, 2 * d * g:2 * d * g + d] = O.stored_bits(k, O.prefill_dtype(wl))
+    return out
+
+
+def _gqa_rope_key_of_next_slot(wl, inp, seq_ids, positions, rows, kvg_init):
+    out = _orig["gqa_cache_image"](wl, inp, seq_ids, positions, rows, kvg_init)
+    off = 2 * wl.groups * wl.head_dim
+    out["kvg"][:, :, off:] = np.roll(out["kvg"][:, :, off:], 1, axis=1)
+    return out
+
+
+def _gqa_decode_groups_swapped(wl, q_img, kvg, block_table, seq_lens, num_splits, rows=None):
+    # heads of group 0 read group 1's keys and values and the reverse
+    d = wl.head_dim
+    kvg = np.array(kvg, copy=True)
+    if wl.groups > 1:
+        g0 = kvg[:, :, 0:2 * d].copy()
+        kvg[:, :, 0:2 * d] = kvg[:, :, 2 * d:4 * d]
+        kvg[:, :, 2 * d:4 * d] = g0
+    return _orig["gqa_decode_on_image"](wl, q_img, kvg, block_table, seq_lens, num_splits, rows)
+
+
 MUTATIONS = {
     "absorb drops gamma_k": ("absorb_query", _absorb_without_gamma_k,
                              [lambda: P.check_explicit_equals_absorbed("grouped")]),
@@ -210,6 +245,18 @@ MUTATIONS = {
                                       P.check_prefill_matches_explicit_f32]),
     "prefill causal window one token long": ("prefill_on_images", _prefill_window_one_longer,
                                              [P.check_prefill_matches_explicit_f32]),
+    "GQA values projected with W^K": ("gqa_cache_image", _gqa_values_with_w_k,
+                                      [P.check_gqa_image_against_torch,
+                                       P.check_gqa_matches_explicit_f32]),
+    "GQA keys stored without the norm": ("gqa_cache_image", _gqa_keys_not_normed,
+                                         [P.check_gqa_image_against_torch,
+                                          P.check_gqa_matches_explicit_f32]),
+    "GQA RoPE key of the neighbouring slot": ("gqa_cache_image", _gqa_rope_key_of_next_slot,
+                                              [P.check_gqa_image_against_torch,
+                                               P.check_gqa_matches_explicit_f32]),
+    "GQA decode swaps two groups": ("gqa_decode_on_image", _gqa_decode_groups_swapped,
+                                    [P.check_gqa_matches_explicit_f32,
+                                     P.check_gqa_equals_absorbed_f32]),
     "explicit path skips the key norm": ("explicit_rows", _explicit_unnormalised_key,
                                          [P.check_textbook_reduction,
                                           lambda: P.check_explicit_equals_absorbed("dsv3")]),

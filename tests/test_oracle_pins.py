@@ -139,3 +139,23 @@ def test_prefill_matches_explicit_f32():
 
 def test_prefill_bf16_within_tolerance():
     P.check_prefill_bf16_within_tolerance()
+
+
+def test_gqa_image_against_torch():
+    P.check_gqa_image_against_torch()
+
+
+def test_gqa_matches_explicit_f32():
+    P.check_gqa_matches_explicit_f32()
+
+
+def test_gqa_equals_absorbed_f32():
+    P.check_gqa_equals_absorbed_f32()
+
+
+def test_gqa_split_invariance():
+    P.check_gqa_split_invariance()
+
+
+def test_gqa_bf16_within_tolerance():
+    P.check_gqa_bf16_within_tolerance()
