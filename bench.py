@@ -107,6 +107,42 @@ def default_splits(wl, seq_lens, cus=256):
     return best[1]
 
 
+def gqa_splits(wl, seq_lens, cus=256):
+    """Split count of the GQA-path attention with the smallest estimated
+    attention + combine time.  Cost model, in units of one 32-key tile of one
+    workgroup: a workgroup costs GQA_WG_FIXED (loading its queries, writing its
+    output) plus its tiles; the workgroups are dealt as the kernel numbers them
+    (XCD x takes the x-th eighth of the logical ids, each XCD's CUs taking them
+    in order as they free up); the combine costs its half partials, written and
+    read back, at about 6 TB/s."""
+    GQA_WG_FIXED, TILE_US = 4.0, 0.6
+    tpw = 4
+    while tpw > 1 and tpw // 2 >= wl.s_q and (wl.heads // wl.groups // 32) % (8 // tpw) == 0:
+        tpw //= 2
+    per_seq = math.ceil(wl.s_q / tpw) * (wl.heads // 32 // (4 // tpw))
+    rows = wl.batch * wl.s_q * wl.heads
+    lens = [int(T) for T in seq_lens]
+    best = None
+    for P in range(1, max(1, min(1024, 8 * cus // (wl.batch * per_seq))) + 1):
+        flat = []
+        for T in lens:
+            L = split_len(max(T, 1), P)
+            for p in range(P):
+                n = min(T, (p + 1) * L) - p * L
+                flat += [GQA_WG_FIXED + math.ceil(n / 32) if n > 0 else 1.0] * per_seq
+        per_xcd = math.ceil(len(flat) / 8)
+        makespan = 0.0
+        for x in range(8):
+            loads = [0.0] * (cus // 8)
+            for c in flat[x * per_xcd:(x + 1) * per_xcd]:
+                heapq.heappush(loads, heapq.heappop(loads) + c)
+            makespan = max(makespan, max(loads))
+        t = makespan * TILE_US + (rows * P * wl.head_dim * 2 * 2 / 6e12 * 1e6 if P > 1 else 0.0)
+        if best is None or t < best[0] - 1e-9:
+            best = (t, P)
+    return best[1]
+
+
 def kernel_source_sha():
     path = os.path.join(ROOT, "qk_normed_mla_amd", "csrc", "qkn_decode_mfma.hip")
     with open(path, "rb") as f:
@@ -498,6 +534,75 @@ def measure_prefill(Q, W, torch, timer):
             "expand_tflops": round(exp_flops / (e_ms * 1e-3) / 1e12, 1)}
 
 
+def measure_gqa(Q, W, torch, timer, name, absorbed_step_us=None, sweep=()):
+    """The GQA path on one workload: the step (query side, GQA append of the
+    s_q new tokens, attention over the per-group cache with its combine) and
+    the attention call alone, over rotating cache replicas.  FLOPs: the
+    q^.k^ + q^R.k^R and P.V products over each query's visible keys; bytes: the
+    cache rows read (2 G d half + d_R bf16 per token).  ``sweep``: split
+    counts to time the attention call at as well (logged)."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS[name]
+    log(f"gqa {name}: generating inputs")
+    inp = W.make_inputs(wl, seed=0)
+    splits = gqa_splits(wl, inp["seq_lens"])
+    r = DecodeRunner(wl, inp)
+    r.alloc_gqa(splits)
+    r.err_flag.zero_()
+    r.gqa_fill_history()
+    r.gqa_step()
+    torch.cuda.synchronize()
+    if int(r.err_flag.item()) != 0:
+        raise RuntimeError("the GQA path flagged its inputs")
+    del r.kv, r.alpha_k  # the latent cache is not used on this path
+    torch.cuda.empty_cache()
+    lens = [int(T) for T in inp["seq_lens"]]
+    vis = sum(T - wl.s_q + i + 1 for T in lens for i in range(wl.s_q))
+    flops = vis * wl.heads * 2 * (2 * wl.head_dim + wl.rope_dim)
+    nbytes = sum(lens) * Q.gqa_row_words(r.dims) * 2
+    cache_bytes = r.kvg.numel() * 2
+    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / cache_bytes) + 1)
+    kvgs = [r.kvg] + [r.kvg.clone() for _ in range(n_rep - 1)]
+    n = max(20, 4 * n_rep)
+
+    def attend_graph():
+        return timer.capture(lambda k: r.gqa_attend(kvg=kvgs[k % n_rep]), n)
+
+    out_sweep = []
+    for P_ in sweep:
+        r.set_gqa_splits(P_)
+        g = attend_graph()
+        timer.warm(g)
+        t = timer.timed([g], reps=9)[0] / n
+        out_sweep.append({"splits": P_, "attend_us": round(t * 1e3, 2)})
+        log(f"gqa {name}: splits {P_}: attend {t * 1e3:.1f} us")
+        del g
+    r.set_gqa_splits(splits)
+    graphs = [timer.capture(lambda k: r.gqa_step(kvg=kvgs[k % n_rep]), n), attend_graph()]
+    timer.warm(graphs[1])
+    step_ms, att_ms = [t / n for t in timer.timed(graphs, reps=15)]
+    tf = flops / (att_ms * 1e-3) / 1e12
+    log(f"gqa {name}: B={wl.batch} s_q={wl.s_q} G={wl.groups} splits={splits}: step "
+        f"{step_ms * 1e3:.1f} us, attention+combine {att_ms * 1e3:.1f} us ({tf:.0f} TFLOP/s, "
+        f"{nbytes / (att_ms * 1e-3) / 1e9:.0f} GB/s of cache rows)")
+    res = {"workload": name, "batch": wl.batch, "s_q": wl.s_q, "heads": wl.heads,
+           "kv_groups": wl.groups, "num_splits": splits, "cache_row_bytes": Q.gqa_row_words(r.dims) * 2,
+           "flops": flops, "cache_bytes": nbytes, "step_us": round(step_ms * 1e3, 2),
+           "attend_us": round(att_ms * 1e3, 2), "attend_tflops": round(tf, 1),
+           "attend_mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+           "attend_gbs": round(nbytes / (att_ms * 1e-3) / 1e9, 1),
+           "attend_hbm_frac": round(nbytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if absorbed_step_us:
+        res["absorbed_step_us"] = absorbed_step_us
+        res["speedup_vs_absorbed"] = round(absorbed_step_us / (step_ms * 1e3), 3)
+    if out_sweep:
+        res["split_sweep"] = out_sweep
+    del kvgs, graphs, r
+    torch.cuda.empty_cache()
+    return res
+
+
 def qknorm_sweep(Q, W, torch, timer, lengths=(4096, 8192, 16384, 32768, 65536, 131072, 262144)):
     """Batch-1 decode + combine (128 heads, r = 512, d_R = 64, latent scales
     log-normal sigma 0.5) with and without the inverse-RMS factors over a
@@ -663,9 +768,13 @@ def main():
             if name != args.workload:
                 others.append(run(name, False)[2]["summary"])
     sparse = prefill = None
+    gqa = []
     if not args.only:
         sparse = measure_sparse(Q, W, torch, timer)
         prefill = measure_prefill(Q, W, torch, timer)
+        absorbed = {w["workload"]: w.get("us_per_step") for w in [head["summary"]] + others}
+        for name in ("mtp", "dsv3", "grouped"):
+            gqa.append(measure_gqa(Q, W, torch, timer, name, absorbed.get(name)))
     sweep = None
     if not args.only and not args.no_sweep:
         log("batch-1 QK-norm overhead sweep")
@@ -706,6 +815,7 @@ def main():
         "workloads": [hs] + others,
         "sparse": sparse,
         "prefill": prefill,
+        "gqa_path": gqa or None,
         "qknorm_sweep": sweep,
         "cpu_baseline": cpu,
     }

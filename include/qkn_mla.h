@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 7
+#define QKN_MLA_ABI_VERSION 8
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -437,6 +437,84 @@ QKN_API int qkn_mla_combine_project(const qkn_mla_dims* dims, int32_t num_splits
                             const void* o_partial, const float* lse_partial,
                             const float* w_v, float* o_latent, float* lse, float* o,
                             uint32_t flags, void* stream);
+
+/*
+ * The GQA path of GQLA with QK-norm.
+ *   Source: GQLA summary, section 2 "Arquitectura" (the GQA path: the latent is
+ *   expanded into g groups of keys and values that the cache stores, plus the
+ *   shared RoPE key, and the decode is plain grouped-query attention with no
+ *   latent expansion per step; the compute-friendly one of two algebraically
+ *   equivalent paths over the same weights) and the QK-Normed MLA summary,
+ *   "Planteamiento del Problema" (the key is RMS-normed after its
+ *   up-projection, so the stored key is the normed one).
+ *   Supported for a bf16 latent dtype with d = 128, d_R = 64, r a multiple of
+ *   16 and a multiple of 32 heads per group (QKN_ERR_UNSUPPORTED otherwise).
+ *
+ *   The GQA cache is paged like the latent cache (the same block table and
+ *   64-token pages), one row of W = 2 G d + d_R 16-bit words per token:
+ *     words [2 d g, 2 d g + d)        the normed key of group g  (IEEE half)
+ *     words [2 d g + d, 2 d (g + 1))  the value of group g       (IEEE half)
+ *     words [2 d G, 2 d G + d_R)      the normed, rotated RoPE key (bf16)
+ *   kvg_cache [num_pages, 64, W], owned by the caller.  The query side is
+ *   qkn_mla_prefill_query's q_hat (fp16) and q_rope_normed (bf16).
+ */
+
+/*
+ * qkn_mla_gqa_append: for each of the n_tokens new tokens (seq_idx[n],
+ *   pos[n]), with c the latent rounded to bf16 (the latent cache's stored
+ *   value):
+ *     key_g   = gamma_k[g] * k / RMS(k),  k = c W^K_g      (half)
+ *     value_g = c W^V_g                                    (half)
+ *     RoPE key as qkn_mla_append stores it                 (bf16)
+ *   into the slot block_table[seq][pos / 64] * 64 + pos % 64.  The products
+ *   run on the matrix cores with every product exact and float32 sums.
+ *   c_new [N, r], k_rope_new [N, d_R], w_k, w_v [G, r, d], gamma_k [G, d],
+ *   gamma_kr [d_R] float32; seq_idx, pos [N] int32.
+ *   err_flag (nullable): a token whose sequence, position or page entry is out
+ *   of range is skipped and ORs QKN_FLAG_INDEX; a value beyond the half range
+ *   (stored as +-inf) ORs QKN_FLAG_PARTIAL_RANGE.  Tokens of one call must
+ *   name distinct slots.
+ */
+QKN_API int qkn_mla_gqa_append(const qkn_mla_dims* dims, int32_t n_tokens, const float* c_new,
+                       const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
+                       const int32_t* block_table, const float* w_k, const float* w_v,
+                       const float* gamma_k, const float* gamma_kr, void* kvg_cache,
+                       int32_t* err_flag, void* stream);
+
+/*
+ * Bytes of device workspace qkn_mla_gqa_attend needs for `num_splits` > 1:
+ *   half partials [B, s_q, H, num_splits, d] and float32 lse partials
+ *   [B, s_q, H, num_splits], each on a 256-byte boundary.  0 for invalid
+ *   dims or num_splits.
+ */
+QKN_API size_t qkn_mla_gqa_workspace_bytes(const qkn_mla_dims* dims, int32_t num_splits);
+
+/*
+ * qkn_mla_gqa_attend: decode over the GQA cache.  For query i of sequence b
+ *   and head h (group g), over the visible tokens t <= T_b - s_q + i:
+ *     l_t = softmax_scale * (q_hat . key_g[t] + q_rope_normed . kR[t]),
+ *     o[b,i,h,:] = sum_t softmax(l)_t value_g[t],  lse[b,i,h] = ln sum_t e^{l_t}.
+ *   The keys are split into num_splits partitions of whole pages (split p
+ *   covers [p L, min((p + 1) L, T_b)), L = 64 ceil(ceil(T_b / P) / 64), as the
+ *   latent decode); each is attended on the matrix cores (fp16 key and value
+ *   operands, bf16 RoPE operands, float32 accumulation, probabilities rounded
+ *   to fp16 and normalised by the sum of the same rounded values), and with
+ *   num_splits > 1 the partials (half, in `workspace`) are merged by the
+ *   log-sum-exp combine.  With num_splits == 1 o and lse are written directly
+ *   and `workspace` may be null; otherwise `workspace` is a device buffer of
+ *   `workspace_bytes` >= qkn_mla_gqa_workspace_bytes(dims, num_splits) bytes,
+ *   256-byte aligned, owned by the caller (contents on return unspecified;
+ *   calls sharing one must be ordered on one stream).
+ *   q_hat [B, s_q, H, d] fp16, q_rope_normed [B, s_q, H, d_R] bf16.
+ *   out: o [B, s_q, H, d], lse [B, s_q, H] float32.
+ *   err_flag (nullable): T_b < s_q, T_b beyond the page table, or a bad page
+ *   entry ORs QKN_FLAG_INDEX (a bad page reads as zero keys and values).
+ */
+QKN_API int qkn_mla_gqa_attend(const qkn_mla_dims* dims, const void* q_hat,
+                       const void* q_rope_normed, const void* kvg_cache,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t num_splits, void* workspace, size_t workspace_bytes,
+                       float* o, float* lse, int32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 QKN_OK = 0
 QKN_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -115,6 +115,13 @@ def library() -> ctypes.CDLL:
         lib.qkn_mla_combine.argtypes = [D, _c_int32, P, P, P, P, P]
         lib.qkn_mla_combine_project.restype = ctypes.c_int
         lib.qkn_mla_combine_project.argtypes = [D, _c_int32, P, P, P, P, P, P, ctypes.c_uint32, P]
+        lib.qkn_mla_gqa_append.restype = ctypes.c_int
+        lib.qkn_mla_gqa_append.argtypes = [D, _c_int32, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.qkn_mla_gqa_workspace_bytes.restype = ctypes.c_size_t
+        lib.qkn_mla_gqa_workspace_bytes.argtypes = [D, _c_int32]
+        lib.qkn_mla_gqa_attend.restype = ctypes.c_int
+        lib.qkn_mla_gqa_attend.argtypes = [D, P, P, P, P, P, _c_int32, P, ctypes.c_size_t, P, P, P,
+                                           P]
         if lib.qkn_mla_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qkn_mla_abi_version()}, "
                                f"this binding needs {ABI_VERSION}: rebuild it")
@@ -130,6 +137,7 @@ EXPORTED_SYMBOLS = (
     "qkn_mla_decode_attend_noalloc",
     "qkn_mla_combine", "qkn_mla_combine_project",
     "qkn_mla_prefill_query", "qkn_mla_prefill_expand", "qkn_mla_prefill_attend",
+    "qkn_mla_gqa_append", "qkn_mla_gqa_workspace_bytes", "qkn_mla_gqa_attend",
 )
 
 
@@ -465,3 +473,65 @@ def qkn_mla_combine_project(dims: Dims, num_splits: int, o_partial, lse_partial,
         _ptr(o, "o", f32, rows * d.head_dim),
         ctypes.c_uint32(int(flags)), ctypes.c_void_p(_stream_ptr(stream)))
     _check("qkn_mla_combine_project", st)
+
+
+# -- the GQA path ----------------------------------------------------------------
+
+def gqa_row_words(dims: Dims) -> int:
+    """16-bit words per token of the GQA cache: every group's key and value
+    (half) and the shared RoPE key (bf16)."""
+    return 2 * dims.groups * dims.head_dim + dims.rope_dim
+
+
+def gqa_workspace_bytes(dims: Dims, num_splits: int) -> int:
+    n = int(library().qkn_mla_gqa_workspace_bytes(ctypes.byref(dims), int(num_splits)))
+    if n == 0:
+        raise QknError("qkn_mla_gqa_workspace_bytes", -1)
+    return n
+
+
+def qkn_mla_gqa_append(dims: Dims, c_new, k_rope_new, seq_idx, pos, block_table, w_k, w_v,
+                       gamma_k, gamma_kr, kvg_cache, err_flag=None, stream=None):
+    """``kvg_cache``: int16 words [num_pages, 64, gqa_row_words(dims)]."""
+    d = dims
+    n = int(seq_idx.numel()) if seq_idx is not None else 0
+    f32, i32 = torch.float32, torch.int32
+    st = library().qkn_mla_gqa_append(
+        ctypes.byref(d), n,
+        _ptr(c_new, "c_new", f32, n * d.rank),
+        _ptr(k_rope_new, "k_rope_new", f32, n * d.rope_dim),
+        _ptr(seq_idx, "seq_idx", i32, n),
+        _ptr(pos, "pos", i32, n),
+        _ptr(block_table, "block_table", i32, d.batch * d.max_pages_per_seq),
+        _ptr(w_k, "w_k", f32, d.groups * d.rank * d.head_dim),
+        _ptr(w_v, "w_v", f32, d.groups * d.rank * d.head_dim),
+        _ptr(gamma_k, "gamma_k", f32, d.groups * d.head_dim),
+        _ptr(gamma_kr, "gamma_kr", f32, d.rope_dim),
+        _ptr(kvg_cache, "kvg_cache", torch.int16, d.num_pages * PAGE_SIZE * gqa_row_words(d)),
+        _ptr(err_flag, "err_flag", i32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_gqa_append", st)
+
+
+def qkn_mla_gqa_attend(dims: Dims, q_hat, q_rope_normed, kvg_cache, block_table, seq_lens,
+                       num_splits: int, workspace, o, lse, err_flag=None, stream=None):
+    """``workspace``: a uint8 device buffer of gqa_workspace_bytes(dims,
+    num_splits) bytes, or None when num_splits == 1."""
+    d = dims
+    rows = d.batch * d.s_q * d.heads
+    ws_bytes = 0 if workspace is None else int(workspace.numel())
+    st = library().qkn_mla_gqa_attend(
+        ctypes.byref(d),
+        _ptr(q_hat, "q_hat", torch.float16, rows * d.head_dim),
+        _ptr(q_rope_normed, "q_rope_normed", cache_torch_dtype(d), rows * d.rope_dim),
+        _ptr(kvg_cache, "kvg_cache", torch.int16, d.num_pages * PAGE_SIZE * gqa_row_words(d)),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_pages_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        int(num_splits),
+        _ptr(workspace, "workspace", torch.uint8, ws_bytes, allow_none=True),
+        ws_bytes,
+        _ptr(o, "o", torch.float32, rows * d.head_dim),
+        _ptr(lse, "lse", torch.float32, rows),
+        _ptr(err_flag, "err_flag", torch.int32, 1, allow_none=True),
+        ctypes.c_void_p(_stream_ptr(stream)))
+    _check("qkn_mla_gqa_attend", st)

@@ -56,6 +56,16 @@ WorkspaceLayout workspace_layout(const qkn_mla_dims& d, int num_splits) {
   return w;
 }
 
+// The split partials of one qkn_mla_gqa_attend call inside its workspace: half
+// o_partial [rows, P, d] at 0, float32 lse_partial [rows, P] at lse_offset.
+WorkspaceLayout gqa_workspace_layout(const qkn_mla_dims& d, int num_splits) {
+  const size_t rows = (size_t)d.batch * d.s_q * d.heads * num_splits;
+  WorkspaceLayout w;
+  w.lse_offset = round256(rows * d.head_dim * 2);
+  w.total = w.lse_offset + round256(rows * 4);
+  return w;
+}
+
 // Checks of qkn_mla_decode's arguments (not the partials); returns the kernel
 // kind (0 generic, 1 matrix cores) or a negative status.
 int check_decode_args(const qkn_mla_dims* dims, const void* q_tilde, const float* alpha_q,
@@ -376,6 +386,62 @@ int qkn_mla_combine_project(const qkn_mla_dims* dims, int32_t num_splits, const 
   return hip_status(qkn::launch_combine_project(*dims, num_splits, o_partial, lse_partial, w_v,
                                                 o_latent, lse, o, flags,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t qkn_mla_gqa_workspace_bytes(const qkn_mla_dims* dims, int32_t num_splits) {
+  if (check_dims(dims) != QKN_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return gqa_workspace_layout(*dims, num_splits).total;
+}
+
+int qkn_mla_gqa_append(const qkn_mla_dims* dims, int32_t n_tokens, const float* c_new,
+                       const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
+                       const int32_t* block_table, const float* w_k, const float* w_v,
+                       const float* gamma_k, const float* gamma_kr, void* kvg_cache,
+                       int32_t* err_flag, void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (!qkn::gqa_supported(*dims)) return QKN_ERR_UNSUPPORTED;
+  if (n_tokens < 0) return QKN_ERR_INVALID_ARG;
+  if (n_tokens == 0) return QKN_OK;
+  if (!c_new || !k_rope_new || !seq_idx || !pos || !block_table || !w_k || !w_v || !gamma_k ||
+      !gamma_kr || !kvg_cache)
+    return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {c_new, k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
+                        kvg_cache};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_gqa_append(*dims, n_tokens, c_new, k_rope_new, seq_idx, pos,
+                                           block_table, w_k, w_v, gamma_k, gamma_kr, kvg_cache,
+                                           err_flag, static_cast<hipStream_t>(stream)));
+}
+
+int qkn_mla_gqa_attend(const qkn_mla_dims* dims, const void* q_hat, const void* q_rope_normed,
+                       const void* kvg_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t num_splits, void* workspace, size_t workspace_bytes, float* o,
+                       float* lse, int32_t* err_flag, void* stream) {
+  int st = check_dims(dims);
+  if (st != QKN_OK) return st;
+  if (!qkn::gqa_supported(*dims)) return QKN_ERR_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > kMaxSplits) return QKN_ERR_INVALID_ARG;
+  const int64_t blocks = (int64_t)dims->batch * num_splits * ((dims->s_q + 3) / 4) * (dims->heads / 32);
+  if (blocks > INT32_MAX) return QKN_ERR_INVALID_ARG;
+  if (!q_hat || !q_rope_normed || !kvg_cache || !block_table || !seq_lens || !o || !lse)
+    return QKN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_hat, q_rope_normed, kvg_cache, block_table, seq_lens, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QKN_ERR_ALIGNMENT;
+  void* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (num_splits > 1) {
+    const WorkspaceLayout w = gqa_workspace_layout(*dims, num_splits);
+    if (!workspace || workspace_bytes < w.total) return QKN_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QKN_ERR_ALIGNMENT;
+    o_part = workspace;
+    lse_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + w.lse_offset);
+  }
+  return hip_status(qkn::launch_gqa_attend(*dims, q_hat, q_rope_normed, kvg_cache, block_table,
+                                           seq_lens, num_splits, o_part, lse_part, o, lse, err_flag,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

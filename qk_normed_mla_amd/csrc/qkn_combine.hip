@@ -152,24 +152,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(const PartT* __
 
 }  // namespace
 
-hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
-                          const float* lse_part, float* o_lat, float* lse, hipStream_t s) {
-  const int n_rows = d.batch * d.s_q * d.heads;
+hipError_t launch_combine_rows(int n_rows, int num_splits, int row_len, bool half_parts,
+                               const void* o_part, const float* lse_part, float* o, float* lse,
+                               hipStream_t s) {
   const int group = num_splits <= 16 ? 1 : num_splits <= 64 ? 4 : num_splits <= 128 ? 8 : 16;
   const int waves = group < 4 ? 4 : group;  // per block
   const int per_block = waves / group;
-  if (d.cache_dtype == QKN_BF16) {
-    const int units = n_rows * cdiv(d.rank, 64 * Chunk<_Float16>::N);
+  if (half_parts) {
+    const int units = n_rows * cdiv(row_len, 64 * Chunk<_Float16>::N);
     hipLaunchKernelGGL(combine_kernel<_Float16>, dim3(cdiv(units, per_block)), dim3(64 * waves), 0,
-                       s, static_cast<const _Float16*>(o_part), lse_part, o_lat, lse, n_rows,
-                       num_splits, d.rank, group);
+                       s, static_cast<const _Float16*>(o_part), lse_part, o, lse, n_rows,
+                       num_splits, row_len, group);
   } else {
-    const int units = n_rows * cdiv(d.rank, 64 * Chunk<float>::N);
+    const int units = n_rows * cdiv(row_len, 64 * Chunk<float>::N);
     hipLaunchKernelGGL(combine_kernel<float>, dim3(cdiv(units, per_block)), dim3(64 * waves), 0, s,
-                       static_cast<const float*>(o_part), lse_part, o_lat, lse, n_rows, num_splits,
-                       d.rank, group);
+                       static_cast<const float*>(o_part), lse_part, o, lse, n_rows, num_splits,
+                       row_len, group);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
+                          const float* lse_part, float* o_lat, float* lse, hipStream_t s) {
+  return launch_combine_rows(d.batch * d.s_q * d.heads, num_splits, d.rank,
+                             d.cache_dtype == QKN_BF16, o_part, lse_part, o_lat, lse, s);
 }
 
 }  // namespace qkn

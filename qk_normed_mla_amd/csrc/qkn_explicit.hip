@@ -1,8 +1,10 @@
-// Chunked prefill on the explicit path (QK-Normed MLA summary, "Planteamiento
-// del Problema": keys k = c W^K_g are materialised and RMS-normed after the
-// projection; "Metodologia" item 4: the RoPE block is normed on its own).  A
-// chunk of s_q new query tokens per sequence attends causally to its whole
-// cache, the chunk included (its tokens appended first).  Three kernels:
+// Kernels of the explicit path, where the normed keys are materialised
+// (QK-Normed MLA summary, "Planteamiento del Problema": keys k = c W^K_g are
+// RMS-normed after the projection; "Metodologia" item 4: the RoPE block is
+// normed on its own).  Two users:
+//
+// Chunked prefill.  A chunk of s_q new query tokens per sequence attends
+// causally to its whole cache, the chunk included (its tokens appended first):
 //   prefill_query:  q^ = gamma_q * q / RMS(q) per head (IEEE half), and the
 //                   normed, rotated RoPE query (bf16, as the absorb call's).
 //   prefill_expand: for every cached token and KV group, k^ = gamma_k *
@@ -13,9 +15,20 @@
 // sqrt(d) |gamma_q,j| and |k^_j| likewise, and half's three more bits keep the
 // explicit path inside the end-to-end tolerance; a value beyond the half range
 // is reported (QKN_FLAG_PARTIAL_RANGE).
-//   prefill_attend: flash attention of the chunk over the materialised keys
+//   attend:         flash attention of the chunk over the materialised keys
 //                   and values, l = scale * (q^ . k^ + q^R . k^R), online
 //                   softmax, o = sum p v.
+//
+// The GQA path of GQLA (GQLA summary, section 2: the latent expanded into g
+// groups of keys and values that the cache stores, plus the shared RoPE key;
+// the decode is plain grouped attention).  Under QK-norm the stored key is the
+// normed one.  The cache is paged like the latent cache, one row per token:
+// [G x (k^ (d) | v (d)) half | k^R (d_R) bf16].
+//   gqa_append:     for each new token, k^ = gamma_k * k / RMS(k), k = c W^K_g,
+//                   and v = c W^V_g from the latent rounded to bf16, and the
+//                   normed, rotated RoPE key.
+//   attend:         the same attention kernel over the paged cache, split over
+//                   the keys (half partials merged by the combine kernel).
 #include <math.h>
 
 #include <algorithm>
@@ -242,9 +255,138 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attention: one workgroup per (sequence, 4 consecutive chunk tokens, 32 heads
-// of one group); wave w takes query token i0 + w with the 32 heads as its
-// rows (lane l % 32).  Keys stream in tiles of 32 (k^ 8 KB, k^R 4 KB, v 8 KB)
+// GQA-path append: one block per (32 new tokens, group, keys | values); wave w
+// computes columns 32 w .. 32 w + 31 of the 32 tokens' projections (d = 128).
+// A operand: the latent rounded to bf16 (the latent cache's stored words, an
+// exact operand); B: W_g columns read from global memory 8 rows per lane and
+// split into three bf16 words (hi + mid + lo, exact to 2^-24), so every
+// product is exact and the sums are float32.  Keys: the block sums the squares
+// of each token's 128 entries (per wave over its 32 lanes, then over the 4
+// waves in LDS) for 1 / RMS; the key blocks of group 0 also write the normed,
+// rotated RoPE key.  Tokens with an out-of-range sequence, position or page are
+// skipped and reported.
+// ---------------------------------------------------------------------------
+constexpr int GA_D = 128, GA_DR = 64;
+
+__global__ __launch_bounds__(256) void gqa_append_kernel(
+    const float* __restrict__ c_new, const float* __restrict__ k_rope_new,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_table, const float* __restrict__ w_k,
+    const float* __restrict__ w_v, const float* __restrict__ gamma_k,
+    const float* __restrict__ gamma_kr, uint16_t* __restrict__ kvg, int32_t* __restrict__ err_flag,
+    int n_tokens, int batch, int groups, int rank, int max_pages, int num_pages, float eps,
+    float theta) {
+  __shared__ float ssq[4][32];
+  __shared__ int slot_of[32];
+  __shared__ int pos_of[32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  const int g = blockIdx.y;
+  const bool values = blockIdx.z == 1;
+  const int row_words = 2 * GA_D * groups + GA_DR;
+  if (tid < 32) {
+    const int n = n0 + tid;
+    int slot = -1, p = 0;
+    if (n < n_tokens) {
+      const int b = seq_idx[n];
+      p = pos[n];
+      if (b >= 0 && b < batch && p >= 0 && p < max_pages * QKN_MLA_PAGE_SIZE) {
+        const int pg = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
+        if (pg >= 0 && pg < num_pages) slot = pg * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
+      }
+      if (slot < 0 && err_flag && g == 0 && !values) atomicOr(err_flag, QKN_FLAG_INDEX);
+    }
+    slot_of[tid] = slot;
+    pos_of[tid] = p;
+  }
+
+  // ---- the 32 x 32 tile of this wave: tokens n0 + i, columns 32 w + j ----
+  const int tok = n0 + l32;
+  const bool tok_ok = tok < n_tokens;
+  const float* crow = c_new + (size_t)(tok_ok ? tok : 0) * rank + 8 * hh;
+  const float* wcol = (values ? w_v : w_k) + (size_t)g * rank * GA_D + (size_t)(8 * hh) * GA_D + 32 * w + l32;
+  f32x16 acc = {};
+#pragma unroll 4
+  for (int k0 = 0; k0 < rank; k0 += 16) {
+    const float4 c0 = tok_ok ? *reinterpret_cast<const float4*>(crow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 c1 = tok_ok ? *reinterpret_cast<const float4*>(crow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = wcol[(size_t)(k0 + j) * GA_D];
+    const f32x8 cx = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const bf16x8 a = __builtin_convertvector(cx, bf16x8);  // nearest-even, as the latent cache stores it
+    bf16x4 h0, m0, lo0, h1, m1, lo1;
+    split3(make_float4(wv[0], wv[1], wv[2], wv[3]), h0, m0, lo0);
+    split3(make_float4(wv[4], wv[5], wv[6], wv[7]), h1, m1, lo1);
+    acc = mfma(a, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    acc = mfma(a, __builtin_shufflevector(m0, m1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    acc = mfma(a, __builtin_shufflevector(lo0, lo1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+  }
+
+  // acc[r]: token i = r % 4 + 8 (r / 4) + 4 hh of the tile, column 32 w + l32
+  float scl[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) scl[r] = 1.f;
+  if (!values) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float q = acc[r] * acc[r];
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) q += __shfl_xor(q, m, 32);
+      if (l32 == 0) ssq[w][(r & 3) + 8 * (r >> 2) + 4 * hh] = q;
+    }
+  }
+  __syncthreads();  // slot_of, pos_of and the partial sums of squares
+  const int col = 32 * w + l32;
+  const float gk = values ? 1.f : gamma_k[(size_t)g * GA_D + col];
+  if (!values) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = (r & 3) + 8 * (r >> 2) + 4 * hh;
+      const float ss = (ssq[0][i] + ssq[1][i]) + (ssq[2][i] + ssq[3][i]);
+      scl[r] = 1.0f / sqrtf(ss / (float)GA_D + eps);
+    }
+  }
+  float big = 0.f;
+  const int part = 2 * GA_D * g + (values ? GA_D : 0) + col;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = (r & 3) + 8 * (r >> 2) + 4 * hh;
+    const int slot = slot_of[i];
+    if (slot < 0) continue;
+    const float x = values ? acc[r] : acc[r] * scl[r] * gk;
+    big = fmaxf(big, fabsf(x));
+    const _Float16 hx = static_cast<_Float16>(x);
+    kvg[(size_t)slot * row_words + part] = __builtin_bit_cast(uint16_t, hx);
+  }
+  if (big >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
+
+  // ---- the RoPE key (key blocks of group 0): wave w takes tokens w, w + 4, ... ----
+  if (values || g != 0) return;
+  for (int i = w; i < 32; i += 4) {
+    const int slot = slot_of[i];
+    if (slot < 0) continue;  // uniform over the wave
+    const float x = k_rope_new[(size_t)(n0 + i) * GA_DR + lane];
+    const float ss = wave_sum(fmaf(x, x, 0.f));
+    const float inv = 1.0f / sqrtf(ss / (float)GA_DR + eps);
+    const float xn = x * inv * gamma_kr[lane];
+    const float x2 = __shfl(xn, lane + GA_DR / 2);
+    if (lane < GA_DR / 2) {
+      float c = 1.f, sn = 0.f;
+      if (theta != 0.f) rope_cos_sin<false>(pos_of[i], lane, GA_DR, theta, &c, &sn);
+      uint16_t* out = kvg + (size_t)slot * row_words + 2 * GA_D * groups;
+      out[lane] = f32_to_bf16(xn * c - x2 * sn);
+      out[lane + GA_DR / 2] = f32_to_bf16(x2 * c + xn * sn);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention: one workgroup per (sequence, key split, 4 consecutive query
+// tokens, 32 heads of one group); wave w takes query token i0 + w with the 32
+// heads as its rows (lane l % 32).  Keys stream in tiles of 32 (k^ 8 KB, k^R 4 KB, v 8 KB)
 // through two LDS buffers: the next tile's loads are in flight during the
 // current tile's products.  Per tile and wave:
 //   S^T[32 keys x 32 heads] = K^ q^^T + K^R q^R^T (12 products; A a 16-byte
@@ -274,33 +416,67 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(256, 1) void prefill_attend_kernel(
-    const _Float16* __restrict__ q_hat, const uint16_t* __restrict__ q_rope,
-    const _Float16* __restrict__ k_hat, const _Float16* __restrict__ v_in,
-    const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ o, float* __restrict__ lse,
-    int32_t* __restrict__ err_flag, int s_q, int heads, int groups, int max_pages, int num_pages,
-    int max_T, int token_groups, int head_blocks, float scale) {
+struct AttendArgs {
+  const _Float16* q_hat;
+  const uint16_t* q_rope;
+  // GQA: the paged cache (rows of row_words 16-bit words); prefill: k^ and v
+  // [B, max_T, G, d] and the latent cache (its RoPE keys)
+  const uint16_t* kvg;
+  const _Float16* k_hat;
+  const _Float16* v;
+  const uint16_t* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* o;               // [rows, d] float32 when num_splits == 1
+  float* lse;             // [rows]
+  _Float16* o_part;       // [rows, P, d] half when num_splits > 1
+  float* lse_part;        // [rows, P]
+  int32_t* err_flag;
+  // a workgroup: tpw query tokens x 4 / tpw blocks of 32 heads (one group)
+  int s_q, heads, groups, max_pages, num_pages, max_T, tpw, token_groups, head_groups, num_splits;
+  int row_words, rank;
+  float scale;
+};
+
+// Consecutive workgroup ids go to the 8 XCDs in turn; this renumbering gives
+// each XCD a contiguous run of logical ids, so the head blocks that read the
+// same keys share one L2.
+__device__ __forceinline__ int xcd_local(int id, int n) {
+  const int full = n & ~7;
+  if (id >= full) return id;
+  return (id & 7) * (full >> 3) + (id >> 3);
+}
+
+template <bool GQA>
+__global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * AT_TILE];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int hb = blockIdx.x % head_blocks;
-  const int tg = (blockIdx.x / head_blocks) % token_groups;
-  const int b = blockIdx.x / (head_blocks * token_groups);
-  const int h0 = 32 * hb;
-  const int g = h0 / (heads / groups);
-  const int i = 4 * tg + w;  // this wave's chunk token
+  const int s_q = A.s_q, heads = A.heads, groups = A.groups, max_pages = A.max_pages;
+  const int head_groups = A.head_groups, token_groups = A.token_groups, tpw = A.tpw;
+  const int lid = xcd_local(blockIdx.x, gridDim.x);
+  const int hg = lid % head_groups;
+  const int tg = (lid / head_groups) % token_groups;
+  const int sp = (lid / (head_groups * token_groups)) % A.num_splits;
+  const int b = lid / (head_groups * token_groups * A.num_splits);
+  const int h0 = 32 * ((4 / tpw) * hg + w / tpw);  // this wave's heads
+  const int g = h0 / (heads / groups);              // the same for every wave
+  const int i = tpw * tg + w % tpw;                 // this wave's query token
   const bool active = i < s_q;
-  int T = seq_lens[b];
+  int T = A.seq_lens[b];
   int err = 0;
   if (T < s_q || T > max_pages * QKN_MLA_PAGE_SIZE) {
     err = 1;
     T = min(max(T, s_q), max_pages * QKN_MLA_PAGE_SIZE);
   }
+  // this split's keys [lo, hi): whole pages (the decode's split rule)
+  const int L = split_len(T, A.num_splits);
+  const int lo = min(sp * L, T), hi = min(sp * L + L, T);  // lo < hi: lo a multiple of 64
   const int vis = active ? T - s_q + i + 1 : 0;                        // keys of this wave
-  const int vis_max = T - s_q + min(4 * tg + 3, s_q - 1) + 1;          // keys of the block
-  const int n_tiles = (vis_max + AT_KEYS - 1) / AT_KEYS;
+  const int vis_max = T - s_q + min(tpw * tg + tpw - 1, s_q - 1) + 1;  // keys of the block
+  const int kt_lo = lo / AT_KEYS;
+  const int kt_hi = lo < hi ? (min(hi, vis_max) + AT_KEYS - 1) / AT_KEYS : kt_lo;
 
   // queries as the B operand: lane holds head l32, entries 16 kk + 8 hh .. + 7
   const size_t qrow = ((size_t)b * s_q + (active ? i : 0)) * heads + h0 + l32;
@@ -308,31 +484,41 @@ __global__ __launch_bounds__(256, 1) void prefill_attend_kernel(
   bf16x8 qrb[AT_DR / 16];
 #pragma unroll
   for (int kk = 0; kk < AT_D / 16; ++kk)
-    qb[kk] = *reinterpret_cast<const f16x8*>(q_hat + qrow * AT_D + 16 * kk + 8 * hh);
+    qb[kk] = *reinterpret_cast<const f16x8*>(A.q_hat + qrow * AT_D + 16 * kk + 8 * hh);
 #pragma unroll
   for (int kk = 0; kk < AT_DR / 16; ++kk)
-    qrb[kk] = *reinterpret_cast<const bf16x8*>(q_rope + qrow * AT_DR + 16 * kk + 8 * hh);
+    qrb[kk] = *reinterpret_cast<const bf16x8*>(A.q_rope + qrow * AT_DR + 16 * kk + 8 * hh);
 
   // tile loads: thread e < 512 of K^ / V takes row e / 16, chunk e % 16 (two
   // each); thread e < 256 of K^R row e / 8, chunk e % 8
   uint4 nk[2], nv[2], nr;
   auto fetch = [&](int kt) {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    // a 32-key tile lies in one 64-token page
+    const int pg = A.block_table[(size_t)b * max_pages + kt * AT_KEYS / QKN_MLA_PAGE_SIZE];
+    const bool page_ok = pg >= 0 && pg < A.num_pages;
+    const size_t row0 = (size_t)(page_ok ? pg : 0) * QKN_MLA_PAGE_SIZE + kt * AT_KEYS % QKN_MLA_PAGE_SIZE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
       const int t = kt * AT_KEYS + rr;
-      const size_t at = (((size_t)b * max_T + t) * groups + g) * AT_D + 8 * c;
-      nk[u] = t < vis_max ? *reinterpret_cast<const uint4*>(k_hat + at) : make_uint4(0u, 0u, 0u, 0u);
-      nv[u] = t < vis_max ? *reinterpret_cast<const uint4*>(v_in + at) : make_uint4(0u, 0u, 0u, 0u);
+      if (GQA) {
+        const uint16_t* p = A.kvg + (row0 + rr) * A.row_words + 2 * AT_D * g + 8 * c;
+        nk[u] = t < vis_max && page_ok ? *reinterpret_cast<const uint4*>(p) : z;
+        nv[u] = t < vis_max && page_ok ? *reinterpret_cast<const uint4*>(p + AT_D) : z;
+      } else {
+        const size_t at = (((size_t)b * A.max_T + t) * groups + g) * AT_D + 8 * c;
+        nk[u] = t < vis_max ? *reinterpret_cast<const uint4*>(A.k_hat + at) : z;
+        nv[u] = t < vis_max ? *reinterpret_cast<const uint4*>(A.v + at) : z;
+      }
     }
     const int rr = tid >> 3, c = tid & 7;
     const int t = kt * AT_KEYS + rr;
-    nr = make_uint4(0u, 0u, 0u, 0u);
+    nr = z;
     if (t < vis_max) {
-      const int pg = block_table[(size_t)b * max_pages + t / QKN_MLA_PAGE_SIZE];
-      if (pg >= 0 && pg < num_pages) {
-        const size_t row = (size_t)pg * QKN_MLA_PAGE_SIZE + t % QKN_MLA_PAGE_SIZE;
-        nr = *reinterpret_cast<const uint4*>(kv + row * (AT_R + AT_DR) + AT_R + 8 * c);
+      if (page_ok) {
+        nr = GQA ? *reinterpret_cast<const uint4*>(A.kvg + (row0 + rr) * A.row_words + 2 * AT_D * groups + 8 * c)
+                 : *reinterpret_cast<const uint4*>(A.kv + (row0 + rr) * (A.rank + AT_DR) + A.rank + 8 * c);
       } else {
         err = 1;
       }
@@ -365,16 +551,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attend_kernel(
 #pragma unroll
   for (int om = 0; om < AT_D / 32; ++om) acc[om] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = scale * kLog2e;
+  const float c2 = A.scale * kLog2e;
   const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  if (n_tiles > 0) {
-    fetch(0);
-    stash(0);
+  if (kt_lo < kt_hi) {
+    fetch(kt_lo);
+    stash(kt_lo);
   }
   __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    if (kt + 1 < n_tiles) fetch(kt + 1);  // in flight during this tile's products
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    if (kt + 1 < kt_hi) fetch(kt + 1);  // in flight during this tile's products
     const LDS_AS uint8_t* buf = (const LDS_AS uint8_t*)smem + (kt & 1) * AT_TILE;
     if (active && kt * AT_KEYS < vis) {
       // ---- S^T = K^ q^^T + K^R q^R^T ----
@@ -441,28 +627,45 @@ __global__ __launch_bounds__(256, 1) void prefill_attend_kernel(
     }
     // the next tile goes to the other buffer, which every wave finished
     // reading before the previous barrier
-    if (kt + 1 < n_tiles) stash(kt + 1);
+    if (kt + 1 < kt_hi) stash(kt + 1);
     __syncthreads();
   }
 
-  // ---- o = acc / l (lane: head l32, entries 32 om + r % 4 + 8 (r / 4) + 4 hh) ----
+  // ---- o = acc / l (lane: head l32, entries 32 om + r % 4 + 8 (r / 4) + 4 hh);
+  // a split with no visible key gives o = 0, lse = -inf ----
   if (active) {
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float ls = l_tot > 0.f ? m_run * A.scale + log2f(l_tot) * kLn2 : -INFINITY;
     const size_t orow = ((size_t)b * s_q + i) * heads + h0 + l32;
+    if (A.num_splits == 1) {
 #pragma unroll
-    for (int om = 0; om < AT_D / 32; ++om) {
+      for (int om = 0; om < AT_D / 32; ++om) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const f32x4 x = {acc[om][4 * qd] * inv, acc[om][4 * qd + 1] * inv,
-                         acc[om][4 * qd + 2] * inv, acc[om][4 * qd + 3] * inv};
-        *reinterpret_cast<f32x4*>(o + orow * AT_D + 32 * om + 8 * qd + 4 * hh) = x;
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 x = {acc[om][4 * qd] * inv, acc[om][4 * qd + 1] * inv,
+                           acc[om][4 * qd + 2] * inv, acc[om][4 * qd + 3] * inv};
+          *reinterpret_cast<f32x4*>(A.o + orow * AT_D + 32 * om + 8 * qd + 4 * hh) = x;
+        }
       }
+      if (hh == 0) A.lse[orow] = ls;
+    } else {
+      // a partial is a convex combination of half values: it stays in range
+      const size_t prow = orow * A.num_splits + sp;
+#pragma unroll
+      for (int om = 0; om < AT_D / 32; ++om) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 x = {acc[om][4 * qd] * inv, acc[om][4 * qd + 1] * inv,
+                           acc[om][4 * qd + 2] * inv, acc[om][4 * qd + 3] * inv};
+          *reinterpret_cast<f16x4*>(A.o_part + prow * AT_D + 32 * om + 8 * qd + 4 * hh) =
+              __builtin_convertvector(x, f16x4);
+        }
+      }
+      if (hh == 0) A.lse_part[prow] = ls;
     }
-    if (hh == 0)
-      lse[orow] = l_tot > 0.f ? m_run * scale + log2f(l_tot) * kLn2 : -INFINITY;
   }
-  if (err && err_flag && lane == 0) atomicOr(err_flag, QKN_FLAG_INDEX);
+  if (err && A.err_flag && lane == 0) atomicOr(A.err_flag, QKN_FLAG_INDEX);
 }
 
 template <int NT>
@@ -482,6 +685,17 @@ hipError_t launch_expand_nt(const qkn_mla_dims& d, const void* kv, const float* 
                      static_cast<_Float16*>(v), err_flag, d.groups, d.rank, d.rope_dim,
                      d.max_pages_per_seq, d.num_pages, max_T);
   return hipGetLastError();
+}
+
+// Query tokens per workgroup: 4, or fewer when s_q is smaller and the heads of
+// one group fill the other waves (so no wave idles at s_q = 1 or 2).
+void set_shape(const qkn_mla_dims& d, AttendArgs& A) {
+  const int blocks_per_group = d.heads / d.groups / 32;
+  int tpw = 4;
+  while (tpw > 1 && tpw / 2 >= d.s_q && blocks_per_group % (8 / tpw) == 0) tpw /= 2;
+  A.tpw = tpw;
+  A.token_groups = cdiv(d.s_q, tpw);
+  A.head_groups = d.heads / 32 / (4 / tpw);
 }
 
 }  // namespace
@@ -514,16 +728,83 @@ hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const
                                  const void* k_hat, const void* v, const void* kv,
                                  const int32_t* block_table, const int32_t* seq_lens, float* o,
                                  float* lse, int32_t* err_flag, hipStream_t s) {
-  const int token_groups = cdiv(d.s_q, 4);
-  const int head_blocks = d.heads / 32;
-  const int max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
-  hipLaunchKernelGGL(prefill_attend_kernel, dim3(d.batch * token_groups * head_blocks), dim3(256), 0,
-                     s, static_cast<const _Float16*>(q_hat),
-                     static_cast<const uint16_t*>(q_rope_normed), static_cast<const _Float16*>(k_hat),
-                     static_cast<const _Float16*>(v), static_cast<const uint16_t*>(kv), block_table,
-                     seq_lens, o, lse, err_flag, d.s_q, d.heads, d.groups, d.max_pages_per_seq,
-                     d.num_pages, max_T, token_groups, head_blocks, d.softmax_scale);
+  AttendArgs A{};
+  A.q_hat = static_cast<const _Float16*>(q_hat);
+  A.q_rope = static_cast<const uint16_t*>(q_rope_normed);
+  A.k_hat = static_cast<const _Float16*>(k_hat);
+  A.v = static_cast<const _Float16*>(v);
+  A.kv = static_cast<const uint16_t*>(kv);
+  A.block_table = block_table;
+  A.seq_lens = seq_lens;
+  A.o = o;
+  A.lse = lse;
+  A.err_flag = err_flag;
+  A.s_q = d.s_q;
+  A.heads = d.heads;
+  A.groups = d.groups;
+  A.max_pages = d.max_pages_per_seq;
+  A.num_pages = d.num_pages;
+  A.max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
+  set_shape(d, A);
+  A.num_splits = 1;
+  A.rank = d.rank;
+  A.scale = d.softmax_scale;
+  hipLaunchKernelGGL(attend_kernel<false>, dim3(d.batch * A.token_groups * A.head_groups), dim3(256),
+                     0, s, A);
   return hipGetLastError();
+}
+
+bool gqa_supported(const qkn_mla_dims& d) {
+  return d.cache_dtype == QKN_BF16 && d.head_dim == AT_D && d.rope_dim == AT_DR && d.rank % 16 == 0 &&
+         (d.heads / d.groups) % 32 == 0;
+}
+
+int gqa_row_words(const qkn_mla_dims& d) { return 2 * d.head_dim * d.groups + d.rope_dim; }
+
+hipError_t launch_gqa_append(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new,
+                             const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
+                             const int32_t* block_table, const float* w_k, const float* w_v,
+                             const float* gamma_k, const float* gamma_kr, void* kvg,
+                             int32_t* err_flag, hipStream_t s) {
+  hipLaunchKernelGGL(gqa_append_kernel, dim3(cdiv(n_tokens, 32), d.groups, 2), dim3(256), 0, s, c_new,
+                     k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
+                     static_cast<uint16_t*>(kvg), err_flag, n_tokens, d.batch, d.groups, d.rank,
+                     d.max_pages_per_seq, d.num_pages, d.eps, d.rope_theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const void* q_rope_normed,
+                             const void* kvg, const int32_t* block_table, const int32_t* seq_lens,
+                             int num_splits, void* o_part, float* lse_part, float* o, float* lse,
+                             int32_t* err_flag, hipStream_t s) {
+  AttendArgs A{};
+  A.q_hat = static_cast<const _Float16*>(q_hat);
+  A.q_rope = static_cast<const uint16_t*>(q_rope_normed);
+  A.kvg = static_cast<const uint16_t*>(kvg);
+  A.block_table = block_table;
+  A.seq_lens = seq_lens;
+  A.o = o;
+  A.lse = lse;
+  A.o_part = static_cast<_Float16*>(o_part);
+  A.lse_part = lse_part;
+  A.err_flag = err_flag;
+  A.s_q = d.s_q;
+  A.heads = d.heads;
+  A.groups = d.groups;
+  A.max_pages = d.max_pages_per_seq;
+  A.num_pages = d.num_pages;
+  A.max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
+  set_shape(d, A);
+  A.num_splits = num_splits;
+  A.row_words = gqa_row_words(d);
+  A.rank = d.rank;
+  A.scale = d.softmax_scale;
+  hipLaunchKernelGGL(attend_kernel<true>,
+                     dim3(d.batch * num_splits * A.token_groups * A.head_groups), dim3(256), 0, s, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || num_splits == 1) return e;
+  return launch_combine_rows(d.batch * d.s_q * d.heads, num_splits, AT_D, true, o_part, lse_part, o,
+                             lse, s);
 }
 
 }  // namespace qkn

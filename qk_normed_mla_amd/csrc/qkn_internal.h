@@ -198,8 +198,29 @@ hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const
                                  float* lse, int32_t* err_flag, hipStream_t s);
 hipError_t launch_decode_sparse(const qkn_mla_dims& d, const DecodeArgs& a, hipStream_t s);
 
+// The GQA path (bf16 cache, d = 128, d_R = 64, r a multiple of 16, a multiple
+// of 32 heads per group): a paged cache of gqa_row_words(d) 16-bit words per
+// token.  With num_splits > 1 the attend writes half partials [rows, P, d]
+// and lse partials [rows, P] and merges them into o, lse.
+bool gqa_supported(const qkn_mla_dims& d);
+int gqa_row_words(const qkn_mla_dims& d);
+hipError_t launch_gqa_append(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new,
+                             const float* k_rope_new, const int32_t* seq_idx, const int32_t* pos,
+                             const int32_t* block_table, const float* w_k, const float* w_v,
+                             const float* gamma_k, const float* gamma_kr, void* kvg,
+                             int32_t* err_flag, hipStream_t s);
+hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const void* q_rope_normed,
+                             const void* kvg, const int32_t* block_table, const int32_t* seq_lens,
+                             int num_splits, void* o_part, float* lse_part, float* o, float* lse,
+                             int32_t* err_flag, hipStream_t s);
+
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);
+// The same merge for n_rows rows of row_len (a multiple of 8) entries, the
+// partials half (half_parts) or float32.
+hipError_t launch_combine_rows(int n_rows, int num_splits, int row_len, bool half_parts,
+                               const void* o_part, const float* lse_part, float* o, float* lse,
+                               hipStream_t s);
 bool append_bulk_applies(const qkn_mla_dims& d);
 hipError_t launch_append_alpha_bulk(const qkn_mla_dims& d, int32_t n_tokens, const float* c_new,
                                     const int32_t* seq_idx, const int32_t* pos,

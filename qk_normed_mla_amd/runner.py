@@ -19,6 +19,7 @@ import torch
 from . import (QKN_BF16, PAGE_SIZE, Dims, alloc_decode_workspace, cache_torch_dtype, dims_for,
                partial_torch_dtype, qkn_mla_absorb_query, qkn_mla_append, qkn_mla_combine,
                qkn_mla_combine_project, qkn_mla_decode, qkn_mla_decode_attend,
+               gqa_row_words, gqa_workspace_bytes, qkn_mla_gqa_append, qkn_mla_gqa_attend,
                qkn_mla_prefill_attend, qkn_mla_prefill_expand, qkn_mla_prefill_query)
 
 
@@ -206,6 +207,62 @@ class DecodeRunner:
                                self.kv, self.block_table, self.seq_lens, self.o_prefill,
                                self.lse_prefill, self.err_flag, stream)
 
+    # -- the GQA path: cache of per-group normed keys and values ------------------
+    def alloc_gqa(self, num_splits: int = 1, fill_word: int = 0x7E01):
+        """The GQA cache (int16 words [num_pages, 64, 2 G d + d_R], every word
+        ``fill_word`` until written), the half query, the output and, for
+        several splits, the workspace."""
+        wl, dev = self.wl, self.device
+        B, sq, H = wl.batch, wl.s_q, wl.heads
+        w = np.uint16(fill_word).view(np.int16)
+        self.kvg = torch.full((self.num_pages, PAGE_SIZE, gqa_row_words(self.dims)), int(w),
+                              dtype=torch.int16, device=dev)
+        if not hasattr(self, "q_hat"):
+            self.q_hat = torch.empty((B, sq, H, wl.head_dim), dtype=torch.float16, device=dev)
+        self.o_gqa = torch.empty((B, sq, H, wl.head_dim), dtype=torch.float32, device=dev)
+        self.lse_gqa = torch.empty((B, sq, H), dtype=torch.float32, device=dev)
+        self.set_gqa_splits(num_splits)
+
+    def set_gqa_splits(self, num_splits: int):
+        self.gqa_splits = int(num_splits)
+        self.gqa_ws = None
+        if self.gqa_splits > 1:
+            self.gqa_ws = torch.empty(gqa_workspace_bytes(self.dims, self.gqa_splits),
+                                      dtype=torch.uint8, device=self.device)
+
+    def gqa_append_tokens(self, c, kr, seq, pos, stream=None):
+        qkn_mla_gqa_append(self.dims, c, kr, seq, pos, self.block_table, self.w_k, self.w_v,
+                           self.gamma_k, self.gamma_kr, self.kvg, self.err_flag, stream)
+
+    def gqa_fill_history(self, chunk: int = 1 << 18, stream=None):
+        """GQA-append every token except the s_q newest of each sequence."""
+        rows = np.asarray(self._old_rows)
+        for s in range(0, len(rows), chunk):
+            r = rows[s:s + chunk]
+            self.gqa_append_tokens(_dev(self.inp["c"][r], self.device),
+                                   _dev(self.inp["k_rope"][r], self.device),
+                                   _dev(self._all_seq[r], self.device),
+                                   _dev(self._all_pos[r], self.device), stream)
+
+    def gqa_append_new(self, stream=None):
+        self.gqa_append_tokens(self.c_new, self.kr_new, self.new_seq, self.new_pos, stream)
+
+    def gqa_attend(self, stream=None, kvg=None):
+        qkn_mla_gqa_attend(self.dims, self.q_hat, self.q_rope_normed,
+                           self.kvg if kvg is None else kvg, self.block_table, self.seq_lens,
+                           self.gqa_splits, self.gqa_ws, self.o_gqa, self.lse_gqa, self.err_flag,
+                           stream)
+
+    def gqa_step(self, stream=None, kvg=None):
+        """One decode step of the GQA path: the query side, the append of the
+        new tokens, the attention (on ``kvg``, default the runner's cache)."""
+        kvg = self.kvg if kvg is None else kvg
+        self.prefill_query(stream)
+        qkn_mla_gqa_append(self.dims, self.c_new, self.kr_new, self.new_seq, self.new_pos,
+                           self.block_table, self.w_k, self.w_v, self.gamma_k, self.gamma_kr, kvg,
+                           self.err_flag, stream)
+        self.gqa_attend(stream, kvg)
+
     # -- host copies -------------------------------------------------------------
     def kv_words(self) -> np.ndarray:
         """Cache as raw storage words (uint16 for bf16, float32 for f32)."""
@@ -214,6 +271,6 @@ class DecodeRunner:
         return self.kv.cpu().numpy()
 
     def words(self, t: torch.Tensor) -> np.ndarray:
-        if t.dtype in (torch.bfloat16, torch.float16):
+        if t.dtype in (torch.bfloat16, torch.float16, torch.int16):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()

@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 20, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 7
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 8
     for st in (0, -1, -2, -3, -4, -5):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -280,3 +280,35 @@ def test_prefill_rejections():
     assert lib.qkn_mla_prefill_query(ctypes.byref(d), P(0x1004), *a[:6], None) == -3
     assert lib.qkn_mla_prefill_expand(ctypes.byref(d), P(0x1008), *a[:8], None, None) == -3
     assert lib.qkn_mla_prefill_attend(ctypes.byref(d), *a[:8], P(0x1004), None, None) == -3
+
+
+def test_gqa_rejections():
+    """The GQA-path calls check their arguments before any launch: the dims
+    they take (bf16 latent dtype, d = 128, d_R = 64, r a multiple of 16, a
+    multiple of 32 heads per group), null pointers, misalignment, split counts
+    and the workspace of a split attention."""
+    lib = Q.library()
+    P = ctypes.c_void_p
+    a = [P(0x1000)] * 12
+    d = good_dims(s_q=4)
+    for bad in (good_dims(cache_dtype="f32"), good_dims(head_dim=64), good_dims(heads=48, groups=1),
+                good_dims(rank=72)):
+        assert lib.qkn_mla_gqa_append(ctypes.byref(bad), 4, *a[:10], None, None) == -2
+        assert lib.qkn_mla_gqa_attend(ctypes.byref(bad), *a[:5], 1, None, 0, *a[:2], None,
+                                      None) == -2
+    assert lib.qkn_mla_gqa_append(ctypes.byref(d), 0, *[None] * 10, None, None) == 0  # nothing to do
+    assert lib.qkn_mla_gqa_append(ctypes.byref(d), -1, *a[:10], None, None) == -1
+    assert lib.qkn_mla_gqa_append(ctypes.byref(d), 4, *a[:9], None, None, None) == -1
+    assert lib.qkn_mla_gqa_append(ctypes.byref(d), 4, P(0x1008), *a[:9], None, None) == -3
+    ws = lib.qkn_mla_gqa_workspace_bytes(ctypes.byref(d), 3)
+    rows = d.batch * d.s_q * d.heads * 3
+    assert ws >= rows * d.head_dim * 2 + rows * 4 and ws % 256 == 0
+    assert lib.qkn_mla_gqa_workspace_bytes(ctypes.byref(d), 0) == 0
+    attend = lambda P_, w, nb, q=P(0x1000): lib.qkn_mla_gqa_attend(  # noqa: E731
+        ctypes.byref(d), q, *a[:4], P_, w, nb, *a[:2], None, None)
+    assert attend(0, None, 0) == -1
+    assert attend(3, None, 0) == -1                          # no workspace
+    assert attend(3, P(0x1000), ws - 1) == -1                # too small
+    assert attend(3, P(0x1010), ws) == -3                    # not 256-byte aligned
+    assert attend(1, None, 0, q=None) == -1
+    assert attend(1, None, 0, q=P(0x1004)) == -3
