@@ -703,6 +703,49 @@ def profile_run(Q, W, torch, name, launches):
                       "replicas": n_rep}), flush=True)
 
 
+def profile_gqa_run(Q, W, torch, name, launches):
+    """Only `launches` eager GQA-path steps (query side, append of the new
+    tokens, attention and combine) of one workload over rotating replicas of
+    its cache, after one warm-up step."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, seed=0)
+    splits = gqa_splits(wl, inp["seq_lens"])
+    r = DecodeRunner(wl, inp)
+    r.alloc_gqa(splits)
+    r.gqa_fill_history()
+    del r.kv, r.alpha_k
+    n_rep = max(2, math.ceil(MIN_ROTATION_BYTES / (r.kvg.numel() * 2)) + 1)
+    kvgs = [r.kvg] + [r.kvg.clone() for _ in range(n_rep - 1)]
+    torch.cuda.synchronize()
+    for k in range(launches + 1):
+        r.gqa_step(kvg=kvgs[k % n_rep])
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": f"gqa {name}", "num_splits": splits, "launches": launches + 1,
+                      "replicas": n_rep}), flush=True)
+
+
+def profile_prefill_run(Q, W, torch, launches):
+    """Only `launches` eager prefill passes (query side, expansion, attention)
+    of the chunked-prefill workload, after one warm-up pass."""
+    from qk_normed_mla_amd.runner import DecodeRunner
+
+    wl = W.WORKLOADS["prefill"]
+    inp = W.make_inputs(wl, seed=0)
+    r = DecodeRunner(wl, inp)
+    r.fill_history()
+    r.append_new()
+    r.alloc_prefill()
+    torch.cuda.synchronize()
+    for _ in range(launches + 1):
+        r.prefill_query()
+        r.prefill_expand()
+        r.prefill_attend()
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": "prefill", "launches": launches + 1}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -717,6 +760,9 @@ def main():
     ap.add_argument("--profile", type=int, default=0, metavar="N",
                     help="only run N + 1 eager decode + combine calls of --workload (the "
                          "program rocprofv3 profiles) and exit")
+    ap.add_argument("--profile-path", default="decode", choices=("decode", "gqa", "prefill"),
+                    help="what --profile runs: the latent decode + combine, the GQA-path step "
+                         "or the chunked prefill")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -745,7 +791,12 @@ def main():
     torch.cuda.set_device(0)
     Q.library()
     if args.profile:
-        profile_run(Q, W, torch, args.workload, args.profile)
+        if args.profile_path == "gqa":
+            profile_gqa_run(Q, W, torch, args.workload, args.profile)
+        elif args.profile_path == "prefill":
+            profile_prefill_run(Q, W, torch, args.profile)
+        else:
+            profile_run(Q, W, torch, args.workload, args.profile)
         return
     timer = Timer(torch)
 

@@ -255,20 +255,25 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GQA-path append: one block per (32 new tokens, group, keys | values); wave w
-// computes columns 32 w .. 32 w + 31 of the 32 tokens' projections (d = 128).
-// A operand: the latent rounded to bf16 (the latent cache's stored words, an
-// exact operand); B: W_g columns read from global memory 8 rows per lane and
-// split into three bf16 words (hi + mid + lo, exact to 2^-24), so every
-// product is exact and the sums are float32.  Keys: the block sums the squares
-// of each token's 128 entries (per wave over its 32 lanes, then over the 4
-// waves in LDS) for 1 / RMS; the key blocks of group 0 also write the normed,
-// rotated RoPE key.  Tokens with an out-of-range sequence, position or page are
-// skipped and reported.
+// GQA-path append: one block of 16 waves per (32 new tokens, group, keys |
+// values).  Wave w computes the 32 x 32 tile of columns 32 (w % 4) .. + 31
+// over the latent rows of its quarter of the rank (16-row steps w / 4, w / 4 +
+// 4, ...), with every load of its steps issued before its products; the four
+// quarters' partial tiles are summed through LDS in a fixed order.  A operand:
+// the latent rounded to bf16 (the latent cache's stored words, an exact
+// operand); B: W_g columns read 8 rows per lane and split into three bf16
+// words (hi + mid + lo, exact to 2^-24), so every product is exact and the
+// sums are float32.  Keys: the sums of squares of each token's 128 entries
+// (per wave over its 32 lanes, then over the 4 column tiles in LDS) give
+// 1 / RMS; the key blocks of group 0 also write the normed, rotated RoPE key.
+// Tokens with an out-of-range sequence, position or page are skipped and
+// reported.
 // ---------------------------------------------------------------------------
 constexpr int GA_D = 128, GA_DR = 64;
+constexpr int GA_WAVES = 16;
+constexpr int GA_MAX_STEPS = 4;  // 16-row steps of a wave whose loads are in flight together
 
-__global__ __launch_bounds__(256) void gqa_append_kernel(
+__global__ __launch_bounds__(64 * GA_WAVES) void gqa_append_kernel(
     const float* __restrict__ c_new, const float* __restrict__ k_rope_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ block_table, const float* __restrict__ w_k,
@@ -276,12 +281,14 @@ __global__ __launch_bounds__(256) void gqa_append_kernel(
     const float* __restrict__ gamma_kr, uint16_t* __restrict__ kvg, int32_t* __restrict__ err_flag,
     int n_tokens, int batch, int groups, int rank, int max_pages, int num_pages, float eps,
     float theta) {
+  __shared__ f32x4 part[3][4][4][64];  // partial tiles of quarters 1..3: [q - 1][ct][r / 4][lane]
   __shared__ float ssq[4][32];
   __shared__ int slot_of[32];
   __shared__ int pos_of[32];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int ct = w & 3, quarter = w >> 2;
   const int n0 = blockIdx.x * 32;
   const int g = blockIdx.y;
   const bool values = blockIdx.z == 1;
@@ -302,70 +309,96 @@ __global__ __launch_bounds__(256) void gqa_append_kernel(
     pos_of[tid] = p;
   }
 
-  // ---- the 32 x 32 tile of this wave: tokens n0 + i, columns 32 w + j ----
+  // ---- this wave's partial tile: tokens n0 + i, columns 32 ct + j ----
   const int tok = n0 + l32;
   const bool tok_ok = tok < n_tokens;
   const float* crow = c_new + (size_t)(tok_ok ? tok : 0) * rank + 8 * hh;
-  const float* wcol = (values ? w_v : w_k) + (size_t)g * rank * GA_D + (size_t)(8 * hh) * GA_D + 32 * w + l32;
+  const float* wcol = (values ? w_v : w_k) + (size_t)g * rank * GA_D + (size_t)(8 * hh) * GA_D + 32 * ct + l32;
+  const int steps = rank / 16;
   f32x16 acc = {};
-#pragma unroll 4
-  for (int k0 = 0; k0 < rank; k0 += 16) {
-    const float4 c0 = tok_ok ? *reinterpret_cast<const float4*>(crow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 c1 = tok_ok ? *reinterpret_cast<const float4*>(crow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float wv[8];
+  for (int s0 = quarter; s0 < steps; s0 += 4 * GA_MAX_STEPS) {
+    float4 cv[GA_MAX_STEPS][2];
+    float wv[GA_MAX_STEPS][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wv[j] = wcol[(size_t)(k0 + j) * GA_D];
-    const f32x8 cx = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const bf16x8 a = __builtin_convertvector(cx, bf16x8);  // nearest-even, as the latent cache stores it
-    bf16x4 h0, m0, lo0, h1, m1, lo1;
-    split3(make_float4(wv[0], wv[1], wv[2], wv[3]), h0, m0, lo0);
-    split3(make_float4(wv[4], wv[5], wv[6], wv[7]), h1, m1, lo1);
-    acc = mfma(a, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
-    acc = mfma(a, __builtin_shufflevector(m0, m1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
-    acc = mfma(a, __builtin_shufflevector(lo0, lo1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    for (int u = 0; u < GA_MAX_STEPS; ++u) {
+      const int st = s0 + 4 * u;
+      const bool live = st < steps;
+      const int k0 = 16 * (live ? st : 0);
+      cv[u][0] = tok_ok && live ? *reinterpret_cast<const float4*>(crow + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      cv[u][1] = tok_ok && live ? *reinterpret_cast<const float4*>(crow + k0 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[u][j] = live ? wcol[(size_t)(k0 + j) * GA_D] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < GA_MAX_STEPS; ++u) {
+      const f32x8 cx = {cv[u][0].x, cv[u][0].y, cv[u][0].z, cv[u][0].w,
+                        cv[u][1].x, cv[u][1].y, cv[u][1].z, cv[u][1].w};
+      const bf16x8 a = __builtin_convertvector(cx, bf16x8);  // nearest-even, as the latent cache stores it
+      bf16x4 h0, m0, lo0, h1, m1, lo1;
+      split3(make_float4(wv[u][0], wv[u][1], wv[u][2], wv[u][3]), h0, m0, lo0);
+      split3(make_float4(wv[u][4], wv[u][5], wv[u][6], wv[u][7]), h1, m1, lo1);
+      acc = mfma(a, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+      acc = mfma(a, __builtin_shufflevector(m0, m1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+      acc = mfma(a, __builtin_shufflevector(lo0, lo1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    }
+  }
+  if (quarter > 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      part[quarter - 1][ct][q][lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+  }
+  __syncthreads();  // slot_of, pos_of and the partial tiles
+  const bool owner = quarter == 0;  // the wave that finishes column tile ct
+  if (owner) {
+#pragma unroll
+    for (int qt = 0; qt < 3; ++qt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 p = part[qt][ct][q][lane];
+        acc[4 * q] += p[0];
+        acc[4 * q + 1] += p[1];
+        acc[4 * q + 2] += p[2];
+        acc[4 * q + 3] += p[3];
+      }
+    }
   }
 
-  // acc[r]: token i = r % 4 + 8 (r / 4) + 4 hh of the tile, column 32 w + l32
-  float scl[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) scl[r] = 1.f;
-  if (!values) {
+  // acc[r]: token i = r % 4 + 8 (r / 4) + 4 hh of the tile, column 32 ct + l32
+  if (owner && !values) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float q = acc[r] * acc[r];
 #pragma unroll
       for (int m = 1; m < 32; m <<= 1) q += __shfl_xor(q, m, 32);
-      if (l32 == 0) ssq[w][(r & 3) + 8 * (r >> 2) + 4 * hh] = q;
+      if (l32 == 0) ssq[ct][(r & 3) + 8 * (r >> 2) + 4 * hh] = q;
     }
   }
-  __syncthreads();  // slot_of, pos_of and the partial sums of squares
-  const int col = 32 * w + l32;
-  const float gk = values ? 1.f : gamma_k[(size_t)g * GA_D + col];
-  if (!values) {
+  __syncthreads();  // the column tiles' sums of squares
+  if (owner) {
+    const int col = 32 * ct + l32;
+    const float gk = values ? 1.f : gamma_k[(size_t)g * GA_D + col];
+    float big = 0.f;
+    const int part_off = 2 * GA_D * g + (values ? GA_D : 0) + col;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = (r & 3) + 8 * (r >> 2) + 4 * hh;
-      const float ss = (ssq[0][i] + ssq[1][i]) + (ssq[2][i] + ssq[3][i]);
-      scl[r] = 1.0f / sqrtf(ss / (float)GA_D + eps);
+      const int slot = slot_of[i];
+      if (slot < 0) continue;
+      float x = acc[r];
+      if (!values) {
+        const float ss = (ssq[0][i] + ssq[1][i]) + (ssq[2][i] + ssq[3][i]);
+        x = x * (1.0f / sqrtf(ss / (float)GA_D + eps)) * gk;
+      }
+      big = fmaxf(big, fabsf(x));
+      const _Float16 hx = static_cast<_Float16>(x);
+      kvg[(size_t)slot * row_words + part_off] = __builtin_bit_cast(uint16_t, hx);
     }
+    if (big >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
   }
-  float big = 0.f;
-  const int part = 2 * GA_D * g + (values ? GA_D : 0) + col;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = (r & 3) + 8 * (r >> 2) + 4 * hh;
-    const int slot = slot_of[i];
-    if (slot < 0) continue;
-    const float x = values ? acc[r] : acc[r] * scl[r] * gk;
-    big = fmaxf(big, fabsf(x));
-    const _Float16 hx = static_cast<_Float16>(x);
-    kvg[(size_t)slot * row_words + part] = __builtin_bit_cast(uint16_t, hx);
-  }
-  if (big >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
 
-  // ---- the RoPE key (key blocks of group 0): wave w takes tokens w, w + 4, ... ----
+  // ---- the RoPE key (key blocks of group 0): wave w takes tokens w, w + 16 ----
   if (values || g != 0) return;
-  for (int i = w; i < 32; i += 4) {
+  for (int i = w; i < 32; i += GA_WAVES) {
     const int slot = slot_of[i];
     if (slot < 0) continue;  // uniform over the wave
     const float x = k_rope_new[(size_t)(n0 + i) * GA_DR + lane];
@@ -415,6 +448,10 @@ __device__ __forceinline__ float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// Word 3 of a raw buffer descriptor on gfx950 (32-bit data format; offsets
+// at or past the size field read as zero).
+constexpr int kRsrcWord3 = 0x00020000;
 
 struct AttendArgs {
   const _Float16* q_hat;
@@ -488,41 +525,63 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
 #pragma unroll
   for (int kk = 0; kk < AT_DR / 16; ++kk)
     qrb[kk] = *reinterpret_cast<const bf16x8*>(A.q_rope + qrow * AT_DR + 16 * kk + 8 * hh);
+  // the queries are in registers before the tile loop: otherwise the wait for
+  // them inside the loop would also wait for the next tile's loads
+#pragma unroll
+  for (int kk = 0; kk < AT_D / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+#pragma unroll
+  for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
 
   // tile loads: thread e < 512 of K^ / V takes row e / 16, chunk e % 16 (two
-  // each); thread e < 256 of K^R row e / 8, chunk e % 8
+  // each); thread e < 256 of K^R row e / 8, chunk e % 8.  Buffer loads
+  // through a descriptor per tile whose size ends at the last visible row (a
+  // bad page: size 0), so rows past it read as zeros with no branch.
   uint4 nk[2], nv[2], nr;
+  // a 32-key tile lies in one 64-token page; the page of the next tile is
+  // loaded with this tile's loads, a tile ahead of its use
+  const int32_t* pages = A.block_table + (size_t)b * max_pages;
+  int pg_next = kt_lo < kt_hi ? pages[kt_lo * AT_KEYS / QKN_MLA_PAGE_SIZE] : 0;
   auto fetch = [&](int kt) {
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    // a 32-key tile lies in one 64-token page
-    const int pg = A.block_table[(size_t)b * max_pages + kt * AT_KEYS / QKN_MLA_PAGE_SIZE];
+    const int pg = __builtin_amdgcn_readfirstlane(pg_next);
     const bool page_ok = pg >= 0 && pg < A.num_pages;
+    if (!page_ok) err = 1;
+    const int nvalid = min(AT_KEYS, vis_max - kt * AT_KEYS);
     const size_t row0 = (size_t)(page_ok ? pg : 0) * QKN_MLA_PAGE_SIZE + kt * AT_KEYS % QKN_MLA_PAGE_SIZE;
+    if (GQA) {
+      const uint32_t rb = 2u * A.row_words;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(A.kvg + row0 * A.row_words), 0, page_ok ? nvalid * rb : 0, kRsrcWord3);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
-      const int t = kt * AT_KEYS + rr;
-      if (GQA) {
-        const uint16_t* p = A.kvg + (row0 + rr) * A.row_words + 2 * AT_D * g + 8 * c;
-        nk[u] = t < vis_max && page_ok ? *reinterpret_cast<const uint4*>(p) : z;
-        nv[u] = t < vis_max && page_ok ? *reinterpret_cast<const uint4*>(p + AT_D) : z;
-      } else {
-        const size_t at = (((size_t)b * A.max_T + t) * groups + g) * AT_D + 8 * c;
-        nk[u] = t < vis_max ? *reinterpret_cast<const uint4*>(A.k_hat + at) : z;
-        nv[u] = t < vis_max ? *reinterpret_cast<const uint4*>(A.v + at) : z;
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
+        const uint32_t off = rr * rb + 4u * AT_D * g + 16u * c;
+        nk[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        nv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 2u * AT_D, 0, 0));
       }
-    }
-    const int rr = tid >> 3, c = tid & 7;
-    const int t = kt * AT_KEYS + rr;
-    nr = z;
-    if (t < vis_max) {
-      if (page_ok) {
-        nr = GQA ? *reinterpret_cast<const uint4*>(A.kvg + (row0 + rr) * A.row_words + 2 * AT_D * groups + 8 * c)
-                 : *reinterpret_cast<const uint4*>(A.kv + (row0 + rr) * (A.rank + AT_DR) + A.rank + 8 * c);
-      } else {
-        err = 1;
+      const int rr = tid >> 3, c = tid & 7;
+      nr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs, rr * rb + 4u * AT_D * groups + 16u * c, 0, 0));
+    } else {
+      const uint32_t stride = 2u * AT_D * groups;
+      const size_t first = ((size_t)b * A.max_T + kt * AT_KEYS) * groups + g;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(A.k_hat + first * AT_D), 0, nvalid * stride, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(A.v + first * AT_D), 0, nvalid * stride, kRsrcWord3);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
+        nk[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, rr * stride + 16u * c, 0, 0));
+        nv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, rr * stride + 16u * c, 0, 0));
       }
+      const uint32_t rb = 2u * (A.rank + AT_DR);
+      const __amdgpu_buffer_rsrc_t rr_ = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(A.kv + row0 * (A.rank + AT_DR)), 0, page_ok ? nvalid * rb : 0, kRsrcWord3);
+      const int rr = tid >> 3, c = tid & 7;
+      nr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rr_, rr * rb + 2u * A.rank + 16u * c, 0, 0));
     }
+    if (kt + 1 < kt_hi) pg_next = pages[(kt + 1) * AT_KEYS / QKN_MLA_PAGE_SIZE];
   };
   auto stash = [&](int kt) {
     uint8_t* buf = smem + (kt & 1) * AT_TILE;
@@ -668,6 +727,58 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   if (err && A.err_flag && lane == 0) atomicOr(A.err_flag, QKN_FLAG_INDEX);
 }
 
+// ---------------------------------------------------------------------------
+// combine of the GQA path's half partials (rows of d = 128): 16 lanes per row,
+// 4 rows per wave.  M = max_p lse_p, lse = M + ln sum_p e^{lse_p - M},
+// o = sum_p e^{lse_p - lse} o_p; every split empty gives o = 0, lse = -inf.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16* __restrict__ o_part,
+                                                          const float* __restrict__ lse_part,
+                                                          float* __restrict__ o, float* __restrict__ lse,
+                                                          int n_rows, int num_splits) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int row = (blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  if (row >= n_rows) return;  // whole 16-lane groups
+  const float* lp = lse_part + (size_t)row * num_splits;
+  float M = -INFINITY;
+  for (int p = l16; p < num_splits; p += 16) M = fmaxf(M, lp[p]);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 16));
+  float* out = o + (size_t)row * AT_D + 8 * l16;
+  if (M == -INFINITY) {
+    *reinterpret_cast<float4*>(out) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (l16 == 0) lse[row] = -INFINITY;
+    return;
+  }
+  float sum = 0.f;
+  for (int p = l16; p < num_splits; p += 16) sum += expf(lp[p] - M);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m, 16);
+  const float L = M + logf(sum);
+  if (l16 == 0) lse[row] = L;
+  const _Float16* op = o_part + (size_t)row * num_splits * AT_D + 8 * l16;
+  float acc[8] = {};
+  for (int p0 = 0; p0 < num_splits; p0 += 4) {
+    f16x8 v[4];
+    float wgt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u;
+      const float l = p < num_splits ? lp[p] : -INFINITY;
+      wgt[u] = l == -INFINITY ? 0.f : expf(l - L);
+      v[u] = p < num_splits ? *reinterpret_cast<const f16x8*>(op + (size_t)p * AT_D) : f16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt[u], static_cast<float>(v[u][j]), acc[j]);
+  }
+  *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 template <int NT>
 hipError_t launch_expand_nt(const qkn_mla_dims& d, const void* kv, const float* alpha_k,
                             const int32_t* block_table, const int32_t* seq_lens, const float* w_k,
@@ -766,7 +877,7 @@ hipError_t launch_gqa_append(const qkn_mla_dims& d, int32_t n_tokens, const floa
                              const int32_t* block_table, const float* w_k, const float* w_v,
                              const float* gamma_k, const float* gamma_kr, void* kvg,
                              int32_t* err_flag, hipStream_t s) {
-  hipLaunchKernelGGL(gqa_append_kernel, dim3(cdiv(n_tokens, 32), d.groups, 2), dim3(256), 0, s, c_new,
+  hipLaunchKernelGGL(gqa_append_kernel, dim3(cdiv(n_tokens, 32), d.groups, 2), dim3(64 * GA_WAVES), 0, s, c_new,
                      k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
                      static_cast<uint16_t*>(kvg), err_flag, n_tokens, d.batch, d.groups, d.rank,
                      d.max_pages_per_seq, d.num_pages, d.eps, d.rope_theta);
@@ -803,8 +914,10 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
                      dim3(d.batch * num_splits * A.token_groups * A.head_groups), dim3(256), 0, s, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || num_splits == 1) return e;
-  return launch_combine_rows(d.batch * d.s_q * d.heads, num_splits, AT_D, true, o_part, lse_part, o,
-                             lse, s);
+  const int rows = d.batch * d.s_q * d.heads;
+  hipLaunchKernelGGL(gqa_combine_kernel, dim3(cdiv(rows, 16)), dim3(256), 0, s,
+                     static_cast<const _Float16*>(o_part), lse_part, o, lse, rows, num_splits);
+  return hipGetLastError();
 }
 
 }  // namespace qkn
