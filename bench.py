@@ -112,10 +112,12 @@ def gqa_splits(wl, seq_lens, cus=256):
     attention + combine time.  Cost model, in units of one 32-key tile of one
     workgroup: a workgroup costs GQA_WG_FIXED (loading its queries, writing its
     output) plus its tiles; the workgroups are dealt as the kernel numbers them
-    (XCD x takes the x-th eighth of the logical ids, each XCD's CUs taking them
-    in order as they free up); the combine costs its half partials, written and
-    read back, at about 6 TB/s."""
-    GQA_WG_FIXED, TILE_US = 4.0, 0.6
+    (XCD x takes the x-th eighth of the logical ids, its 32 CUs running two
+    workgroups each and taking the next as one frees up); the combine costs its
+    half partials, written and read back, at about 3 TB/s.  The constants are
+    fitted to measured attention times of the mtp, dsv3 and grouped workloads
+    at several split counts."""
+    GQA_WG_FIXED, TILE_US, SLOTS = 8.0, 1.26, 2
     tpw = 4
     while tpw > 1 and tpw // 2 >= wl.s_q and (wl.heads // wl.groups // 32) % (8 // tpw) == 0:
         tpw //= 2
@@ -133,11 +135,11 @@ def gqa_splits(wl, seq_lens, cus=256):
         per_xcd = math.ceil(len(flat) / 8)
         makespan = 0.0
         for x in range(8):
-            loads = [0.0] * (cus // 8)
+            loads = [0.0] * (SLOTS * cus // 8)
             for c in flat[x * per_xcd:(x + 1) * per_xcd]:
                 heapq.heappush(loads, heapq.heappop(loads) + c)
             makespan = max(makespan, max(loads))
-        t = makespan * TILE_US + (rows * P * wl.head_dim * 2 * 2 / 6e12 * 1e6 if P > 1 else 0.0)
+        t = makespan * TILE_US + (rows * P * wl.head_dim * 2 * 2 / 3e12 * 1e6 if P > 1 else 0.0)
         if best is None or t < best[0] - 1e-9:
             best = (t, P)
     return best[1]

@@ -6,7 +6,8 @@
 // Chunked prefill.  A chunk of s_q new query tokens per sequence attends
 // causally to its whole cache, the chunk included (its tokens appended first):
 //   prefill_query:  q^ = gamma_q * q / RMS(q) per head (IEEE half), and the
-//                   normed, rotated RoPE query (bf16, as the absorb call's).
+//                   normed, rotated RoPE query (bf16, as the absorb call's);
+//                   also the query side of the GQA path.
 //   prefill_expand: for every cached token and KV group, k^ = gamma_k *
 //                   (c W^K_g) * alpha^k (the stored inverse RMS of that same
 //                   projection of the stored latent) and v = c W^V_g, as IEEE
@@ -58,43 +59,53 @@ __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------
-// query side: one wave per query row (b, i, h)
+// query side: one block per (query token (b, i), 16 heads), d = 128, d_R = 64.
+// The RoPE angles depend on the position alone, so the block forms the 32
+// cos / sin pairs once; each wave then takes 4 of the heads, all their loads
+// in flight: q^ = gamma_q q / RMS(q) as half, the RoPE query normed, rotated
+// and rounded to bf16.
 // ---------------------------------------------------------------------------
+constexpr int PQ_D = 128, PQ_DR = 64, PQ_ROWS = 4;
+
 __global__ __launch_bounds__(256) void prefill_query_kernel(
     const float* __restrict__ q, const float* __restrict__ q_rope, const int32_t* __restrict__ q_pos,
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_qr,
-    _Float16* __restrict__ q_hat, uint16_t* __restrict__ qr_out, int rows, int heads,
-    int head_dim, int rope_dim, float eps, float theta) {
-  const int lane = threadIdx.x & 63;
-  const int half = rope_dim / 2;
-  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
-    float x[4];
-    float ss = 0.f;
+    _Float16* __restrict__ q_hat, uint16_t* __restrict__ qr_out, int heads, float eps, float theta) {
+  __shared__ float cs[PQ_DR / 2], sn[PQ_DR / 2];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int token = blockIdx.x / (heads / 16);
+  const int hb = 16 * (blockIdx.x % (heads / 16)) + w;  // this wave's heads: hb + 4 u
+  if (threadIdx.x < PQ_DR / 2) {
+    float c = 1.f, s = 0.f;
+    if (theta != 0.f) rope_cos_sin<false>(q_pos[token], threadIdx.x, PQ_DR, theta, &c, &s);
+    cs[threadIdx.x] = c;
+    sn[threadIdx.x] = s;
+  }
+  const float g0 = gamma_q[lane], g1 = gamma_q[lane + 64], gr = gamma_qr[lane];
+  __syncthreads();
+  const float c = cs[lane & 31], s = sn[lane & 31];
+  float x0[PQ_ROWS], x1[PQ_ROWS], xr[PQ_ROWS];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int j = lane + 64 * k;
-      x[k] = j < head_dim ? q[(size_t)row * head_dim + j] : 0.f;
-      ss = fmaf(x[k], x[k], ss);
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)head_dim + eps);
+  for (int u = 0; u < PQ_ROWS; ++u) {
+    const size_t row = (size_t)token * heads + hb + 4 * u;
+    x0[u] = q[row * PQ_D + lane];
+    x1[u] = q[row * PQ_D + 64 + lane];
+    xr[u] = q_rope[row * PQ_DR + lane];
+  }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int j = lane + 64 * k;
-      if (j < head_dim) q_hat[(size_t)row * head_dim + j] = static_cast<_Float16>(x[k] * inv * gamma_q[j]);
-    }
-    if (rope_dim == 0) continue;
-    const float x1 = lane < half ? q_rope[(size_t)row * rope_dim + lane] : 0.f;
-    const float x2 = lane < half ? q_rope[(size_t)row * rope_dim + lane + half] : 0.f;
-    const float sr = wave_sum(fmaf(x1, x1, x2 * x2));
-    const float ir = 1.0f / sqrtf(sr / (float)rope_dim + eps);
-    if (lane < half) {
-      float c = 1.f, s = 0.f;
-      if (theta != 0.f) rope_cos_sin<false>(q_pos[row / heads], lane, rope_dim, theta, &c, &s);
-      const float y1 = x1 * ir * gamma_qr[lane], y2 = x2 * ir * gamma_qr[lane + half];
-      qr_out[(size_t)row * rope_dim + lane] = f32_to_bf16(y1 * c - y2 * s);
-      qr_out[(size_t)row * rope_dim + lane + half] = f32_to_bf16(y2 * c + y1 * s);
-    }
+  for (int u = 0; u < PQ_ROWS; ++u) {
+    const size_t row = (size_t)token * heads + hb + 4 * u;
+    const float ss = wave_sum(fmaf(x1[u], x1[u], x0[u] * x0[u]));
+    const float inv = 1.0f / sqrtf(ss / (float)PQ_D + eps);
+    q_hat[row * PQ_D + lane] = static_cast<_Float16>(x0[u] * inv * g0);
+    q_hat[row * PQ_D + 64 + lane] = static_cast<_Float16>(x1[u] * inv * g1);
+    const float sr = wave_sum(xr[u] * xr[u]);
+    const float ir = 1.0f / sqrtf(sr / (float)PQ_DR + eps);
+    const float y = xr[u] * ir * gr;
+    const float other = __shfl_xor(y, 32);  // the pair partner j +- d_R / 2
+    // first half: y1 c - y2 s; second half: y2 c + y1 s
+    const float out = lane < 32 ? y * c - other * s : y * c + other * s;
+    qr_out[row * PQ_DR + lane] = f32_to_bf16(out);
   }
 }
 
@@ -819,11 +830,10 @@ bool prefill_supported(const qkn_mla_dims& d) {
 hipError_t launch_prefill_query(const qkn_mla_dims& d, const float* q, const float* q_rope,
                                 const int32_t* q_pos, const float* gamma_q, const float* gamma_qr,
                                 void* q_hat, void* q_rope_normed, hipStream_t s) {
-  const int rows = d.batch * d.s_q * d.heads;
-  const int blocks = std::min(cdiv(rows, 4), 4096);
-  hipLaunchKernelGGL(prefill_query_kernel, dim3(blocks), dim3(256), 0, s, q, q_rope, q_pos, gamma_q,
-                     gamma_qr, static_cast<_Float16*>(q_hat), static_cast<uint16_t*>(q_rope_normed),
-                     rows, d.heads, d.head_dim, d.rope_dim, d.eps, d.rope_theta);
+  hipLaunchKernelGGL(prefill_query_kernel, dim3(d.batch * d.s_q * (d.heads / 16)), dim3(256), 0, s,
+                     q, q_rope, q_pos,
+                     gamma_q, gamma_qr, static_cast<_Float16*>(q_hat),
+                     static_cast<uint16_t*>(q_rope_normed), d.heads, d.eps, d.rope_theta);
   return hipGetLastError();
 }
 
