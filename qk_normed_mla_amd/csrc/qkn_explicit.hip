@@ -440,8 +440,8 @@ __global__ __launch_bounds__(64 * GA_WAVES) void gqa_append_kernel(
 //     normaliser summed from the same rounded values),
 //   O^T[128 x 32 heads] += V^T P^T (8 products; V^T read with
 //     ds_read_b64_tr_b16 from the row-major tile).
-// Rows of 256 bytes store chunk c of key t at chunk c ^ (t mod 16) (RoPE rows:
-// c ^ (t mod 8)), so the column reads of 32 rows spread over the banks.
+// Rows of 256 bytes store chunk c of key t at chunk c ^ kswz(t) (RoPE rows:
+// c ^ rswz(t)), so the column reads of 32 rows spread over the banks.
 // ---------------------------------------------------------------------------
 constexpr int AT_D = 128, AT_DR = 64, AT_R = 512;
 constexpr int AT_KEYS = 32;
@@ -463,6 +463,19 @@ __device__ __forceinline__ float pair_sum(float v) {
 // Word 3 of a raw buffer descriptor on gfx950 (32-bit data format; offsets
 // at or past the size field read as zero).
 constexpr int kRsrcWord3 = 0x00020000;
+
+typedef const __attribute__((address_space(4))) int32_t ConstI32;  // read through the scalar cache
+
+// Chunk swizzles for the 64 four-byte LDS banks.  Chunk c of a 256-byte key
+// or value row t is stored at c ^ kswz(t): kswz is a bijection on 16 rows (so
+// the 16-byte reads of 16 rows at one chunk, the QK operand, meet 64 banks)
+// whose rows 4k .. 4k + 3 differ in bits 2-3 (so the 8-byte transposed reads
+// of 4 rows at 4 neighbouring chunks, the PV operand, do too).  Chunk c of a
+// 128-byte RoPE row t is stored at c ^ rswz(t): rows 2j and 2j + 1 fall on the
+// two halves of the banks, so rswz must differ over the even (and the odd)
+// rows of 16.
+__device__ __forceinline__ int kswz(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
+__device__ __forceinline__ int rswz(int t) { return (t >> 1) & 7; }
 
 struct AttendArgs {
   const _Float16* q_hat;
@@ -548,12 +561,15 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   // through a descriptor per tile whose size ends at the last visible row (a
   // bad page: size 0), so rows past it read as zeros with no branch.
   uint4 nk[2], nv[2], nr;
-  // a 32-key tile lies in one 64-token page; the page of the next tile is
-  // loaded with this tile's loads, a tile ahead of its use
-  const int32_t* pages = A.block_table + (size_t)b * max_pages;
+  // a 32-key tile lies in one 64-token page.  The block table is read through
+  // the scalar (constant) cache: it does not change during the kernel, and a
+  // scalar load does not count among the vector loads the tile waits on.  The
+  // page of the next tile is loaded a tile ahead.
+  const ConstI32* pages = (const ConstI32*)(A.block_table) + (size_t)b * max_pages;
   int pg_next = kt_lo < kt_hi ? pages[kt_lo * AT_KEYS / QKN_MLA_PAGE_SIZE] : 0;
   auto fetch = [&](int kt) {
-    const int pg = __builtin_amdgcn_readfirstlane(pg_next);
+    const int pg = pg_next;
+    if (kt + 1 < kt_hi) pg_next = pages[(kt + 1) * AT_KEYS / QKN_MLA_PAGE_SIZE];
     const bool page_ok = pg >= 0 && pg < A.num_pages;
     if (!page_ok) err = 1;
     const int nvalid = min(AT_KEYS, vis_max - kt * AT_KEYS);
@@ -592,19 +608,18 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
       nr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                          rr_, rr * rb + 2u * A.rank + 16u * c, 0, 0));
     }
-    if (kt + 1 < kt_hi) pg_next = pages[(kt + 1) * AT_KEYS / QKN_MLA_PAGE_SIZE];
   };
   auto stash = [&](int kt) {
     uint8_t* buf = smem + (kt & 1) * AT_TILE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
-      const int at = rr * 256 + ((c ^ (rr & 15)) << 4);
+      const int at = rr * 256 + ((c ^ kswz(rr)) << 4);
       *reinterpret_cast<uint4*>(buf + at) = nk[u];
       *reinterpret_cast<uint4*>(buf + AT_K_BYTES + AT_R_BYTES + at) = nv[u];
     }
     const int rr = tid >> 3, c = tid & 7;
-    *reinterpret_cast<uint4*>(buf + AT_K_BYTES + rr * 128 + ((c ^ (rr & 7)) << 4)) = nr;
+    *reinterpret_cast<uint4*>(buf + AT_K_BYTES + rr * 128 + ((c ^ rswz(rr)) << 4)) = nr;
   };
 
   // per-lane read offsets.  QK: key row l32, chunk 2 kk + hh.  PV (V^T, the
@@ -613,9 +628,9 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   // byte 8 (l16 % 2); rows + 16 ks.
   const int l16 = lane & 15, G16 = (lane >> 4) & 1;
   const int t0 = 4 * hh + (l16 >> 2), c_lo = 2 * G16 + ((l16 & 3) >> 1);
-  const uint32_t pv0 = static_cast<uint32_t>(t0 * 256 + 8 * (l16 & 1) + ((c_lo ^ (t0 & 15)) << 4));
+  const uint32_t pv0 = static_cast<uint32_t>(t0 * 256 + 8 * (l16 & 1) + ((c_lo ^ kswz(t0)) << 4));
   const uint32_t pv1 =
-      static_cast<uint32_t>((t0 + 8) * 256 + 8 * (l16 & 1) + ((c_lo ^ ((t0 + 8) & 15)) << 4));
+      static_cast<uint32_t>((t0 + 8) * 256 + 8 * (l16 & 1) + ((c_lo ^ kswz(t0 + 8)) << 4));
 
   f32x16 acc[AT_D / 32];
 #pragma unroll
@@ -638,24 +653,26 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
 #pragma unroll
       for (int kk = 0; kk < AT_D / 16; ++kk) {
         const f16x8 a = *reinterpret_cast<const LDS_AS f16x8*>(
-            buf + l32 * 256 + (((2 * kk + hh) ^ (l32 & 15)) << 4));
+            buf + l32 * 256 + (((2 * kk + hh) ^ kswz(l32)) << 4));
         sc = mfma(a, qb[kk], sc);
       }
 #pragma unroll
       for (int kk = 0; kk < AT_DR / 16; ++kk) {
         const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(
-            buf + AT_K_BYTES + l32 * 128 + (((2 * kk + hh) ^ (l32 & 7)) << 4));
+            buf + AT_K_BYTES + l32 * 128 + (((2 * kk + hh) ^ rswz(l32)) << 4));
         sc = mfma(a, qrb[kk], sc);
       }
       // ---- mask, running max, rescale ----
       // register r holds key kt * 32 + r % 4 + 8 (r / 4) + 4 hh
-      const int lim = vis - kt * AT_KEYS - 4 * hh;
+      if (kt * AT_KEYS + AT_KEYS > vis) {  // the tile reaches past this wave's keys
+        const int lim = vis - kt * AT_KEYS - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((r & 3) + 8 * (r >> 2) >= lim) sc[r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if ((r & 3) + 8 * (r >> 2) >= lim) sc[r] = -INFINITY;
-        mx = fmaxf(mx, sc[r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx);
       if (m_new > m_run && m_run != -INFINITY) {
