@@ -4,8 +4,8 @@
 // (item 4).
 //
 // q~[row, m] = sum_j W^K_g[m, j] * (gamma_q[j] gamma_k[g, j] q[row, j]) is a
-// GEMM per KV group, [rows_g x d] . [d x r], in 64 x 128 tiles per block with
-// both operands staged through LDS.
+// GEMM per KV group, [rows_g x d] . [d x r], in 64 x 128 tiles with both
+// operands staged through LDS.
 //   bf16 q~ (absorb_split, one launch): every float32 operand x is split into
 //     bf16 words hi = bf16(x), lo = bf16(x - hi), and the product is taken as
 //     hi.hi + hi.lo + lo.hi on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
@@ -17,6 +17,8 @@
 //   float32 q~ (absorb_gemm + absorb_rows): the float32 matrix cores
 //     (v_mfma_f32_32x32x2_f32); then alpha^q and the RoPE query, one wave per
 //     query row, four heads of one query token per block.
+#include <algorithm>
+
 #include "qkn_internal.h"
 
 namespace qkn {
@@ -239,17 +241,19 @@ struct QueryRows {
   }
 };
 
-// Block of 8 waves: a 64-row x 128-column tile of q~ for one group, wave
+// Block of 8 waves: 64-row x 128-column tiles of q~ for one group, wave
 // (wr, wc) = (w / 4, w % 4) owning rows 32 wr .. +31 and columns 32 wc .. +31
-// (one 32 x 32 tile).  The global row of each of the 64 tile rows is formed
-// once into LDS; the finished tile is written back through LDS in 16-byte
-// pieces.  Per step of 128 head-dim entries the query rows (times gamma_q
-// gamma_k) and the W^K_g rows are split into hi/lo words as they are stored to
-// LDS.  Block (x, y) of group g also forms alpha^q and the RoPE query of its
-// share of the tile's rows (rows y * share .. of the tile), so every query row
-// is done once; the loads of the first batch of that row work are issued
-// first and its arithmetic runs while the operand loads are in flight.
+// (one 32 x 32 tile) of each.  A block takes `tiles` consecutive row tiles of
+// its column block: with d <= 128 the W^K_g tile is split into hi/lo words in
+// LDS once and kept, and the next row tile's query loads are issued before the
+// current tile's products.  Per step of 128 head-dim entries the query rows
+// (times gamma_q gamma_k) are split into hi/lo words as they are stored to LDS.
+// Block (x, y) of group g also forms alpha^q and the RoPE query of its share of
+// each tile's rows (rows y * share .. of the tile), so every query row is done
+// once; those loads go out ahead of the arithmetic that needs them.  A
+// finished tile is written back through LDS in 16-byte pieces.
 constexpr int SW = 8;  // waves per block
+template <bool KEEP>  // d <= 128: one step, the W^K_g tile kept across row tiles
 __global__ __launch_bounds__(64 * SW) void absorb_split(
     const float* __restrict__ q, const float* __restrict__ q_rope,
     const int32_t* __restrict__ q_pos, const float* __restrict__ w_k,
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
     const float* __restrict__ gamma_qr, uint16_t* __restrict__ q_tilde,
     float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int rows_per_group,
     int heads, int heads_per_group, int head_dim, int rank, int rope_dim, float eps,
-    float theta) {
+    float theta, int tiles) {
   constexpr int NT = 64 * SW;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint16_t* Ah = reinterpret_cast<uint16_t*>(smem);
@@ -265,51 +269,48 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
   uint16_t* Bh = Al + TM * SLD;
   uint16_t* Bl = Bh + TN * SLD;
   float* fold = reinterpret_cast<float*>(Bl + TN * SLD);  // gamma_q gamma_k of the step
-  int* grow = reinterpret_cast<int*>(fold + SK);          // global row of tile row r, or -1
-  int* gtok = grow + TM;                                  // its query token (b, i)
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 2, wc = wave & 3;
-  const int n0 = blockIdx.x * TM, m0 = blockIdx.y * TN;
+  const int m0 = blockIdx.y * TN;
   const float* wg = w_k + (size_t)g * rank * head_dim;
   const float* gk = gamma_k + (size_t)g * head_dim;
+  const int t_lo = blockIdx.x * tiles;
+  const int t_hi = min(cdiv(rows_per_group, TM), t_lo + tiles);
 
-  if (tid < TM) {
-    const int n = n0 + tid;
+  // global row and query token of group row n (n < rows_per_group, else -1)
+  auto grow_of = [&](int n) {
     const int bi = n / heads_per_group, hl = n % heads_per_group;
-    grow[tid] = n < rows_per_group ? bi * heads + g * heads_per_group + hl : -1;
-    gtok[tid] = bi;
-  }
-  __syncthreads();
+    return n < rows_per_group ? bi * heads + g * heads_per_group + hl : -1;
+  };
 
-  // the block's share of the row work, in batches of SW * QR_BATCH rows: the
-  // loads of the first batch first
+  // the block's share of each tile's row work, in batches of SW * QR_BATCH rows
   const int share = cdiv(TM, gridDim.y);
   const int r_lo = min(TM, (int)blockIdx.y * share), r_hi = min(TM, r_lo + share);
   QueryRows qr;
-  auto pick_rows = [&](int base) {
+  auto pick_rows = [&](int n0, int base) {
 #pragma unroll
     for (int u = 0; u < QR_BATCH; ++u) {
       const int lr = base + wave + SW * u;
-      qr.row[u] = lr < r_hi ? grow[lr] : -1;
-      qr.tok[u] = lr < r_hi ? gtok[lr] : 0;
+      qr.row[u] = lr < r_hi ? grow_of(n0 + lr) : -1;
+      qr.tok[u] = lr < r_hi ? (n0 + lr) / heads_per_group : 0;
     }
   };
-  pick_rows(r_lo);
-  qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
 
   // operands of a step: A 64 x 128 floats = 2048 float4 (4 per thread), B 128 x 128 (8)
   constexpr int NA = TM * SK / 4 / NT, NB = TN * SK / 4 / NT;
   float4 ra[NA], rb[NB];
-  auto fetch = [&](int k0) {
+  auto fetch_a = [&](int n0, int k0) {
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int e = tid + NT * u, r = e >> 5, k = k0 + 4 * (e & 31);
-      const int gr = grow[r];
+      const int gr = grow_of(n0 + r);
       ra[u] = (gr >= 0 && k < head_dim) ? *reinterpret_cast<const float4*>(q + (size_t)gr * head_dim + k)
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  auto fetch_b = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int e = tid + NT * u, r = e >> 5, k = k0 + 4 * (e & 31);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
     }
     if (tid < SK) fold[tid] = k0 + tid < head_dim ? gamma_q[k0 + tid] * gk[k0 + tid] : 0.f;
   };
-  auto stash = [&]() {
+  auto stash_a = [&]() {
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int e = tid + NT * u, c = 4 * (e & 31), o = (e >> 5) * SLD + c;
@@ -333,6 +334,8 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
       *reinterpret_cast<bf16x4*>(&Ah[o]) = hi;
       *reinterpret_cast<bf16x4*>(&Al[o]) = lo;
     }
+  };
+  auto stash_b = [&]() {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int e = tid + NT * u, o = (e >> 5) * SLD + 4 * (e & 31);
@@ -343,60 +346,72 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
     }
   };
 
-  fetch(0);
-  {
-    int angle_tok = -1;
-    float cs[2], sn[2];
+  if (t_lo >= t_hi) return;  // uniform: no tile for this block
+  pick_rows(t_lo * TM, r_lo);
+  qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
+  fetch_a(t_lo * TM, 0);
+  fetch_b(0);
+  int angle_tok = -1;
+  float cs[2], sn[2];
+  const int r = lane & 31, kh = lane >> 5;
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int n0 = t * TM;
     qr.finish(alpha_q, q_rope_out, angle_tok, cs, sn, head_dim, rope_dim, eps, theta, lane);
     // further batches when the share is larger than one batch (few column blocks)
     for (int base = r_lo + SW * QR_BATCH; base < r_hi; base += SW * QR_BATCH) {
-      pick_rows(base);
+      pick_rows(n0, base);
       qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
       qr.finish(alpha_q, q_rope_out, angle_tok, cs, sn, head_dim, rope_dim, eps, theta, lane);
     }
-  }
-
-  f32x16 acc = {};
-  const int r = lane & 31, kh = lane >> 5;
-  for (int k0 = 0; k0 < head_dim; k0 += SK) {
-    if (k0 > 0) {
-      __syncthreads();  // every wave is done with the previous step's tiles
-      fetch(k0);
+    f32x16 acc = {};
+    for (int k0 = 0; k0 < (KEEP ? SK : head_dim); k0 += SK) {
+      if (k0 > 0) {
+        __syncthreads();  // every wave is done with the previous step's tiles
+        fetch_a(n0, k0);
+        fetch_b(k0);
+      }
+      __syncthreads();  // the fold factors are visible; the previous tile left LDS
+      stash_a();
+      if (!KEEP || t == t_lo) stash_b();
+      __syncthreads();
+      if (KEEP && t + 1 < t_hi) {
+        // the next tile's operand and row-work loads, in flight during the products
+        fetch_a(n0 + TM, 0);
+        pick_rows(n0 + TM, r_lo);
+        qr.load(q, q_rope, q_pos, gamma_qr, head_dim, rope_dim, lane);
+      }
+#pragma unroll
+      for (int ks = 0; ks < SK / 16; ++ks) {
+        if (k0 + 16 * ks >= head_dim) break;  // uniform
+        // A operand: row 32 wr + r, entries 16 ks + 8 kh .. + 7; B operand: W^K row (column of q~)
+        const int ao = (32 * wr + r) * SLD + 16 * ks + 8 * kh;
+        const int bo = (32 * wc + r) * SLD + 16 * ks + 8 * kh;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[ao]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[ao]);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[bo]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[bo]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+      }
     }
-    __syncthreads();  // the fold factors of the step are visible
-    stash();
+    // The tile goes out through LDS (in the place of the A operand words) as
+    // whole 16-byte pieces of q~ rows.  D[i][j]: column j = lane % 32, row
+    // i = (reg % 4) + 8 (reg / 4) + 4 (lane / 32).
+    __syncthreads();  // every wave is done with the operands
+    uint16_t* T = Ah;  // [TM][SLD]
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg)
+      T[(32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * kh) * SLD + 32 * wc + r] = f32_to_bf16(acc[reg]);
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < SK / 16; ++ks) {
-      if (k0 + 16 * ks >= head_dim) break;  // uniform
-      // A operand: row 32 wr + r, entries 16 ks + 8 kh .. + 7; B operand: W^K row (column of q~)
-      const int ao = (32 * wr + r) * SLD + 16 * ks + 8 * kh;
-      const int bo = (32 * wc + r) * SLD + 16 * ks + 8 * kh;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[ao]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[ao]);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[bo]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[bo]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+    for (int u = 0; u < TM * TN / 8 / NT; ++u) {
+      const int e = tid + NT * u, row = e >> 4, c = 8 * (e & 15);
+      const int gr = grow_of(n0 + row);
+      if (gr >= 0 && m0 + c < rank)  // rank is a multiple of 8
+        *reinterpret_cast<uint4*>(q_tilde + (size_t)gr * rank + m0 + c) =
+            *reinterpret_cast<const uint4*>(&T[row * SLD + c]);
     }
-  }
-  // The tile goes out through LDS (in the place of the A operand words) as
-  // whole 16-byte pieces of q~ rows.  D[i][j]: column j = lane % 32, row
-  // i = (reg % 4) + 8 (reg / 4) + 4 (lane / 32).
-  __syncthreads();  // every wave is done with the operands
-  uint16_t* T = Ah;  // [TM][SLD]
-#pragma unroll
-  for (int reg = 0; reg < 16; ++reg)
-    T[(32 * wr + (reg & 3) + 8 * (reg >> 2) + 4 * kh) * SLD + 32 * wc + r] = f32_to_bf16(acc[reg]);
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < TM * TN / 8 / NT; ++u) {
-    const int e = tid + NT * u, row = e >> 4, c = 8 * (e & 15);
-    const int gr = grow[row];
-    if (gr >= 0 && m0 + c < rank)  // rank is a multiple of 8
-      *reinterpret_cast<uint4*>(q_tilde + (size_t)gr * rank + m0 + c) =
-          *reinterpret_cast<const uint4*>(&T[row * SLD + c]);
   }
 }
 
@@ -480,13 +495,21 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
     if (d.rope_dim / 2 > 128) return hipErrorInvalidValue;
     const int hpg = d.heads / d.groups;
     const int rows_per_group = d.batch * d.s_q * hpg;
-    dim3 grid(cdiv(rows_per_group, TM), cdiv(d.rank, TN), d.groups);
-    const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&absorb_split), SPLIT_LDS);
+    // about one block per CU: a block takes several row tiles when there are
+    // more (the W^K_g tile is staged once per block when d <= 128)
+    const int row_tiles = cdiv(rows_per_group, TM), col_blocks = cdiv(d.rank, TN);
+    const bool keep = d.head_dim <= SK;
+    const int tiles = keep ? std::max(1, row_tiles * col_blocks * d.groups / 256) : 1;
+    dim3 grid(cdiv(row_tiles, tiles), col_blocks, d.groups);
+    const void* fn = keep ? reinterpret_cast<const void*>(&absorb_split<true>)
+                          : reinterpret_cast<const void*>(&absorb_split<false>);
+    const hipError_t e = set_lds_limit_once(fn, SPLIT_LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(absorb_split, grid, dim3(64 * SW), SPLIT_LDS, s, q, q_rope, q_pos, w_k, gamma_q,
+    hipLaunchKernelGGL(keep ? absorb_split<true> : absorb_split<false>, grid, dim3(64 * SW), SPLIT_LDS,
+                       s, q, q_rope, q_pos, w_k, gamma_q,
                        gamma_k, gamma_qr, static_cast<uint16_t*>(q_tilde), alpha_q,
                        static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,
-                       d.head_dim, d.rank, d.rope_dim, d.eps, d.rope_theta);
+                       d.head_dim, d.rank, d.rope_dim, d.eps, d.rope_theta, tiles);
     return hipGetLastError();
   }
   return launch_typed<float>(d, q, q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr, q_tilde,
