@@ -281,6 +281,7 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
 // reported.
 // ---------------------------------------------------------------------------
 constexpr int GA_D = 128, GA_DR = 64;
+constexpr int kGqaSmallAppend = 512;  // up to this many tokens: one block per token
 constexpr int GA_WAVES = 16;
 constexpr int GA_MAX_STEPS = 4;  // 16-row steps of a wave whose loads are in flight together
 
@@ -424,6 +425,105 @@ __global__ __launch_bounds__(64 * GA_WAVES) void gqa_append_kernel(
       out[lane] = f32_to_bf16(xn * c - x2 * sn);
       out[lane + GA_DR / 2] = f32_to_bf16(x2 * c + xn * sn);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GQA-path append of a few tokens: one block of 16 waves per (token, group,
+// keys | values).  Thread t takes columns 4 (t % 32) .. + 3 over the latent
+// rows t / 32, t / 32 + 32, ... (all its weight loads, 16-byte pieces, in
+// flight together), accumulating in float32 with fused multiply-adds; the 32
+// row groups' partial sums are added in a fixed order through LDS.  Keys: the
+// sum of squares over the 128 entries gives 1 / RMS.  The key block of group 0
+// also writes the normed, rotated RoPE key.  A token with an out-of-range
+// sequence, position or page is skipped and reported.
+// ---------------------------------------------------------------------------
+constexpr int GS_RG = 32;                  // row groups (d = 128: 32 column quads)
+constexpr int GS_MAX_ROWS = 512 / GS_RG;   // rows per thread, all in flight (r <= 512)
+
+__global__ __launch_bounds__(1024) void gqa_append_small_kernel(
+    const float* __restrict__ c_new, const float* __restrict__ k_rope_new,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_table, const float* __restrict__ w_k,
+    const float* __restrict__ w_v, const float* __restrict__ gamma_k,
+    const float* __restrict__ gamma_kr, uint16_t* __restrict__ kvg, int32_t* __restrict__ err_flag,
+    int batch, int groups, int rank, int max_pages, int num_pages, float eps, float theta) {
+  __shared__ float4 part[GS_RG][GA_D / 4];
+  __shared__ float red[2];
+  __shared__ int slot_s, pos_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = blockIdx.x, g = blockIdx.y;
+  const bool values = blockIdx.z == 1;
+  const int cq = tid % GS_RG, rg = tid / GS_RG;  // column quad, row group
+  // this thread's weight loads go out before the slot lookup resolves
+  const float* wg = (values ? w_v : w_k) + (size_t)g * rank * GA_D + 4 * cq;
+  const int nrows = (rank - rg + GS_RG - 1) / GS_RG;
+  float4 wv[GS_MAX_ROWS];
+  float cv[GS_MAX_ROWS];
+#pragma unroll
+  for (int u = 0; u < GS_MAX_ROWS; ++u) {
+    const int m = rg + GS_RG * u;
+    wv[u] = u < nrows ? *reinterpret_cast<const float4*>(wg + (size_t)m * GA_D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    cv[u] = u < nrows ? c_new[(size_t)n * rank + m] : 0.f;
+  }
+  if (tid == 0) {
+    const int b = seq_idx[n], p = pos[n];
+    int slot = -1;
+    if (b >= 0 && b < batch && p >= 0 && p < max_pages * QKN_MLA_PAGE_SIZE) {
+      const int pg = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
+      if (pg >= 0 && pg < num_pages) slot = pg * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
+    }
+    if (slot < 0 && err_flag && g == 0 && !values) atomicOr(err_flag, QKN_FLAG_INDEX);
+    slot_s = slot;
+    pos_s = p;
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < GS_MAX_ROWS; ++u) {
+    // the latent as the latent cache stores it (bf16, nearest-even)
+    const float c = static_cast<float>(static_cast<__bf16>(cv[u]));
+    acc.x = fmaf(c, wv[u].x, acc.x);
+    acc.y = fmaf(c, wv[u].y, acc.y);
+    acc.z = fmaf(c, wv[u].z, acc.z);
+    acc.w = fmaf(c, wv[u].w, acc.w);
+  }
+  part[rg][cq] = acc;
+  __syncthreads();
+  const int slot = slot_s;
+  if (slot < 0) return;  // uniform
+  const int row_words = 2 * GA_D * groups + GA_DR;
+  float x = 0.f;  // waves 0 and 1: column tid
+  if (tid < GA_D) {
+    const float* pc = reinterpret_cast<const float*>(&part[0][0]) + tid;
+#pragma unroll
+    for (int q = 0; q < GS_RG; ++q) x += pc[q * GA_D];
+  }
+  if (!values) {  // uniform over the block
+    if (tid < GA_D) {
+      const float ss = wave_sum(x * x);
+      if (lane == 0) red[w] = ss;
+    }
+    __syncthreads();
+  }
+  if (tid < GA_D) {
+    if (!values) x = x * (1.0f / sqrtf((red[0] + red[1]) / (float)GA_D + eps)) * gamma_k[(size_t)g * GA_D + tid];
+    if (fabsf(x) >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
+    const _Float16 hx = static_cast<_Float16>(x);
+    kvg[(size_t)slot * row_words + 2 * GA_D * g + (values ? GA_D : 0) + tid] = __builtin_bit_cast(uint16_t, hx);
+  }
+  if (values || g != 0 || w != 2) return;
+  // the RoPE key (wave 2 of the key block of group 0)
+  const float xr = k_rope_new[(size_t)n * GA_DR + lane];
+  const float sr = wave_sum(fmaf(xr, xr, 0.f));
+  const float inv = 1.0f / sqrtf(sr / (float)GA_DR + eps);
+  const float xn = xr * inv * gamma_kr[lane];
+  const float x2 = __shfl(xn, lane + GA_DR / 2);
+  if (lane < GA_DR / 2) {
+    float c = 1.f, sn = 0.f;
+    if (theta != 0.f) rope_cos_sin<false>(pos_s, lane, GA_DR, theta, &c, &sn);
+    uint16_t* out = kvg + (size_t)slot * row_words + 2 * GA_D * groups;
+    out[lane] = f32_to_bf16(xn * c - x2 * sn);
+    out[lane + GA_DR / 2] = f32_to_bf16(x2 * c + xn * sn);
   }
 }
 
@@ -904,6 +1004,13 @@ hipError_t launch_gqa_append(const qkn_mla_dims& d, int32_t n_tokens, const floa
                              const int32_t* block_table, const float* w_k, const float* w_v,
                              const float* gamma_k, const float* gamma_kr, void* kvg,
                              int32_t* err_flag, hipStream_t s) {
+  if (n_tokens <= kGqaSmallAppend && d.rank <= GS_RG * GS_MAX_ROWS) {
+    hipLaunchKernelGGL(gqa_append_small_kernel, dim3(n_tokens, d.groups, 2), dim3(1024), 0, s, c_new,
+                       k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
+                       static_cast<uint16_t*>(kvg), err_flag, d.batch, d.groups, d.rank,
+                       d.max_pages_per_seq, d.num_pages, d.eps, d.rope_theta);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(gqa_append_kernel, dim3(cdiv(n_tokens, 32), d.groups, 2), dim3(64 * GA_WAVES), 0, s, c_new,
                      k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
                      static_cast<uint16_t*>(kvg), err_flag, n_tokens, d.batch, d.groups, d.rank,

@@ -35,6 +35,7 @@ CASES = [
 ]
 APPEND_CASES = [(n, kw) for n, kw, _ in CASES] + [
     ("grouped", dict(batch=2, seq_len=90, rank=256, heads=64, groups=2)),  # r = 256, G = 2
+    ("grouped", dict(batch=2, seq_len=400)),  # G = 4, a history of 798 tokens: the matrix-core route
 ]
 SENTINEL = 0x7E01
 
@@ -58,7 +59,9 @@ def _token_slots(wl, inp):
 
 @pytest.mark.parametrize("name,kw", APPEND_CASES)
 def test_gqa_append_image(name, kw):
-    """History in bulk, then the s_q new tokens: every written key and value
+    """History in bulk (more than 512 tokens in one call take the matrix-core
+    route, fewer one block per token), then the s_q new tokens: every written
+    key and value
     within 2^-11 |x| + 2^-25 (half rounding) of exact, plus the float32 sum's
     gamma_{3r+2} sum_m |c_m W_mj| (times gamma_k alpha for a key, plus the
     key's share of the inverse RMS's own error); RoPE keys within one bf16 step
