@@ -114,7 +114,8 @@ def gqa_splits(wl, seq_lens, cus=256):
     output) plus its tiles; the workgroups are dealt as the kernel numbers them
     (XCD x takes the x-th eighth of the logical ids, its 32 CUs running two
     workgroups each and taking the next as one frees up); the combine costs its
-    half partials, written and read back, at about 3 TB/s.  The constants are
+    half partials, written and read back, at about 3 TB/s, or the latency of
+    walking a row's partials four at a time when that is longer.  The constants are
     fitted to measured attention times of the mtp, dsv3 and grouped workloads
     at several split counts."""
     GQA_WG_FIXED, TILE_US, SLOTS = 8.0, 1.26, 2
@@ -139,7 +140,10 @@ def gqa_splits(wl, seq_lens, cus=256):
             for c in flat[x * per_xcd:(x + 1) * per_xcd]:
                 heapq.heappush(loads, heapq.heappop(loads) + c)
             makespan = max(makespan, max(loads))
-        t = makespan * TILE_US + (rows * P * wl.head_dim * 2 * 2 / 3e12 * 1e6 if P > 1 else 0.0)
+        # the combine: its partial bytes, or the walk of each row's P partials
+        # (16 lanes per row, 4 partials in flight, ~0.35 us a round), if longer
+        comb = max(rows * P * wl.head_dim * 2 * 2 / 3e12 * 1e6, P / 4 * 0.35) if P > 1 else 0.0
+        t = makespan * TILE_US + comb
         if best is None or t < best[0] - 1e-9:
             best = (t, P)
     return best[1]
@@ -499,7 +503,7 @@ def measure_sparse(Q, W, torch, timer, splits=8):
             "decode_hbm_frac": round(nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def measure_prefill(Q, W, torch, timer):
+def measure_prefill(Q, W, torch, timer, cpu=False):
     """Chunked prefill on the explicit path: 2 sequences of 8192 tokens whose
     last 512 are the chunk; the query side, the materialised keys and values of
     the whole cache, and the causal attention, each timed back to back.  FLOPs:
@@ -533,10 +537,60 @@ def measure_prefill(Q, W, torch, timer):
             "attend_tflops": round(att_flops / (a_ms * 1e-3) / 1e12, 1),
             "attend_mfma_frac": round(att_flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "expand_flops": exp_flops,
-            "expand_tflops": round(exp_flops / (e_ms * 1e-3) / 1e12, 1)}
+            "expand_tflops": round(exp_flops / (e_ms * 1e-3) / 1e12, 1),
+            "cpu_oracle": cpu_oracle_sample("prefill", wl, inp) if cpu else None}
 
 
-def measure_gqa(Q, W, torch, timer, name, absorbed_step_us=None, sweep=()):
+def _one_sequence(wl, inp, b):
+    """Workload and inputs of sequence b alone, its pages renumbered 0 .. n-1."""
+    offs = inp["tok_offsets"]
+    T = int(inp["seq_lens"][b])
+    pages = -(-T // 64)
+    one = dict(inp)
+    one.update(seq_lens=inp["seq_lens"][b:b + 1], tok_offsets=np.array([0, T]),
+               c=inp["c"][offs[b]:offs[b + 1]], k_rope=inp["k_rope"][offs[b]:offs[b + 1]],
+               q=inp["q"][b:b + 1], q_rope=inp["q_rope"][b:b + 1],
+               block_table=np.arange(pages, dtype=np.int32)[None, :], num_pages=pages)
+    return wl.replace(batch=1, seq_len=T, seq_len_range=None), one
+
+
+def cpu_oracle_sample(kind, wl, inp, seconds=3.0):
+    """The oracle's attention of the GQA path (kind "gqa") or of the chunked
+    prefill ("prefill") on the host cores, on a sample: the first sequence,
+    every head of its last query token, repeated for about `seconds`.  The
+    stored images are built first and not timed.  FLOPs as the GPU figure
+    counts them (q^.k^ + q^R.k^R and P.V over the visible keys)."""
+    from oracle import qkn_oracle as O
+    from threadpoolctl import threadpool_info
+    cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    one_wl, one = _one_sequence(wl, inp, 0)
+    T = int(one["seq_lens"][0])
+    rows = [(0, wl.s_q - 1, h) for h in range(wl.heads)]
+    qi = O.prefill_query_image(one_wl, one)
+    if kind == "gqa":
+        img = O.gqa_full_image(one_wl, one)["kvg"]
+        run = lambda: O.gqa_decode_on_image(one_wl, qi, img, one["block_table"], one["seq_lens"], 1,  # noqa: E731
+                                            rows=rows)
+    else:
+        cache = O.full_cache_image(one_wl, one)
+        e = O.expand_image(one_wl, cache["kv"], cache["alpha_k"], one["block_table"], one["seq_lens"],
+                           one["w_k"], one["w_v"], one["gamma_k"], -(-T // 64) * 64)
+        run = lambda: O.prefill_on_images(one_wl, qi, e, cache["kv"], one["block_table"],  # noqa: E731
+                                          one["seq_lens"], rows=rows)
+    done, spent = 0, 0.0
+    while spent < seconds:
+        t0 = time.perf_counter()
+        run()
+        spent += time.perf_counter() - t0
+        done += 1
+    flops = done * wl.heads * T * 2 * (2 * wl.head_dim + wl.rope_dim)
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"{done} attentions of the last query token of one {T}-token "
+                                        f"sequence, all {wl.heads} heads, float64 NumPy over the stored "
+                                        f"images, {spent:.1f} s of host time"}
+
+
+def measure_gqa(Q, W, torch, timer, name, absorbed_step_us=None, sweep=(), cpu=False):
     """The GQA path on one workload: the step (query side, GQA append of the
     s_q new tokens, attention over the per-group cache with its combine) and
     the attention call alone, over rotating cache replicas.  FLOPs: the
@@ -600,6 +654,9 @@ def measure_gqa(Q, W, torch, timer, name, absorbed_step_us=None, sweep=()):
         res["speedup_vs_absorbed"] = round(absorbed_step_us / (step_ms * 1e3), 3)
     if out_sweep:
         res["split_sweep"] = out_sweep
+    if cpu:
+        log(f"gqa {name}: timing the CPU oracle on a sample")
+        res["cpu_oracle"] = cpu_oracle_sample("gqa", wl, inp)
     del kvgs, graphs, r
     torch.cuda.empty_cache()
     return res
@@ -824,10 +881,11 @@ def main():
     gqa = []
     if not args.only:
         sparse = measure_sparse(Q, W, torch, timer)
-        prefill = measure_prefill(Q, W, torch, timer)
+        prefill = measure_prefill(Q, W, torch, timer, cpu=not args.no_cpu)
         absorbed = {w["workload"]: w.get("us_per_step") for w in [head["summary"]] + others}
-        for name in ("mtp", "dsv3", "grouped"):
-            gqa.append(measure_gqa(Q, W, torch, timer, name, absorbed.get(name)))
+        for name in ("mtp", "dsv3", "grouped", "long"):
+            gqa.append(measure_gqa(Q, W, torch, timer, name, absorbed.get(name),
+                                   cpu=name == "mtp" and not args.no_cpu))
     sweep = None
     if not args.only and not args.no_sweep:
         log("batch-1 QK-norm overhead sweep")
