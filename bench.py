@@ -115,7 +115,8 @@ def gqa_splits(wl, seq_lens, cus=256):
     (XCD x takes the x-th eighth of the logical ids, its 32 CUs running two
     workgroups each and taking the next as one frees up); the combine costs its
     half partials, written and read back, at about 3 TB/s, or the latency of
-    walking a row's partials four at a time when that is longer.  The constants are
+    walking a row's partials four at a time when that is longer; at most 256
+    splits (more measured slower at 262144 tokens).  The constants are
     fitted to measured attention times of the mtp, dsv3 and grouped workloads
     at several split counts."""
     GQA_WG_FIXED, TILE_US, SLOTS = 8.0, 1.26, 2
@@ -126,7 +127,7 @@ def gqa_splits(wl, seq_lens, cus=256):
     rows = wl.batch * wl.s_q * wl.heads
     lens = [int(T) for T in seq_lens]
     best = None
-    for P in range(1, max(1, min(1024, 8 * cus // (wl.batch * per_seq))) + 1):
+    for P in range(1, max(1, min(256, 8 * cus // (wl.batch * per_seq))) + 1):
         flat = []
         for T in lens:
             L = split_len(max(T, 1), P)
