@@ -33,6 +33,7 @@ CASES = [
     ("grouped", dict(batch=2, seq_len=150, s_q=2), (1, 4)),  # G = 4: 32 heads per group
     ("long", dict(seq_len=1000), (7,)),                      # 32 key tiles
     ("mtp", dict(batch=2, s_q=2, seq_len_range=(40, 300)), (1, 2)),  # s_q = 2: 2 tokens x 64 heads per workgroup
+    ("mtp", dict(batch=3, s_q=4, seq_len_range=(4, 6)), (1, 2)),     # sequences of 4 to 6 tokens: T = s_q included
 ]
 APPEND_CASES = [(n, kw) for n, kw, _ in CASES] + [
     ("grouped", dict(batch=2, seq_len=90, rank=256, heads=64, groups=2)),  # r = 256, G = 2

@@ -26,6 +26,7 @@ CASES = [
     ("mtp", dict(batch=3, s_q=4)),                        # ragged lengths, shuffled pages
     ("grouped", dict(batch=2, seq_len=150, s_q=5)),       # G = 4; the last token group half idle
     ("long", dict(seq_len=1000, s_q=33)),                 # 32 key tiles
+    ("dsv3", dict(batch=2, seq_len=70, s_q=70)),          # the chunk is the whole sequence: T = s_q
 ]
 
 
