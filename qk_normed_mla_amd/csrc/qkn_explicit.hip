@@ -649,12 +649,6 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
 #pragma unroll
   for (int kk = 0; kk < AT_DR / 16; ++kk)
     qrb[kk] = *reinterpret_cast<const bf16x8*>(A.q_rope + qrow * AT_DR + 16 * kk + 8 * hh);
-  // the queries are in registers before the tile loop: otherwise the wait for
-  // them inside the loop would also wait for the next tile's loads
-#pragma unroll
-  for (int kk = 0; kk < AT_D / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
-#pragma unroll
-  for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
 
   // tile loads: thread e < 512 of K^ / V takes row e / 16, chunk e % 16 (two
   // each); thread e < 256 of K^R row e / 8, chunk e % 8.  Buffer loads
@@ -740,9 +734,15 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   if (kt_lo < kt_hi) {
-    fetch(kt_lo);
+    fetch(kt_lo);  // in flight together with the query loads
     stash(kt_lo);
   }
+  // the queries are in registers before the tile loop: otherwise the wait for
+  // them inside the loop would also wait for the next tile's loads
+#pragma unroll
+  for (int kk = 0; kk < AT_D / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+#pragma unroll
+  for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
   __syncthreads();
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     if (kt + 1 < kt_hi) fetch(kt + 1);  // in flight during this tile's products
