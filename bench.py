@@ -112,14 +112,15 @@ def gqa_splits(wl, seq_lens, cus=256):
     attention + combine time.  Cost model, in units of one 32-key tile of one
     workgroup: a workgroup costs GQA_WG_FIXED (loading its queries, writing its
     output) plus its tiles; the workgroups are dealt as the kernel numbers them
-    (XCD x takes the x-th eighth of the logical ids, its 32 CUs running two
-    workgroups each and taking the next as one frees up); the combine costs its
-    half partials, written and read back, at about 3 TB/s, or the latency of
-    walking a row's partials four at a time when that is longer; at most 256
-    splits (more measured slower at 262144 tokens).  The constants are
-    fitted to measured attention times of the mtp, dsv3 and grouped workloads
-    at several split counts."""
-    GQA_WG_FIXED, TILE_US, SLOTS = 8.0, 1.26, 2
+    (XCD x takes the x-th eighth of the logical ids) to the least-loaded of the
+    XCD's 32 CUs; a CU holding two or more runs them at 1.2 times the
+    throughput of one (two waves per SIMD).  The combine costs its half
+    partials, written and read back, at about 3 TB/s, or the latency of walking
+    a row's partials (four at a time in each of 1 or 4 lane groups) when that
+    is longer.  At most 256 splits.  The constants are fitted to measured
+    attention times of the mtp, dsv3, grouped and long workloads at several
+    split counts."""
+    GQA_WG_FIXED, TILE_US, PAIR_GAIN = 8.0, 1.24, 1.2
     tpw = 4
     while tpw > 1 and tpw // 2 >= wl.s_q and (wl.heads // wl.groups // 32) % (8 // tpw) == 0:
         tpw //= 2
@@ -137,13 +138,14 @@ def gqa_splits(wl, seq_lens, cus=256):
         per_xcd = math.ceil(len(flat) / 8)
         makespan = 0.0
         for x in range(8):
-            loads = [0.0] * (SLOTS * cus // 8)
+            loads = [(0.0, 0, c) for c in range(cus // 8)]  # (work, items, cu)
+            heapq.heapify(loads)
             for c in flat[x * per_xcd:(x + 1) * per_xcd]:
-                heapq.heappush(loads, heapq.heappop(loads) + c)
-            makespan = max(makespan, max(loads))
-        # the combine: its partial bytes, or the walk of each row's P partials
-        # (16 lanes per row, 4 partials in flight, ~0.35 us a round), if longer
-        comb = max(rows * P * wl.head_dim * 2 * 2 / 3e12 * 1e6, P / 4 * 0.35) if P > 1 else 0.0
+                w, k, cu = heapq.heappop(loads)
+                heapq.heappush(loads, (w + c, k + 1, cu))
+            makespan = max(makespan, max(w / (PAIR_GAIN if k >= 2 else 1.0) for w, k, _ in loads))
+        walk = P / 16 if P >= 32 else P / 4  # rounds of partial loads per lane group
+        comb = max(rows * P * wl.head_dim * 2 * 2 / 3e12 * 1e6, walk * 0.35) if P > 1 else 0.0
         t = makespan * TILE_US + comb
         if best is None or t < best[0] - 1e-9:
             best = (t, P)

@@ -907,6 +907,64 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16* __rest
   *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// The same merge for many splits: one wave per row; its four 16-lane groups
+// take the splits p = 4 k + group, and their sums are added across the
+// groups at the end.
+__global__ __launch_bounds__(256) void gqa_combine_wide_kernel(const _Float16* __restrict__ o_part,
+                                                               const float* __restrict__ lse_part,
+                                                               float* __restrict__ o,
+                                                               float* __restrict__ lse, int n_rows,
+                                                               int num_splits) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, sub = lane >> 4;
+  const int row = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (row >= n_rows) return;  // whole waves
+  const float* lp = lse_part + (size_t)row * num_splits;
+  float M = -INFINITY;
+  for (int p = lane; p < num_splits; p += 64) M = fmaxf(M, lp[p]);
+  M = wave_max(M);
+  float* out = o + (size_t)row * AT_D + 8 * l16;
+  if (M == -INFINITY) {
+    if (sub == 0) {
+      *reinterpret_cast<float4*>(out) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(out + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (lane == 0) lse[row] = -INFINITY;
+    return;
+  }
+  float sum = 0.f;
+  for (int p = lane; p < num_splits; p += 64) sum += expf(lp[p] - M);
+  sum = wave_sum(sum);
+  const float L = M + logf(sum);
+  if (lane == 0) lse[row] = L;
+  const _Float16* op = o_part + (size_t)row * num_splits * AT_D + 8 * l16;
+  float acc[8] = {};
+  for (int p0 = sub; p0 < num_splits; p0 += 16) {
+    f16x8 v[4];
+    float wgt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + 4 * u;
+      const float l = p < num_splits ? lp[p] : -INFINITY;
+      wgt[u] = l == -INFINITY ? 0.f : expf(l - L);
+      v[u] = p < num_splits ? *reinterpret_cast<const f16x8*>(op + (size_t)p * AT_D) : f16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt[u], static_cast<float>(v[u][j]), acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc[j] += __shfl_xor(acc[j], 16);
+    acc[j] += __shfl_xor(acc[j], 32);
+  }
+  if (sub == 0) {
+    *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
 template <int NT>
 hipError_t launch_expand_nt(const qkn_mla_dims& d, const void* kv, const float* alpha_k,
                             const int32_t* block_table, const int32_t* seq_lens, const float* w_k,
@@ -1049,8 +1107,13 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || num_splits == 1) return e;
   const int rows = d.batch * d.s_q * d.heads;
-  hipLaunchKernelGGL(gqa_combine_kernel, dim3(cdiv(rows, 16)), dim3(256), 0, s,
-                     static_cast<const _Float16*>(o_part), lse_part, o, lse, rows, num_splits);
+  if (num_splits >= 32) {  // a wave per row: the walk over many partials in four lane groups
+    hipLaunchKernelGGL(gqa_combine_wide_kernel, dim3(cdiv(rows, 4)), dim3(256), 0, s,
+                       static_cast<const _Float16*>(o_part), lse_part, o, lse, rows, num_splits);
+  } else {
+    hipLaunchKernelGGL(gqa_combine_kernel, dim3(cdiv(rows, 16)), dim3(256), 0, s,
+                       static_cast<const _Float16*>(o_part), lse_part, o, lse, rows, num_splits);
+  }
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ CASES = [
     ("dsv3", dict(batch=2, seq_len=200), (1, 3)),            # s_q = 1: one token x 128 heads per workgroup
     ("mtp", dict(batch=3, s_q=4), (1, 3)),                   # ragged lengths, shuffled pages
     ("grouped", dict(batch=2, seq_len=150, s_q=2), (1, 4)),  # G = 4: 32 heads per group
-    ("long", dict(seq_len=1000), (7,)),                      # 32 key tiles
+    ("long", dict(seq_len=1000), (7, 40)),                   # 32 key tiles; 40 splits: the wide combine, 24 empty
     ("mtp", dict(batch=2, s_q=2, seq_len_range=(40, 300)), (1, 2)),  # s_q = 2: 2 tokens x 64 heads per workgroup
     ("mtp", dict(batch=3, s_q=4, seq_len_range=(4, 6)), (1, 2)),     # sequences of 4 to 6 tokens: T = s_q included
 ]
