@@ -550,6 +550,7 @@ constexpr int AT_R_BYTES = AT_KEYS * AT_DR * 2;   // 4096
 constexpr int AT_TILE = 2 * AT_K_BYTES + AT_R_BYTES;  // 20480
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyLog2 = 8.f;  // probabilities up to 256: far inside the half range
 
 __device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -612,7 +613,10 @@ template <bool GQA>
 __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * AT_TILE];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform over the wave: held in a scalar register, the
+  // heads, group and query token derived from it are too, and so are the
+  // tile descriptors built from them
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int s_q = A.s_q, heads = A.heads, groups = A.groups, max_pages = A.max_pages;
   const int head_groups = A.head_groups, token_groups = A.token_groups, tpw = A.tpw;
@@ -774,16 +778,22 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = pair_max(mx);
+      // the reference m_run moves only when the tile's maximum passes it by
+      // more than 2^kLazyLog2 in probability (always on a row's first key):
+      // probabilities stay at most 2^kLazyLog2, and the rescale of the
+      // accumulators is rare after the first tiles
       const float m_new = fmaxf(m_run, mx);
-      if (m_new > m_run && m_run != -INFINITY) {
-        const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-        l_run *= al;
+      if ((m_new - m_run) * c2 > kLazyLog2) {
+        if (m_run != -INFINITY) {
+          const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+          l_run *= al;
 #pragma unroll
-        for (int om = 0; om < AT_D / 32; ++om)
+          for (int om = 0; om < AT_D / 32; ++om)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[om][r] *= al;
+            for (int r = 0; r < 16; ++r) acc[om][r] *= al;
+        }
+        m_run = m_new;
       }
-      m_run = m_new;
       const float mc = m_run == -INFINITY ? 0.f : m_run * c2;
       f16x8 pb[2];
 #pragma unroll
