@@ -753,6 +753,9 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
     const LDS_AS uint8_t* buf = (const LDS_AS uint8_t*)smem + (kt & 1) * AT_TILE;
     if (active && kt * AT_KEYS < vis) {
       // ---- S^T = K^ q^^T + K^R q^R^T ----
+      // the two waves on a SIMD (two workgroups per CU): the one issuing
+      // products goes first, the other's softmax fills the matrix core's gaps
+      __builtin_amdgcn_s_setprio(1);
       f32x16 sc = {};
 #pragma unroll
       for (int kk = 0; kk < AT_D / 16; ++kk) {
@@ -767,6 +770,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
         sc = mfma(a, qrb[kk], sc);
       }
       // ---- mask, running max, rescale ----
+      __builtin_amdgcn_s_setprio(0);
       // register r holds key kt * 32 + r % 4 + 8 (r / 4) + 4 hh
       if (kt * AT_KEYS + AT_KEYS > vis) {  // the tile reaches past this wave's keys
         const int lim = vis - kt * AT_KEYS - 4 * hh;
@@ -806,6 +810,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
         l_run = __builtin_amdgcn_fdot2(pr, ones, l_run, false);
       }
       // ---- O^T += V^T P^T ----
+      __builtin_amdgcn_s_setprio(1);
       const LDS_AS uint8_t* vb = buf + AT_K_BYTES + AT_R_BYTES;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -824,6 +829,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
     }
     // the next tile goes to the other buffer, which every wave finished
     // reading before the previous barrier
+    __builtin_amdgcn_s_setprio(0);
     if (kt + 1 < kt_hi) stash(kt + 1);
     __syncthreads();
   }
