@@ -575,6 +575,21 @@ typedef const __attribute__((address_space(4))) int32_t ConstI32;  // read throu
 // 128-byte RoPE row t is stored at c ^ rswz(t): rows 2j and 2j + 1 fall on the
 // two halves of the banks, so rswz must differ over the even (and the odd)
 // rows of 16.
+// compile-time unrolled loop: f(integral_constant<int, i>) for i in [B, E)
+template <int B, int E>
+struct Unroll {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, B>{});
+    Unroll<B + 1, E>::run(f);
+  }
+};
+template <int E>
+struct Unroll<E, E> {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
+
 __device__ __forceinline__ int kswz(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
 __device__ __forceinline__ int rswz(int t) { return (t >> 1) & 7; }
 
@@ -611,7 +626,7 @@ __device__ __forceinline__ int xcd_local(int id, int n) {
 
 template <bool GQA>
 __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * AT_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * AT_TILE];
   const int tid = threadIdx.x;
   // the wave index is uniform over the wave: held in a scalar register, the
   // heads, group and query token derived from it are too, and so are the
@@ -665,12 +680,15 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   // page of the next tile is loaded a tile ahead.
   const ConstI32* pages = (const ConstI32*)(A.block_table) + (size_t)b * max_pages;
   int pg_next = kt_lo < kt_hi ? pages[kt_lo * AT_KEYS / QKN_MLA_PAGE_SIZE] : 0;
+  // tiles are fetched in order; one at or past kt_hi reads nothing (size 0)
+  // and its registers hold zeros, so the loop needs no branch for it
   auto fetch = [&](int kt) {
+    const bool real = kt < kt_hi;
     const int pg = pg_next;
-    if (kt + 1 < kt_hi) pg_next = pages[(kt + 1) * AT_KEYS / QKN_MLA_PAGE_SIZE];
+    pg_next = pages[min(kt + 1, kt_hi - 1) * AT_KEYS / QKN_MLA_PAGE_SIZE];
     const bool page_ok = pg >= 0 && pg < A.num_pages;
-    if (!page_ok) err = 1;
-    const int nvalid = min(AT_KEYS, vis_max - kt * AT_KEYS);
+    if (real && !page_ok) err = 1;
+    const int nvalid = real ? min(AT_KEYS, vis_max - kt * AT_KEYS) : 0;
     const size_t row0 = (size_t)(page_ok ? pg : 0) * QKN_MLA_PAGE_SIZE + kt * AT_KEYS % QKN_MLA_PAGE_SIZE;
     if (GQA) {
       const uint32_t rb = 2u * A.row_words;
@@ -707,8 +725,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
                                          rr_, rr * rb + 2u * A.rank + 16u * c, 0, 0));
     }
   };
-  auto stash = [&](int kt) {
-    uint8_t* buf = smem + (kt & 1) * AT_TILE;
+  auto stash = [&](int slot) {
+    uint8_t* buf = smem + slot * AT_TILE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + 256 * u, rr = e >> 4, c = e & 15;
@@ -737,101 +755,153 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   const float c2 = A.scale * kLog2e;
   const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  if (kt_lo < kt_hi) {
-    fetch(kt_lo);  // in flight together with the query loads
-    stash(kt_lo);
+  // per-lane LDS offsets within a slot: the QK operands (8 normed-key and 4
+  // RoPE-key reads) and the PV operands (two transposed reads per product)
+  constexpr int NQ = AT_D / 16 + AT_DR / 16, QK_AHEAD = 4;
+  uint32_t qk_off[NQ], pv_off[2][AT_D / 32];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+    qk_off[n] = n < AT_D / 16 ? l32 * 256 + (((2 * n + hh) ^ kswz(l32)) << 4)
+                              : AT_K_BYTES + l32 * 128 + (((2 * (n - AT_D / 16) + hh) ^ rswz(l32)) << 4);
+#pragma unroll
+  for (int om = 0; om < AT_D / 32; ++om) {
+    pv_off[0][om] = AT_K_BYTES + AT_R_BYTES + (pv0 ^ (64u * om));
+    pv_off[1][om] = AT_K_BYTES + AT_R_BYTES + (pv1 ^ (64u * om));
   }
-  // the queries are in registers before the tile loop: otherwise the wait for
-  // them inside the loop would also wait for the next tile's loads
+  const LDS_AS uint8_t* lds = (const LDS_AS uint8_t*)smem;
+
+  // S^T of the tile in slot SLOT: 8 products over the normed keys, then 4
+  // over the RoPE keys, operands read QK_AHEAD products ahead; fill(n) runs
+  // after product n (the softmax of the previous tile)
+  auto qk = [&](auto SLOT, auto&& fill) {
+    constexpr uint32_t base = decltype(SLOT)::value * AT_TILE;
+    auto rd = [&](int n) { return *reinterpret_cast<const LDS_AS f16x8*>(lds + base + qk_off[n]); };
+    f16x8 ab[QK_AHEAD];
 #pragma unroll
-  for (int kk = 0; kk < AT_D / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+    for (int n = 0; n < QK_AHEAD; ++n) ab[n] = rd(n);
+    f32x16 s_ = {};
+    Unroll<0, NQ>::run([&](auto N) {
+      constexpr int n = decltype(N)::value;
+      const f16x8 a = ab[n % QK_AHEAD];
+      if constexpr (n + QK_AHEAD < NQ) ab[n % QK_AHEAD] = rd(n + QK_AHEAD);
+      if constexpr (n < AT_D / 16)
+        s_ = mfma(a, qb[n], s_);
+      else
+        s_ = mfma(__builtin_bit_cast(bf16x8, a), qrb[n - AT_D / 16], s_);
+      fill(N);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return s_;
+  };
+  // O^T += V^T P^T over the tile in slot SLOT
+  auto pv = [&](auto SLOT, const f16x8 (&pb)[2]) {
+    constexpr uint32_t base = decltype(SLOT)::value * AT_TILE;
 #pragma unroll
-  for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
-  __syncthreads();
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    if (kt + 1 < kt_hi) fetch(kt + 1);  // in flight during this tile's products
-    const LDS_AS uint8_t* buf = (const LDS_AS uint8_t*)smem + (kt & 1) * AT_TILE;
-    if (active && kt * AT_KEYS < vis) {
-      // ---- S^T = K^ q^^T + K^R q^R^T ----
-      // the two waves on a SIMD (two workgroups per CU): the one issuing
-      // products goes first, the other's softmax fills the matrix core's gaps
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 sc = {};
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int kk = 0; kk < AT_D / 16; ++kk) {
-        const f16x8 a = *reinterpret_cast<const LDS_AS f16x8*>(
-            buf + l32 * 256 + (((2 * kk + hh) ^ kswz(l32)) << 4));
-        sc = mfma(a, qb[kk], sc);
-      }
-#pragma unroll
-      for (int kk = 0; kk < AT_DR / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(
-            buf + AT_K_BYTES + l32 * 128 + (((2 * kk + hh) ^ rswz(l32)) << 4));
-        sc = mfma(a, qrb[kk], sc);
-      }
-      // ---- mask, running max, rescale ----
-      __builtin_amdgcn_s_setprio(0);
-      // register r holds key kt * 32 + r % 4 + 8 (r / 4) + 4 hh
-      if (kt * AT_KEYS + AT_KEYS > vis) {  // the tile reaches past this wave's keys
-        const int lim = vis - kt * AT_KEYS - 4 * hh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((r & 3) + 8 * (r >> 2) >= lim) sc[r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = pair_max(mx);
-      // the reference m_run moves only when the tile's maximum passes it by
-      // more than 2^kLazyLog2 in probability (always on a row's first key):
-      // probabilities stay at most 2^kLazyLog2, and the rescale of the
-      // accumulators is rare after the first tiles
-      const float m_new = fmaxf(m_run, mx);
-      if ((m_new - m_run) * c2 > kLazyLog2) {
-        if (m_run != -INFINITY) {
-          const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-          l_run *= al;
-#pragma unroll
-          for (int om = 0; om < AT_D / 32; ++om)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[om][r] *= al;
-        }
-        m_run = m_new;
-      }
-      const float mc = m_run == -INFINITY ? 0.f : m_run * c2;
-      f16x8 pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -mc));
-        const f16x2 pr = __builtin_convertvector((f32x2){p0, p1}, f16x2);
-        pb[r >> 3][r & 7] = pr[0];
-        pb[r >> 3][(r & 7) + 1] = pr[1];
-        l_run = __builtin_amdgcn_fdot2(pr, ones, l_run, false);
-      }
-      // ---- O^T += V^T P^T ----
-      __builtin_amdgcn_s_setprio(1);
-      const LDS_AS uint8_t* vb = buf + AT_K_BYTES + AT_R_BYTES;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int om = 0; om < AT_D / 32; ++om) {
-          const uint32_t off = 4096u * ks;
-          // the transposed read moves 16-bit words; the words are halves here
-          const f16x4 lo4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vb + ((pv0 ^ (64u * om)) + off))));
-          const f16x4 hi4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vb + ((pv1 ^ (64u * om)) + off))));
-          const f16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[om] = mfma(a, pb[ks], acc[om]);
-        }
+      for (int om = 0; om < AT_D / 32; ++om) {
+        // the transposed read moves 16-bit words; the words are halves here
+        const f16x4 lo4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(lds + base + 4096u * ks + pv_off[0][om])));
+        const f16x4 hi4 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(lds + base + 4096u * ks + pv_off[1][om])));
+        const f16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[om] = mfma(a, pb[ks], acc[om]);
       }
     }
-    // the next tile goes to the other buffer, which every wave finished
-    // reading before the previous barrier
-    __builtin_amdgcn_s_setprio(0);
-    if (kt + 1 < kt_hi) stash(kt + 1);
+  };
+
+  // Software pipeline over three LDS slots (slot of tile kt: (kt - kt_lo) mod
+  // 3).  Iteration kt: the loads of tile kt + 2 go out; the QK products of
+  // tile kt + 1 run with the softmax of tile kt between them; then the PV
+  // products of tile kt; tile kt + 2 is stored into the slot of tile kt - 1
+  // and one barrier ends the iteration.  Every wave takes every tile of the
+  // block: a tile past this wave's keys (or a wave past the last query token,
+  // vis = 0) is masked whole, which leaves its max, sum and accumulators as
+  // they were.
+  if (kt_lo < kt_hi) {
+    fetch(kt_lo);  // in flight together with the query loads
+    stash(0);
+    fetch(kt_lo + 1);
+    // the queries are in registers before the tile loop: otherwise the wait
+    // for them inside the loop would also wait for the next tile's loads
+#pragma unroll
+    for (int kk = 0; kk < AT_D / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+#pragma unroll
+    for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
     __syncthreads();
+    f32x16 sc = qk(std::integral_constant<int, 0>{}, [](auto) {});
+    stash(1);
+    __syncthreads();
+
+    auto iteration = [&](auto SLOT, int kt) {
+      constexpr int P = decltype(SLOT)::value;
+      fetch(kt + 2);
+      // ---- softmax of tile kt (mask, running max, probabilities) between
+      // the QK products of tile kt + 1 ----
+      float mx = -INFINITY, mc = 0.f;
+      f16x8 pb[2];
+      auto soft = [&](auto N) {
+        constexpr int n = decltype(N)::value;
+        if constexpr (n == 0) {
+          // register r holds key kt * 32 + r % 4 + 8 (r / 4) + 4 hh
+          if (kt * AT_KEYS + AT_KEYS > vis) {  // the tile reaches past this wave's keys
+            const int lim = vis - kt * AT_KEYS - 4 * hh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if ((r & 3) + 8 * (r >> 2) >= lim) sc[r] = -INFINITY;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        } else if constexpr (n == 1) {
+          mx = pair_max(mx);
+          // the reference m_run moves only when the tile's maximum passes it
+          // by more than 2^kLazyLog2 in probability (always on a row's first
+          // key): probabilities stay at most 2^kLazyLog2, and the rescale of
+          // the accumulators is rare after the first tiles
+          const float m_new = fmaxf(m_run, mx);
+          if ((m_new - m_run) * c2 > kLazyLog2) {
+            if (m_run != -INFINITY) {
+              const float al = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+              l_run *= al;
+#pragma unroll
+              for (int om = 0; om < AT_D / 32; ++om)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[om][r] *= al;
+            }
+            m_run = m_new;
+          }
+          mc = m_run == -INFINITY ? 0.f : m_run * c2;
+        } else if constexpr (n >= 2 && n < 10) {
+          constexpr int r = 2 * (n - 2);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -mc));
+          const f16x2 pr = __builtin_convertvector((f32x2){p0, p1}, f16x2);
+          pb[r >> 3][r & 7] = pr[0];
+          pb[r >> 3][(r & 7) + 1] = pr[1];
+          l_run = __builtin_amdgcn_fdot2(pr, ones, l_run, false);
+        }
+      };
+      // the two waves on a SIMD (two workgroups per CU): the one issuing
+      // products goes first, the other's vector work fills the gaps
+      __builtin_amdgcn_s_setprio(1);
+      const f32x16 sc_next = qk(std::integral_constant<int, (P + 1) % 3>{}, soft);
+      pv(std::integral_constant<int, P>{}, pb);
+      __builtin_amdgcn_s_setprio(0);
+      // tile kt + 2 goes to the slot of tile kt - 1, which every wave
+      // finished reading before the previous barrier
+      stash((P + 2) % 3);
+      __syncthreads();
+      sc = sc_next;
+    };
+    for (int kt = kt_lo;;) {
+      iteration(std::integral_constant<int, 0>{}, kt);
+      if (++kt >= kt_hi) break;
+      iteration(std::integral_constant<int, 1>{}, kt);
+      if (++kt >= kt_hi) break;
+      iteration(std::integral_constant<int, 2>{}, kt);
+      if (++kt >= kt_hi) break;
+    }
   }
 
   // ---- o = acc / l (lane: head l32, entries 32 om + r % 4 + 8 (r / 4) + 4 hh);
