@@ -111,9 +111,10 @@ __global__ __launch_bounds__(256) void prefill_query_kernel(
 
 // ---------------------------------------------------------------------------
 // keys and values: K = C W^K_g, V = C W^V_g for 256 tokens of one sequence and
-// group per block (blockIdx.z: 0 keys, 1 values).  Wave w owns tokens 32 w ..
-// 32 w + 31 (the A rows: the stored bf16 latent words, exact operands) and all
-// d / 32 column tiles.  W passes through LDS in chunks of KC rows split into
+// group and NT column tiles (32 NT of the d columns) per block (blockIdx.z:
+// column block * 2 + 0 for keys, + 1 for values).  Wave w owns tokens 32 w ..
+// 32 w + 31 (the A rows: the stored bf16 latent words, exact operands) and the
+// block's NT column tiles.  W passes through LDS in chunks of KC rows split into
 // three bf16 words (hi + mid + lo, exact to 2^-24), read with
 // ds_read_b64_tr_b16; every product is exact and the sums are float32.
 // ---------------------------------------------------------------------------
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
     const float* __restrict__ w_k, const float* __restrict__ w_v,
     const float* __restrict__ gamma_k, _Float16* __restrict__ k_hat, _Float16* __restrict__ v_out,
     int32_t* __restrict__ err_flag, int groups, int rank, int rope_dim, int max_pages,
-    int num_pages, int max_T) {
-  constexpr int D = NT * 32;
+    int num_pages, int max_T, int width) {
+  constexpr int D = NT * 32;  // columns of this block: col0 .. col0 + D - 1 of the width
   constexpr int KC = ex_chunk_rows(D);
   constexpr int PER = KC * D / 4 / (64 * EX_WAVES);  // float4 of a chunk per thread
   constexpr int SPC = KC / 16;                       // 16-row steps per chunk
@@ -165,8 +166,9 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
   const int l16 = lane & 15, G = (lane >> 4) & 1;
   const int b = blockIdx.y / groups, g = blockIdx.y % groups;
-  const bool values = blockIdx.z == 1;
-  const float* wg = (values ? w_v : w_k) + (size_t)g * rank * D;
+  const bool values = blockIdx.z & 1;
+  const int col0 = (blockIdx.z >> 1) * D;
+  const float* wg = (values ? w_v : w_k) + (size_t)g * rank * width + col0;
   int T = seq_lens[b];
   T = min(max(T, 0), max_pages * QKN_MLA_PAGE_SIZE);
   const int t = blockIdx.x * EX_TOK + 32 * wave + l32;  // token of this lane's A row
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + u * 64 * EX_WAVES;
-      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(k0 + e / (D / 4)) * D + 4 * (e % (D / 4)));
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(k0 + e / (D / 4)) * width + 4 * (e % (D / 4)));
     }
 #pragma unroll
     for (int st = 0; st < SPC; ++st) {
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
   // of the wave; keys are scaled by gamma_k[j] alpha^k of the token.  Tokens
   // past the sequence (or on a bad page) are written as zeros.
   _Float16* out = values ? v_out : k_hat;
-  const float* gk = gamma_k + (size_t)g * D;
+  const float* gk = gamma_k + (size_t)g * width + col0;
   float big = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(64 * EX_WAVES) void prefill_expand_kernel(
       const int j = 32 * ct + l32;
       const float x = row_i >= 0 ? acc[ct][r] * s * (values ? 1.f : gk[j]) : 0.f;
       big = fmaxf(big, fabsf(x));
-      out[(((size_t)b * max_T + tt) * groups + g) * D + j] = static_cast<_Float16>(x);
+      out[(((size_t)b * max_T + tt) * groups + g) * width + col0 + j] = static_cast<_Float16>(x);
     }
   }
   // a value the half rounds to +-inf
@@ -1062,11 +1064,13 @@ hipError_t launch_expand_nt(const qkn_mla_dims& d, const void* kv, const float* 
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&prefill_expand_kernel<NT>), lds);
   if (e != hipSuccess) return e;
   const int max_T = d.max_pages_per_seq * QKN_MLA_PAGE_SIZE;
-  hipLaunchKernelGGL(prefill_expand_kernel<NT>, dim3(cdiv(max_T, EX_TOK), d.batch * d.groups, 2),
+  // blocks of NT column tiles: (token block, sequence and group, column block and keys | values)
+  hipLaunchKernelGGL(prefill_expand_kernel<NT>,
+                     dim3(cdiv(max_T, EX_TOK), d.batch * d.groups, 2 * (d.head_dim / D)),
                      dim3(64 * EX_WAVES), lds, s, static_cast<const uint16_t*>(kv), alpha_k,
                      block_table, seq_lens, w_k, w_v, gamma_k, static_cast<_Float16*>(k_hat),
                      static_cast<_Float16*>(v), err_flag, d.groups, d.rank, d.rope_dim,
-                     d.max_pages_per_seq, d.num_pages, max_T);
+                     d.max_pages_per_seq, d.num_pages, max_T, d.head_dim);
   return hipGetLastError();
 }
 
@@ -1102,7 +1106,9 @@ hipError_t launch_prefill_expand(const qkn_mla_dims& d, const void* kv, const fl
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  const float* w_k, const float* w_v, const float* gamma_k,
                                  void* k_hat, void* v, int32_t* err_flag, hipStream_t s) {
-  return launch_expand_nt<AT_D / 32>(d, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k,
+  // 64 columns per block: twice the blocks of whole-width ones (256 for two
+  // 8192-token sequences), each staging half of W_g
+  return launch_expand_nt<2>(d, kv, alpha_k, block_table, seq_lens, w_k, w_v, gamma_k,
                                      k_hat, v, err_flag, s);
 }
 
