@@ -111,36 +111,46 @@ def gqa_splits(wl, seq_lens, cus=256):
     """Split count of the GQA-path attention with the smallest estimated
     attention + combine time.  Cost model, in units of one 32-key tile of one
     workgroup: a workgroup costs GQA_WG_FIXED (loading its queries, writing its
-    output) plus its tiles; the workgroups are dealt as the kernel numbers them
-    (XCD x takes the x-th eighth of the logical ids) to the least-loaded of the
-    XCD's 32 CUs; a CU holding two or more runs them at 1.2 times the
-    throughput of one (two waves per SIMD).  The combine costs its half
-    partials, written and read back, at about 3 TB/s, or the latency of walking
-    a row's partials (four at a time in each of 1 or 4 lane groups) when that
-    is longer.  At most 256 splits.  The constants are fitted to measured
-    attention times of the mtp, dsv3, grouped and long workloads at several
-    split counts."""
+    output) plus its tiles; the workgroups are dealt to the 8 XCDs as the
+    kernel numbers them (ragged batches of up to 64: the (sequence, split)
+    pairs, longest sequence first, round robin over the XCDs, the token and
+    head blocks of a pair together; otherwise XCD x takes the x-th eighth in
+    order), and each XCD's workgroups go in order to the least-loaded of its 32 CUs; a
+    CU holding two or more runs them at PAIR_GAIN times the throughput of one
+    (two waves per SIMD).  The combine costs its half partials, written and
+    read back, at about 3 TB/s, or the latency of walking a row's partials
+    (four at a time in each of 1 or 4 lane groups) when that is longer.  At
+    most 256 splits.  The constants are fitted to measured attention times of
+    the mtp, dsv3, grouped and long workloads at several split counts."""
     GQA_WG_FIXED, TILE_US, PAIR_GAIN = 8.0, 1.24, 1.2
     tpw = 4
     while tpw > 1 and tpw // 2 >= wl.s_q and (wl.heads // wl.groups // 32) % (8 // tpw) == 0:
         tpw //= 2
-    per_seq = math.ceil(wl.s_q / tpw) * (wl.heads // 32 // (4 // tpw))
+    per_pair = math.ceil(wl.s_q / tpw) * (wl.heads // 32 // (4 // tpw))
     rows = wl.batch * wl.s_q * wl.heads
     lens = [int(T) for T in seq_lens]
+    ragged = len(lens) <= 64 and len(set(lens)) > 1
+    order = sorted(range(len(lens)), key=lambda b: (-lens[b], b)) if ragged else range(len(lens))
     best = None
-    for P in range(1, max(1, min(256, 8 * cus // (wl.batch * per_seq))) + 1):
-        flat = []
-        for T in lens:
+    for P in range(1, max(1, min(256, 8 * cus // (wl.batch * per_pair))) + 1):
+        pairs = []
+        for b in order:
+            T = lens[b]
             L = split_len(max(T, 1), P)
             for p in range(P):
                 n = min(T, (p + 1) * L) - p * L
-                flat += [GQA_WG_FIXED + math.ceil(n / 32) if n > 0 else 1.0] * per_seq
-        per_xcd = math.ceil(len(flat) / 8)
+                pairs.append([GQA_WG_FIXED + math.ceil(n / 32) if n > 0 else 1.0] * per_pair)
+        if ragged:
+            xcd_items = [sum(pairs[x::8], []) for x in range(8)]
+        else:
+            flat = sum(pairs, [])
+            per_xcd = math.ceil(len(flat) / 8)
+            xcd_items = [flat[x * per_xcd:(x + 1) * per_xcd] for x in range(8)]
         makespan = 0.0
-        for x in range(8):
+        for items in xcd_items:
             loads = [(0.0, 0, c) for c in range(cus // 8)]  # (work, items, cu)
             heapq.heapify(loads)
-            for c in flat[x * per_xcd:(x + 1) * per_xcd]:
+            for c in items:
                 w, k, cu = heapq.heappop(loads)
                 heapq.heappush(loads, (w + c, k + 1, cu))
             makespan = max(makespan, max(w / (PAIR_GAIN if k >= 2 else 1.0) for w, k, _ in loads))

@@ -423,7 +423,10 @@ int qkn_mla_gqa_attend(const qkn_mla_dims* dims, const void* q_hat, const void* 
   if (st != QKN_OK) return st;
   if (!qkn::gqa_supported(*dims)) return QKN_ERR_UNSUPPORTED;
   if (num_splits < 1 || num_splits > kMaxSplits) return QKN_ERR_INVALID_ARG;
-  const int64_t blocks = (int64_t)dims->batch * num_splits * ((dims->s_q + 3) / 4) * (dims->heads / 32);
+  // workgroups: (sequence, split) pairs padded to a multiple of 8, times the
+  // token and head blocks of a pair (at most ceil(s_q / 4) x heads / 32)
+  const int64_t pairs = ((int64_t)dims->batch * num_splits + 7) / 8 * 8;
+  const int64_t blocks = pairs * ((dims->s_q + 3) / 4) * (dims->heads / 32);
   if (blocks > INT32_MAX) return QKN_ERR_INVALID_ARG;
   if (!q_hat || !q_rope_normed || !kvg_cache || !block_table || !seq_lens || !o || !lse)
     return QKN_ERR_INVALID_ARG;

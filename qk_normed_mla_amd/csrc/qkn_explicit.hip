@@ -612,7 +612,7 @@ struct AttendArgs {
   float* lse_part;        // [rows, P]
   int32_t* err_flag;
   // a workgroup: tpw query tokens x 4 / tpw blocks of 32 heads (one group)
-  int s_q, heads, groups, max_pages, num_pages, max_T, tpw, token_groups, head_groups, num_splits;
+  int batch, s_q, heads, groups, max_pages, num_pages, max_T, tpw, token_groups, head_groups, num_splits;
   int row_words, rank;
   float scale;
 };
@@ -637,11 +637,56 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int s_q = A.s_q, heads = A.heads, groups = A.groups, max_pages = A.max_pages;
   const int head_groups = A.head_groups, token_groups = A.token_groups, tpw = A.tpw;
-  const int lid = xcd_local(blockIdx.x, gridDim.x);
-  const int hg = lid % head_groups;
-  const int tg = (lid / head_groups) % token_groups;
-  const int sp = (lid / (head_groups * token_groups)) % A.num_splits;
-  const int b = lid / (head_groups * token_groups * A.num_splits);
+  int hg, tg, sp, b;
+  const int items = token_groups * head_groups;  // workgroups of one (sequence, split) pair
+  bool ragged = false;
+  int tl = 0;  // length of sequence `lane` (GQA, batch <= 64)
+  if (GQA && A.batch <= 64) {
+    tl = lane < A.batch ? A.seq_lens[lane] : 0;
+    const int t0 = __builtin_amdgcn_readfirstlane(tl);
+    ragged = __ballot(lane < A.batch && tl != t0) != 0;
+  }
+  if (ragged) {
+    // The (sequence, split) pairs in order of length (longest first, ties by
+    // index) are dealt round robin over the 8 XCDs (block 8 j + x is the j-th
+    // of XCD x), the token and head blocks of a pair together: they read the
+    // same keys and share an L2, and every XCD holds the same mix of lengths,
+    // longest first.  Blocks past the last pair exit.
+    const int pos = blockIdx.x >> 3;
+    const int v = pos % items;
+    const int k = (pos / items) * 8 + (blockIdx.x & 7);
+    if (k >= A.batch * A.num_splits) return;
+    const int o = k / A.num_splits;
+    sp = k - o * A.num_splits;
+    hg = v % head_groups;
+    tg = v / head_groups;
+    int rank = 0;  // place of sequence `lane` in the order
+    for (int j = 0; j < A.batch; ++j) {
+      const int tj = __builtin_amdgcn_readlane(tl, j);
+      rank += (tj > tl || (tj == tl && j < lane)) ? 1 : 0;
+    }
+    // the ranks are a permutation of 0 .. batch - 1: exactly one lane has rank o
+    b = static_cast<int>(__builtin_ctzll(__ballot(lane < A.batch && rank == o)));
+  } else if (GQA) {
+    // equal lengths (or more than 64 sequences): XCD x takes the x-th eighth
+    // of the workgroups in order, so that the splits and blocks of one
+    // sequence share an L2 (the grid may hold more blocks: they exit)
+    const int n_items = A.batch * A.num_splits * items;
+    const int per_xcd = (n_items + 7) / 8;
+    if ((int)(blockIdx.x >> 3) >= per_xcd) return;
+    const int lid = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (lid >= n_items) return;
+    hg = lid % head_groups;
+    tg = (lid / head_groups) % token_groups;
+    sp = (lid / items) % A.num_splits;
+    b = lid / (items * A.num_splits);
+  } else {
+    const int lid = xcd_local(blockIdx.x, gridDim.x);
+    hg = lid % head_groups;
+    tg = (lid / head_groups) % token_groups;
+    sp = (lid / (head_groups * token_groups)) % A.num_splits;
+    b = lid / (head_groups * token_groups * A.num_splits);
+  }
   const int h0 = 32 * ((4 / tpw) * hg + w / tpw);  // this wave's heads
   const int g = h0 / (heads / groups);              // the same for every wave
   const int i = tpw * tg + w % tpw;                 // this wave's query token
@@ -1127,6 +1172,7 @@ hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const
   A.o = o;
   A.lse = lse;
   A.err_flag = err_flag;
+  A.batch = d.batch;
   A.s_q = d.s_q;
   A.heads = d.heads;
   A.groups = d.groups;
@@ -1183,6 +1229,7 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
   A.o_part = static_cast<_Float16*>(o_part);
   A.lse_part = lse_part;
   A.err_flag = err_flag;
+  A.batch = d.batch;
   A.s_q = d.s_q;
   A.heads = d.heads;
   A.groups = d.groups;
@@ -1194,8 +1241,11 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
   A.row_words = gqa_row_words(d);
   A.rank = d.rank;
   A.scale = d.softmax_scale;
-  hipLaunchKernelGGL(attend_kernel<true>,
-                     dim3(d.batch * num_splits * A.token_groups * A.head_groups), dim3(256), 0, s, A);
+  // (sequence, split) pairs padded to a multiple of 8 (one per XCD), each
+  // with its token and head blocks
+  const long long blocks = 8LL * cdiv(d.batch * num_splits, 8) * A.token_groups * A.head_groups;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attend_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || num_splits == 1) return e;
   const int rows = d.batch * d.s_q * d.heads;
