@@ -626,7 +626,10 @@ __device__ __forceinline__ int xcd_local(int id, int n) {
   return (id & 7) * (full >> 3) + (id >> 3);
 }
 
-template <bool GQA>
+// IDLE: s_q is not a multiple of the query tokens per workgroup, so some waves
+// have no query token (they then only move tiles); otherwise every wave works
+// and the loop has no branch for it.
+template <bool GQA, bool IDLE>
 __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[3 * AT_TILE];
   const int tid = threadIdx.x;
@@ -862,10 +865,10 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
   // 3).  Iteration kt: the loads of tile kt + 2 go out; the QK products of
   // tile kt + 1 run with the softmax of tile kt between them; then the PV
   // products of tile kt; tile kt + 2 is stored into the slot of tile kt - 1
-  // and one barrier ends the iteration.  Every wave takes every tile of the
-  // block: a tile past this wave's keys (or a wave past the last query token,
-  // vis = 0) is masked whole, which leaves its max, sum and accumulators as
-  // they were.
+  // and one barrier ends the iteration.  Every active wave takes every tile
+  // of the block: a tile past this wave's keys is masked whole, which leaves
+  // its max, sum and accumulators as they were; a wave past the last query
+  // token only loads and stores tiles.
   if (kt_lo < kt_hi) {
     fetch(kt_lo);  // in flight together with the query loads
     stash(0);
@@ -877,7 +880,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
 #pragma unroll
     for (int kk = 0; kk < AT_DR / 16; ++kk) asm volatile("" ::"v"(qrb[kk]));
     __syncthreads();
-    f32x16 sc = qk(std::integral_constant<int, 0>{}, [](auto) {});
+    f32x16 sc = {};
+    if (!IDLE || active) sc = qk(std::integral_constant<int, 0>{}, [](auto) {});
     stash(1);
     __syncthreads();
 
@@ -931,15 +935,17 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttendArgs A) {
       };
       // the two waves on a SIMD (two workgroups per CU): the one issuing
       // products goes first, the other's vector work fills the gaps
-      __builtin_amdgcn_s_setprio(1);
-      const f32x16 sc_next = qk(std::integral_constant<int, (P + 1) % 3>{}, soft);
-      pv(std::integral_constant<int, P>{}, pb);
-      __builtin_amdgcn_s_setprio(0);
+      if (!IDLE || active) {  // a wave past the last query token only moves tiles
+        __builtin_amdgcn_s_setprio(1);
+        const f32x16 sc_next = qk(std::integral_constant<int, (P + 1) % 3>{}, soft);
+        pv(std::integral_constant<int, P>{}, pb);
+        __builtin_amdgcn_s_setprio(0);
+        sc = sc_next;
+      }
       // tile kt + 2 goes to the slot of tile kt - 1, which every wave
       // finished reading before the previous barrier
       stash((P + 2) % 3);
       __syncthreads();
-      sc = sc_next;
     };
     for (int kt = kt_lo;;) {
       iteration(std::integral_constant<int, 0>{}, kt);
@@ -1183,7 +1189,8 @@ hipError_t launch_prefill_attend(const qkn_mla_dims& d, const void* q_hat, const
   A.num_splits = 1;
   A.rank = d.rank;
   A.scale = d.softmax_scale;
-  hipLaunchKernelGGL(attend_kernel<false>, dim3(d.batch * A.token_groups * A.head_groups), dim3(256),
+  auto kernel = d.s_q % A.tpw ? attend_kernel<false, true> : attend_kernel<false, false>;
+  hipLaunchKernelGGL(kernel, dim3(d.batch * A.token_groups * A.head_groups), dim3(256),
                      0, s, A);
   return hipGetLastError();
 }
@@ -1245,7 +1252,8 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
   // with its token and head blocks
   const long long blocks = 8LL * cdiv(d.batch * num_splits, 8) * A.token_groups * A.head_groups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attend_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, A);
+  auto kernel = d.s_q % A.tpw ? attend_kernel<true, true> : attend_kernel<true, false>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || num_splits == 1) return e;
   const int rows = d.batch * d.s_q * d.heads;
