@@ -431,90 +431,117 @@ __global__ __launch_bounds__(64 * GA_WAVES) void gqa_append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GQA-path append of a few tokens: one block of 16 waves per (token, group,
-// keys | values).  Thread t takes columns 4 (t % 32) .. + 3 over the latent
-// rows t / 32, t / 32 + 32, ... (all its weight loads, 16-byte pieces, in
-// flight together), accumulating in float32 with fused multiply-adds; the 32
-// row groups' partial sums are added in a fixed order through LDS.  Keys: the
-// sum of squares over the 128 entries gives 1 / RMS.  The key block of group 0
-// also writes the normed, rotated RoPE key.  A token with an out-of-range
-// sequence, position or page is skipped and reported.
+// GQA-path append of a few tokens: one block of 16 waves per (TPB consecutive
+// tokens, group, keys | values).  Thread t takes columns 4 (t % 32) .. + 3 over
+// the latent rows t / 32, t / 32 + 32, ... (all its weight loads, 16-byte
+// pieces, in flight together) and applies each weight row to the TPB tokens'
+// latents (staged in LDS), accumulating in float32 with fused multiply-adds;
+// the 32 row groups' partial sums are added in a fixed order through LDS.
+// Keys: the sum of squares over the 128 entries gives 1 / RMS.  The key block
+// of group 0 also writes the normed, rotated RoPE keys.  A token with an
+// out-of-range sequence, position or page is skipped and reported.
 // ---------------------------------------------------------------------------
 constexpr int GS_RG = 32;                  // row groups (d = 128: 32 column quads)
 constexpr int GS_MAX_ROWS = 512 / GS_RG;   // rows per thread, all in flight (r <= 512)
 
+template <int TPB>
 __global__ __launch_bounds__(1024) void gqa_append_small_kernel(
     const float* __restrict__ c_new, const float* __restrict__ k_rope_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ block_table, const float* __restrict__ w_k,
     const float* __restrict__ w_v, const float* __restrict__ gamma_k,
     const float* __restrict__ gamma_kr, uint16_t* __restrict__ kvg, int32_t* __restrict__ err_flag,
-    int batch, int groups, int rank, int max_pages, int num_pages, float eps, float theta) {
-  __shared__ float4 part[GS_RG][GA_D / 4];
-  __shared__ float red[2];
-  __shared__ int slot_s, pos_s;
+    int n_tokens, int batch, int groups, int rank, int max_pages, int num_pages, float eps,
+    float theta) {
+  __shared__ float4 part[TPB][GS_RG][GA_D / 4];
+  __shared__ float lat[TPB][512];  // the tokens' latents as the latent cache stores them
+  __shared__ float red[TPB][2];
+  __shared__ int slot_s[TPB], pos_s[TPB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n = blockIdx.x, g = blockIdx.y;
+  const int n0 = blockIdx.x * TPB, g = blockIdx.y;
   const bool values = blockIdx.z == 1;
   const int cq = tid % GS_RG, rg = tid / GS_RG;  // column quad, row group
-  // this thread's weight loads go out before the slot lookup resolves
+  // this thread's weight loads go out before the latents and slot lookups
   const float* wg = (values ? w_v : w_k) + (size_t)g * rank * GA_D + 4 * cq;
   const int nrows = (rank - rg + GS_RG - 1) / GS_RG;
   float4 wv[GS_MAX_ROWS];
-  float cv[GS_MAX_ROWS];
 #pragma unroll
   for (int u = 0; u < GS_MAX_ROWS; ++u) {
     const int m = rg + GS_RG * u;
     wv[u] = u < nrows ? *reinterpret_cast<const float4*>(wg + (size_t)m * GA_D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    cv[u] = u < nrows ? c_new[(size_t)n * rank + m] : 0.f;
   }
-  if (tid == 0) {
-    const int b = seq_idx[n], p = pos[n];
-    int slot = -1;
-    if (b >= 0 && b < batch && p >= 0 && p < max_pages * QKN_MLA_PAGE_SIZE) {
-      const int pg = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
-      if (pg >= 0 && pg < num_pages) slot = pg * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
+  for (int e = tid; e < TPB * rank; e += 1024) {
+    const int t = e / rank, m = e % rank;
+    const float c = n0 + t < n_tokens ? c_new[(size_t)(n0 + t) * rank + m] : 0.f;
+    lat[t][m] = static_cast<float>(static_cast<__bf16>(c));  // bf16, nearest-even
+  }
+  if (tid < TPB) {
+    const int n = n0 + tid;
+    int slot = -1, p = 0;
+    if (n < n_tokens) {
+      const int b = seq_idx[n];
+      p = pos[n];
+      if (b >= 0 && b < batch && p >= 0 && p < max_pages * QKN_MLA_PAGE_SIZE) {
+        const int pg = block_table[(size_t)b * max_pages + p / QKN_MLA_PAGE_SIZE];
+        if (pg >= 0 && pg < num_pages) slot = pg * QKN_MLA_PAGE_SIZE + p % QKN_MLA_PAGE_SIZE;
+      }
+      if (slot < 0 && err_flag && g == 0 && !values) atomicOr(err_flag, QKN_FLAG_INDEX);
     }
-    if (slot < 0 && err_flag && g == 0 && !values) atomicOr(err_flag, QKN_FLAG_INDEX);
-    slot_s = slot;
-    pos_s = p;
+    slot_s[tid] = slot;
+    pos_s[tid] = p;
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+  float4 acc[TPB];
+#pragma unroll
+  for (int t = 0; t < TPB; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < GS_MAX_ROWS; ++u) {
-    // the latent as the latent cache stores it (bf16, nearest-even)
-    const float c = static_cast<float>(static_cast<__bf16>(cv[u]));
-    acc.x = fmaf(c, wv[u].x, acc.x);
-    acc.y = fmaf(c, wv[u].y, acc.y);
-    acc.z = fmaf(c, wv[u].z, acc.z);
-    acc.w = fmaf(c, wv[u].w, acc.w);
+    const int m = rg + GS_RG * u;
+    if (u < nrows) {
+#pragma unroll
+      for (int t = 0; t < TPB; ++t) {
+        const float c = lat[t][m];
+        acc[t].x = fmaf(c, wv[u].x, acc[t].x);
+        acc[t].y = fmaf(c, wv[u].y, acc[t].y);
+        acc[t].z = fmaf(c, wv[u].z, acc[t].z);
+        acc[t].w = fmaf(c, wv[u].w, acc[t].w);
+      }
+    }
   }
-  part[rg][cq] = acc;
+#pragma unroll
+  for (int t = 0; t < TPB; ++t) part[t][rg][cq] = acc[t];
   __syncthreads();
-  const int slot = slot_s;
-  if (slot < 0) return;  // uniform
   const int row_words = 2 * GA_D * groups + GA_DR;
-  float x = 0.f;  // waves 0 and 1: column tid
-  if (tid < GA_D) {
-    const float* pc = reinterpret_cast<const float*>(&part[0][0]) + tid;
+  // threads t * 128 + j (t < TPB): column j of token t
+  const int tt = tid / GA_D, j = tid % GA_D;
+  float x = 0.f;
+  if (tt < TPB) {
+    const float* pc = reinterpret_cast<const float*>(&part[tt][0][0]) + j;
 #pragma unroll
     for (int q = 0; q < GS_RG; ++q) x += pc[q * GA_D];
   }
   if (!values) {  // uniform over the block
-    if (tid < GA_D) {
+    if (tt < TPB) {
       const float ss = wave_sum(x * x);
-      if (lane == 0) red[w] = ss;
+      if (lane == 0) red[tt][(tid >> 6) & 1] = ss;
     }
     __syncthreads();
   }
-  if (tid < GA_D) {
-    if (!values) x = x * (1.0f / sqrtf((red[0] + red[1]) / (float)GA_D + eps)) * gamma_k[(size_t)g * GA_D + tid];
-    if (fabsf(x) >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
-    const _Float16 hx = static_cast<_Float16>(x);
-    kvg[(size_t)slot * row_words + 2 * GA_D * g + (values ? GA_D : 0) + tid] = __builtin_bit_cast(uint16_t, hx);
+  if (tt < TPB) {
+    const int slot = slot_s[tt];
+    if (slot >= 0) {
+      if (!values)
+        x = x * (1.0f / sqrtf((red[tt][0] + red[tt][1]) / (float)GA_D + eps)) * gamma_k[(size_t)g * GA_D + j];
+      if (fabsf(x) >= 65520.f && err_flag) atomicOr(err_flag, QKN_FLAG_PARTIAL_RANGE);
+      const _Float16 hx = static_cast<_Float16>(x);
+      kvg[(size_t)slot * row_words + 2 * GA_D * g + (values ? GA_D : 0) + j] = __builtin_bit_cast(uint16_t, hx);
+    }
   }
-  if (values || g != 0 || w != 2) return;
-  // the RoPE key (wave 2 of the key block of group 0)
+  // the RoPE keys: wave 2 t of the key block of group 0 takes token t (the
+  // block has 16 waves, TPB <= 8)
+  if (values || g != 0 || (w & 1) || w / 2 >= TPB) return;
+  const int t = w / 2, n = n0 + t, slot = slot_s[t];
+  if (slot < 0) return;  // uniform over the wave
   const float xr = k_rope_new[(size_t)n * GA_DR + lane];
   const float sr = wave_sum(fmaf(xr, xr, 0.f));
   const float inv = 1.0f / sqrtf(sr / (float)GA_DR + eps);
@@ -522,7 +549,7 @@ __global__ __launch_bounds__(1024) void gqa_append_small_kernel(
   const float x2 = __shfl(xn, lane + GA_DR / 2);
   if (lane < GA_DR / 2) {
     float c = 1.f, sn = 0.f;
-    if (theta != 0.f) rope_cos_sin<false>(pos_s, lane, GA_DR, theta, &c, &sn);
+    if (theta != 0.f) rope_cos_sin<false>(pos_s[t], lane, GA_DR, theta, &c, &sn);
     uint16_t* out = kvg + (size_t)slot * row_words + 2 * GA_D * groups;
     out[lane] = f32_to_bf16(xn * c - x2 * sn);
     out[lane + GA_DR / 2] = f32_to_bf16(x2 * c + xn * sn);
@@ -1208,9 +1235,14 @@ hipError_t launch_gqa_append(const qkn_mla_dims& d, int32_t n_tokens, const floa
                              const float* gamma_k, const float* gamma_kr, void* kvg,
                              int32_t* err_flag, hipStream_t s) {
   if (n_tokens <= kGqaSmallAppend && d.rank <= GS_RG * GS_MAX_ROWS) {
-    hipLaunchKernelGGL(gqa_append_small_kernel, dim3(n_tokens, d.groups, 2), dim3(1024), 0, s, c_new,
+    // tokens per block: each block streams all of its W_g once, so several
+    // tokens share it once there are more blocks than CUs
+    const int tpb = n_tokens >= 256 ? 4 : n_tokens >= 128 ? 2 : 1;
+    auto kernel = tpb == 4 ? gqa_append_small_kernel<4>
+                : tpb == 2 ? gqa_append_small_kernel<2> : gqa_append_small_kernel<1>;
+    hipLaunchKernelGGL(kernel, dim3(cdiv(n_tokens, tpb), d.groups, 2), dim3(1024), 0, s, c_new,
                        k_rope_new, seq_idx, pos, block_table, w_k, w_v, gamma_k, gamma_kr,
-                       static_cast<uint16_t*>(kvg), err_flag, d.batch, d.groups, d.rank,
+                       static_cast<uint16_t*>(kvg), err_flag, n_tokens, d.batch, d.groups, d.rank,
                        d.max_pages_per_seq, d.num_pages, d.eps, d.rope_theta);
     return hipGetLastError();
   }

@@ -38,6 +38,8 @@ CASES = [
 APPEND_CASES = [(n, kw) for n, kw, _ in CASES] + [
     ("grouped", dict(batch=2, seq_len=90, rank=256, heads=64, groups=2)),  # r = 256, G = 2
     ("grouped", dict(batch=2, seq_len=400)),  # G = 4, a history of 798 tokens: the matrix-core route
+    ("dsv3", dict(batch=3, seq_len=52)),   # a history of 153 tokens: two per block, a ragged last block
+    ("dsv3", dict(batch=3, seq_len=110)),  # 327 tokens: four per block, a ragged last block
 ]
 SENTINEL = 0x7E01
 
@@ -62,7 +64,7 @@ def _token_slots(wl, inp):
 @pytest.mark.parametrize("name,kw", APPEND_CASES)
 def test_gqa_append_image(name, kw):
     """History in bulk (more than 512 tokens in one call take the matrix-core
-    route, fewer one block per token), then the s_q new tokens: every written
+    route, fewer blocks of 1, 2 or 4 tokens), then the s_q new tokens: every written
     key and value
     within 2^-11 |x| + 2^-25 (half rounding) of exact, plus the float32 sum's
     gamma_{3r+2} sum_m |c_m W_mj| (times gamma_k alpha for a key, plus the
