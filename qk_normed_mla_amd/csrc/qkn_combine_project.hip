@@ -30,6 +30,11 @@
 //            In the two-pass form, when the row tiles alone would not fill the
 //            chip, the d_v columns are split over 2 or 4 blocks per tile (each
 //            streams only its columns of W^V_g).
+// 128-row fused kernel (project_gemm): the fused form when d_v = 128, r is a
+// multiple of 64, there are at most 4 splits and a group has a multiple of 128
+// heads; the same merge and the same split products, but over 128 rows per
+// block with the merge done chunk by chunk of the latent, so W^V_g is streamed
+// once per 128 rows.
 // Generic kernel (every other shape): one block per query row, the row from
 // o_latent in LDS, o_j = sum_m L_m W^V_g[m, j] in float32 in index order.
 #include <math.h>
@@ -288,6 +293,173 @@ __global__ __launch_bounds__(64 * WAVES) void project_mfma(
   }
 }
 
+// Fused form for 128-row tiles within one group (d_v = 128, r a multiple of 64,
+// at most 4 splits): one block of 8 waves per 128 query rows, the latent taken
+// in chunks of GK = 64.  First every wave forms the log-sum-exp statistics of
+// 16 rows exactly as merge_row does (the same loads, reductions and weights),
+// keeping each split's weight (and whether it is empty) in LDS.  Then per
+// chunk: thread t merges latents 8 (t % 8) .. + 7 of rows t / 8 and t / 8 + 64
+// from the half partials, splits in order, as merge_row does (so o_latent is
+// the combine kernel's bits), writes them to o_latent, and stores their bf16
+// hi/lo words in LDS in the reduction order of the products; the chunk of
+// W^V_g goes to LDS as hi/lo words the same way the 32-row kernel stages it.
+// Wave w computes the 32 x 32 output tiles (w / 2, 2 (w % 2)) and (w / 2,
+// 2 (w % 2) + 1) with hi.hi + hi.lo + lo.hi per step.  The next chunk's
+// partial and W^V_g loads are in flight during the current chunk's products.
+// W^V_g is streamed once per 128 rows (four times less than 32-row blocks).
+constexpr int GT = 128;  // rows per block
+constexpr int GK = 64;   // latents per chunk
+constexpr int GD = 128;  // output columns (d_v)
+constexpr int G_MAXP = 4;
+constexpr int GA_ROW = GK + 8;    // bf16 per staged row of the rows' words (16 bytes of padding)
+constexpr int GW_ROW = GD + W_PAD;
+constexpr size_t G_LDS = 2 * (size_t)GT * GA_ROW * 2 + 2 * (size_t)GK * GW_ROW * 2 + (size_t)GT * G_MAXP * 4 + GT * 4;
+
+// position of latent k (within its chunk) among the staged words: in each
+// 16-group the order is k 0-3, 8-11, 4-7, 12-15, so that lane half hh reads the
+// 8 entries 4 hh + (0..3), 8 + 4 hh + (0..3) of a step as one 16-byte piece
+__device__ __forceinline__ int gpos(int k) { return (k & ~15) | (k & 3) | ((k & 8) >> 1) | ((k & 4) << 1); }
+
+__global__ __launch_bounds__(64 * WAVES) void project_gemm(
+    const _Float16* __restrict__ o_part, const float* __restrict__ lse_part,
+    const float* __restrict__ w_v, float* __restrict__ o_lat, float* __restrict__ lse_out,
+    float* __restrict__ o_out, int num_splits, int rank, int heads, int groups) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __bf16* Ah = reinterpret_cast<__bf16*>(smem);
+  __bf16* Al = Ah + GT * GA_ROW;
+  __bf16* Wh = Al + GT * GA_ROW;
+  __bf16* Wl = Wh + GK * GW_ROW;
+  float* wgt = reinterpret_cast<float*>(Wl + GK * GW_ROW);  // [GT][G_MAXP] split weights
+  int* skip = reinterpret_cast<int*>(wgt + GT * G_MAXP);    // [GT] bit p: split p empty
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, G = (lane >> 4) & 1;
+  const int row0 = blockIdx.x * GT;
+  const int g = (row0 % heads) / (heads / groups);
+  const int P = num_splits;
+
+  // ---- statistics of 16 rows per wave (merge_row's first part) ----
+  {
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = row0 + 16 * wave + q;
+      x[q] = lane < P ? lse_part[(size_t)row * P + lane] : -INFINITY;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int lr = 16 * wave + q;
+      // lanes 64 u + lane hold split p0 + 64 u: with P <= 64 only u = 0 is live
+      const float M = wave_max(fmaxf(fmaxf(fmaxf(x[q], -INFINITY), -INFINITY), -INFINITY));
+      float sl = 0.f;
+      sl += expf(x[q] - M);
+      sl += expf(-INFINITY - M);
+      sl += expf(-INFINITY - M);
+      sl += expf(-INFINITY - M);
+      const float s = wave_sum(sl);
+      const bool empty = M == -INFINITY;
+      const float lse = empty ? -INFINITY : M + logf(s);
+      if (lane == 0) lse_out[row0 + lr] = lse;
+      const bool skip_p = empty || x[q] == -INFINITY;
+      const unsigned long long sk = __ballot(lane < P && skip_p);
+      if (lane < P) wgt[lr * G_MAXP + lane] = skip_p ? 0.f : expf(x[q] - lse);
+      if (lane == 0) skip[lr] = static_cast<int>(sk & 0xF);
+    }
+  }
+
+  // ---- chunk loads: partials of items (row t / 8 + 64 u, latents 8 (t % 8)
+  // .. + 7) and W^V_g rows k0 .. k0 + GK - 1 (16 floats per thread) ----
+  const int it_row = tid >> 3, it_c = 8 * (tid & 7);
+  f16x8 pv[2][G_MAXP];
+  float4 wv[GK * GD / 4 / (64 * WAVES)];
+  const float* wg = w_v + (size_t)g * rank * GD;
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = row0 + it_row + 64 * u;
+#pragma unroll
+      for (int p = 0; p < G_MAXP; ++p)
+        pv[u][p] = p < P ? *reinterpret_cast<const f16x8*>(o_part + ((size_t)row * P + p) * rank + k0 + it_c)
+                         : f16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < GK * GD / 4 / (64 * WAVES); ++u) {
+      const int e = tid + u * 64 * WAVES;
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)(k0 + e / (GD / 4)) * GD + 4 * (e % (GD / 4)));
+    }
+  };
+
+  const int rt = wave >> 1, ct0 = 2 * (wave & 1);
+  const int tr_off = (4 * hh + (l16 >> 2)) * GW_ROW + 16 * G + 4 * (l16 & 3);
+  f32x16 acc[2] = {};
+  __syncthreads();  // the weights are in LDS
+  load(0);
+  for (int k0 = 0; k0 < rank; k0 += GK) {
+    // merge, o_latent, the rows' words
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int lr = it_row + 64 * u;
+      const int sk = skip[lr];
+      float a[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = 0.f;
+#pragma unroll
+      for (int p = 0; p < G_MAXP; ++p) {
+        if (p >= P || ((sk >> p) & 1)) continue;
+        const float w = wgt[lr * G_MAXP + p];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = fmaf(w, static_cast<float>(pv[u][p][j]), a[j]);
+      }
+      float4* gp = reinterpret_cast<float4*>(o_lat + (size_t)(row0 + lr) * rank + k0 + it_c);
+      gp[0] = make_float4(a[0], a[1], a[2], a[3]);
+      gp[1] = make_float4(a[4], a[5], a[6], a[7]);
+      bf16x4 h0, l0, h1, l1;
+      split4(make_float4(a[0], a[1], a[2], a[3]), h0, l0);
+      split4(make_float4(a[4], a[5], a[6], a[7]), h1, l1);
+      const int at0 = lr * GA_ROW + gpos(it_c), at1 = lr * GA_ROW + gpos(it_c + 4);
+      *reinterpret_cast<bf16x4*>(Ah + at0) = h0;
+      *reinterpret_cast<bf16x4*>(Al + at0) = l0;
+      *reinterpret_cast<bf16x4*>(Ah + at1) = h1;
+      *reinterpret_cast<bf16x4*>(Al + at1) = l1;
+    }
+#pragma unroll
+    for (int u = 0; u < GK * GD / 4 / (64 * WAVES); ++u) {
+      const int e = tid + u * 64 * WAVES;
+      bf16x4 hi, lo;
+      split4(wv[u], hi, lo);
+      const int at = (e / (GD / 4)) * GW_ROW + 4 * (e % (GD / 4));
+      *reinterpret_cast<bf16x4*>(Wh + at) = hi;
+      *reinterpret_cast<bf16x4*>(Wl + at) = lo;
+    }
+    if (k0 + GK < rank) load(k0 + GK);  // in flight during this chunk's products
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < GK / 16; ++st) {
+      const int ao = (32 * rt + l32) * GA_ROW + 16 * st + 8 * hh;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ah + ao);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + ao);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int off = tr_off + 16 * st * GW_ROW + 32 * (ct0 + c);
+        const bf16x8 bh = __builtin_shufflevector(lds_read_tr(Wh + off), lds_read_tr(Wh + off + 8 * GW_ROW),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 bl = __builtin_shufflevector(lds_read_tr(Wl + off), lds_read_tr(Wl + off + 8 * GW_ROW),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        acc[c] = mfma(ah, bh, acc[c]);
+        acc[c] = mfma(ah, bl, acc[c]);
+        acc[c] = mfma(al, bh, acc[c]);
+      }
+    }
+    __syncthreads();  // every read of this chunk's words done
+  }
+  // D[m][n]: m = r % 4 + 8 (r / 4) + 4 hh, n = l32
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      o_out[(size_t)(row0 + 32 * rt + (r & 3) + 8 * (r >> 2) + 4 * hh) * GD + 32 * (ct0 + c) + l32] = acc[c][r];
+}
+
 // one block per query row
 __global__ __launch_bounds__(256) void project_generic(const float* __restrict__ o_lat,
                                                        const float* __restrict__ w_v,
@@ -353,6 +525,15 @@ hipError_t launch_combine_project(const qkn_mla_dims& d, int num_splits, const v
   const int dvb = d.head_dim / cs;
   const int kc = chunk_rows(dvb);
   const size_t lds = project_lds_bytes(dvb);
+  if (fuse && d.head_dim == GD && d.rank % GK == 0 && num_splits <= G_MAXP &&
+      (d.heads / d.groups) % GT == 0) {
+    const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&project_gemm), (int)G_LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(project_gemm, dim3(n_rows / GT), dim3(64 * WAVES), G_LDS, s,
+                       static_cast<const _Float16*>(o_part), lse_part, w_v, o_lat, lse, o,
+                       num_splits, d.rank, d.heads, d.groups);
+    return hipGetLastError();
+  }
   if (fuse) {
     hipError_t e = set_lds_limit<true>();
     if (e != hipSuccess) return e;

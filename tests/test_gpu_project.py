@@ -116,6 +116,9 @@ def test_combine_project_forms(name):
     ("grouped", dict(batch=1, seq_len=100, num_splits=20)),  # more splits than the fused form takes
     ("dsv3", dict(batch=1, seq_len=100, head_dim=64)),     # d_v = 64: 4 reduction slices
     ("dsv3", dict(batch=1, seq_len=100, head_dim=96)),     # d_v = 96: vector path
+    ("dsv3", dict(batch=2, seq_len=100, num_splits=3)),    # 128-row fused tiles, 3 splits
+    ("dsv3", dict(batch=1, seq_len=64, num_splits=4)),     # 128-row fused tiles, empty splits
+    ("mtp", dict(batch=2, seq_len=90, rank=256, num_splits=2)),  # 128-row fused tiles, r = 256
 ])
 def test_combine_project_shapes(name, kw):
     wl = P.small(name, **kw)
