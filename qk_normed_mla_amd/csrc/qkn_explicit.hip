@@ -558,15 +558,16 @@ __global__ __launch_bounds__(1024) void gqa_append_small_kernel(
 
 // ---------------------------------------------------------------------------
 // attention: one workgroup per (sequence, key split, 4 consecutive query
-// tokens, 32 heads of one group); wave w takes query token i0 + w with the 32
-// heads as its rows (lane l % 32).  Keys stream in tiles of 32 (k^ 8 KB, k^R 4 KB, v 8 KB)
-// through two LDS buffers: the next tile's loads are in flight during the
-// current tile's products.  Per tile and wave:
+// tokens, 32 heads of one group) -- or fewer tokens and more 32-head blocks of
+// the group when s_q is small; wave w takes one query token with 32 heads as
+// its rows (lane l % 32).  Keys stream in tiles of 32 (k^ 8 KB, k^R 4 KB, v 8 KB)
+// through three LDS slots as a software pipeline (the loop below).  Per tile
+// and wave:
 //   S^T[32 keys x 32 heads] = K^ q^^T + K^R q^R^T (12 products; A a 16-byte
 //     key row read per lane, B the queries in registers),
-//   online softmax in base 2 (running max per head, the accumulator rescaled
-//     when it rises; probabilities to the products rounded to bf16 and the
-//     normaliser summed from the same rounded values),
+//   online softmax in base 2 against a lazily moved reference (probabilities
+//     at most 2^8, rounded to half; the normaliser summed from the same rounded
+//     values),
 //   O^T[128 x 32 heads] += V^T P^T (8 products; V^T read with
 //     ds_read_b64_tr_b16 from the row-major tile).
 // Rows of 256 bytes store chunk c of key t at chunk c ^ kswz(t) (RoPE rows:
