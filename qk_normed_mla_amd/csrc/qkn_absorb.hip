@@ -415,6 +415,213 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
   }
 }
 
+// Wave-independent variant for d = 128, rank a multiple of 128 and d_R <= 128
+// (the workloads' shapes).  A block of 4 waves stages one 128-column block of
+// W^K_g, times gamma_q gamma_k, as hi/lo bf16 words in LDS (69.6 KB, two
+// blocks per CU) and needs no barrier after that: each wave takes whole
+// 32-row tiles of q~ on its own.  The product is taken transposed,
+// q~^T = W . q^T, so that the W rows are the first operand (read from LDS)
+// and the query rows the second one, loaded straight from HBM into the
+// operand layout (lane l: row l % 32, head-dim entries 16 s + 8 (l / 32) ..
+// + 7 of step s) and split in registers; the accumulator then holds, per lane,
+// runs of four consecutive q~ columns of one row, stored as 8-byte pieces.
+// The next tile's query loads go out step by step as the current tile's
+// operand words are formed.  alpha^q comes from the same registers (the two
+// lanes of a row hold its two halves); the RoPE query of a share of each
+// tile's rows (per column block) is formed one row per wave step with lanes
+// over the pairs (j, j + d_R / 2), its loads issued with the tile's first
+// products.
+constexpr int WCB = 128;          // q~ columns per block
+constexpr int WLD = 128 + 8;      // LDS row of bf16 words (272 B: as SLD)
+constexpr int WAVE_LDS = 2 * WCB * WLD * 2;  // bytes: hi and lo words
+constexpr int WROWS = 32;         // query rows per wave tile
+constexpr int RCH = 8;            // RoPE rows per chunk
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void absorb_wave(
+    const float* __restrict__ q, const float* __restrict__ q_rope,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ w_k,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const float* __restrict__ gamma_qr, uint16_t* __restrict__ q_tilde,
+    float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int rows_per_group,
+    int heads, int heads_per_group, int rank, int rope_dim, float eps, float theta) {
+  constexpr int D = 128;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint16_t* Wh = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Wl = Wh + WCB * WLD;
+  const int g = blockIdx.z, cb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const int m0 = cb * WCB;
+  const int n_tiles = cdiv(rows_per_group, WROWS);
+  const int t_step = gridDim.x * 4;
+  const int t0 = blockIdx.x * 4 + wave;
+
+  auto grow_of = [&](int n) {  // global query row of group row n, -1 past the end
+    const int bi = n / heads_per_group, hl = n - bi * heads_per_group;
+    return n < rows_per_group ? bi * heads + g * heads_per_group + hl : -1;
+  };
+  // Query operand of tile t, lane (r, h): row r of the tile, entries
+  // 16 s + 8 h .. + 7 of step s.  A row past the end reads row 0 instead: a
+  // q~ row depends on its own query row only, and such rows are not stored.
+  auto row_ptr = [&](int t) {
+    const int gr = grow_of(t * WROWS + r);
+    return q + (size_t)(gr >= 0 ? gr : 0) * D + 8 * h;
+  };
+  float4 raw[8][2];
+  const float* qp = row_ptr(t0 < n_tiles ? t0 : 0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    raw[s][0] = *reinterpret_cast<const float4*>(qp + 16 * s);
+    raw[s][1] = *reinterpret_cast<const float4*>(qp + 16 * s + 4);
+  }
+
+  // stage W^K_g rows m0 .. m0 + 127 times gamma_q gamma_k as hi/lo words
+  {
+    const float* wg = w_k + ((size_t)g * rank + m0) * D;
+    const float* gk = gamma_k + (size_t)g * D;
+    const int k4 = 4 * (tid & 31);
+    const float4 f = make_float4(gamma_q[k4] * gk[k4], gamma_q[k4 + 1] * gk[k4 + 1],
+                                 gamma_q[k4 + 2] * gk[k4 + 2], gamma_q[k4 + 3] * gk[k4 + 3]);
+    float4 wv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)((tid >> 5) + 8 * u) * D + k4);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      float4 v = wv[u];
+      v.x *= f.x;
+      v.y *= f.y;
+      v.z *= f.z;
+      v.w *= f.w;
+      bf16x4 hi, lo;
+      split4(v, hi, lo);
+      const int o = ((tid >> 5) + 8 * u) * WLD + k4;
+      *reinterpret_cast<bf16x4*>(&Wh[o]) = hi;
+      *reinterpret_cast<bf16x4*>(&Wl[o]) = lo;
+    }
+  }
+  __syncthreads();  // the only barrier: from here on the waves are independent
+
+  // RoPE rows of each tile for this column block: rows rr_lo .. rr_hi - 1,
+  // lane j < d_R / 2 on the pair (j, j + d_R / 2)
+  const int share = cdiv(WROWS, (int)gridDim.y);
+  const int rr_lo = min(WROWS, cb * share), rr_hi = min(WROWS, rr_lo + share);
+  const int half = rope_dim / 2;
+  const bool jl = lane < half;
+  const int ja = jl ? lane : 0, jb = jl ? lane + half : 0;  // lanes past d_R / 2 read entry 0
+  const float ga = jl ? gamma_qr[ja] : 0.f, gb = jl ? gamma_qr[jb] : 0.f;
+  const double omega = (jl && theta != 0.f) ? rope_omega(lane, rope_dim, theta) : 0.0;
+  float cs = 1.f, sn = 0.f;
+  int angle_tok = -1;
+  float xa[RCH], xb[RCH];
+  auto rope_load = [&](int n0, int c0) {
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int lr = min(c0 + u, WROWS - 1);
+      const int gr = grow_of(n0 + lr);  // uniform
+      const float* x = q_rope + (size_t)(gr >= 0 ? gr : 0) * rope_dim;
+      xa[u] = x[ja];
+      xb[u] = x[jb];
+    }
+  };
+  auto rope_finish = [&](int n0, int c0) {
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int lr = c0 + u;
+      if (lr >= rr_hi) break;  // uniform
+      const int n = n0 + lr;
+      const int gr = grow_of(n);
+      if (gr < 0) break;  // uniform: rows past the end come last
+      const int tok = n / heads_per_group;
+      if (tok != angle_tok) {
+        cs = 1.f;
+        sn = 0.f;
+        if (jl && theta != 0.f) rope_cos_sin_at<false>(q_pos[tok], omega, &cs, &sn);
+        angle_tok = tok;
+      }
+      const float a = jl ? xa[u] : 0.f, b = jl ? xb[u] : 0.f;
+      const float sr = wave_sum(fmaf(a, a, b * b));
+      const float inv = 1.0f / sqrtf(sr / (float)rope_dim + eps);
+      if (jl) {
+        const float x1 = a * inv * ga, x2 = b * inv * gb;
+        uint16_t* out = q_rope_out + (size_t)gr * rope_dim;
+        out[lane] = f32_to_bf16(x1 * cs - x2 * sn);
+        out[lane + half] = f32_to_bf16(x2 * cs + x1 * sn);
+      }
+    }
+  };
+  const bool has_rope = rope_dim > 0 && rr_lo < rr_hi;
+
+  for (int t = t0; t < n_tiles; t += t_step) {
+    // the W words are read from LDS again for every tile (hoisted out of the
+    // loop they would need 256 registers)
+    asm volatile("" ::: "memory");
+    const int n0 = t * WROWS;
+    const int gr = grow_of(n0 + r);
+    if (has_rope) rope_load(n0, rr_lo);
+    // the next tile's rows (on the last tile: this tile's again, unused)
+    const float* np = row_ptr(t + t_step < n_tiles ? t + t_step : t);
+    f32x16 acc[4] = {};
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float4 a0 = raw[s][0], a1 = raw[s][1];
+      ss = fmaf(a0.x, a0.x, fmaf(a0.y, a0.y, fmaf(a0.z, a0.z, fmaf(a0.w, a0.w, ss))));
+      ss = fmaf(a1.x, a1.x, fmaf(a1.y, a1.y, fmaf(a1.z, a1.z, fmaf(a1.w, a1.w, ss))));
+      bf16x4 h0, l0, h1, l1;
+      split4(a0, h0, l0);
+      split4(a1, h1, l1);
+      const bf16x8 bh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 bl = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+      raw[s][0] = *reinterpret_cast<const float4*>(np + 16 * s);
+      raw[s][1] = *reinterpret_cast<const float4*>(np + 16 * s + 4);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int o = (32 * ct + r) * WLD + 16 * s + 8 * h;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Wh[o]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Wl[o]);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[ct], 0, 0, 0);
+      }
+    }
+    // alpha^q of row r: the lanes r and r + 32 hold its two halves
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      const float tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      if (cb == 0 && h == 0 && gr >= 0) alpha_q[gr] = 1.0f / sqrtf(tot / (float)D + eps);
+    }
+    // D[c][row]: lane (r, h), register 4 a + b holds column 32 ct + 8 a + 4 h + b
+    // of row r.  For a = 2 p, 2 p + 1 the two lanes of a row trade halves
+    // (v_permlane32_swap), so that lane (r, h) holds columns 16 p + 8 h .. + 7
+    // and stores them as one 16-byte piece.
+    {
+      uint16_t* out = q_tilde + (size_t)(gr >= 0 ? gr : 0) * rank + m0 + 8 * h;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const f32x4 v0 = {acc[ct][8 * p], acc[ct][8 * p + 1], acc[ct][8 * p + 2], acc[ct][8 * p + 3]};
+          const f32x4 v1 = {acc[ct][8 * p + 4], acc[ct][8 * p + 5], acc[ct][8 * p + 6], acc[ct][8 * p + 7]};
+          const bf16x4 w0 = __builtin_convertvector(v0, bf16x4), w1 = __builtin_convertvector(v1, bf16x4);
+          const uint2 x = __builtin_bit_cast(uint2, w0), y = __builtin_bit_cast(uint2, w1);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+          if (gr >= 0)
+            *reinterpret_cast<uint4*>(out + 32 * ct + 16 * p) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+    }
+    if (has_rope) {
+      rope_finish(n0, rr_lo);
+      for (int c0 = rr_lo + RCH; c0 < rr_hi; c0 += RCH) {  // shares larger than one chunk
+        rope_load(n0, c0);
+        rope_finish(n0, c0);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // float32 path
 // ---------------------------------------------------------------------------
@@ -495,6 +702,25 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
     if (d.rope_dim / 2 > 128) return hipErrorInvalidValue;
     const int hpg = d.heads / d.groups;
     const int rows_per_group = d.batch * d.s_q * hpg;
+    const int wave_cols = d.rank / WCB, n_tiles = cdiv(rows_per_group, WROWS);
+    if (d.head_dim == 128 && d.rank % WCB == 0 && d.rope_dim <= 128 &&
+        (long)rows_per_group * wave_cols * d.groups >= 65536) {
+      // Enough 32-row tiles for every wave of two blocks per CU to take
+      // about two (from 16384 query rows at r = 512); below that the 8-wave
+      // 64-row tiles keep more waves busy.  The column blocks of one row range
+      // sit on one XCD (block ids that differ by a multiple of 8) and share
+      // its L2.
+      int nb = std::max(1, std::min(cdiv(n_tiles, 4), 512 / (wave_cols * d.groups)));
+      if (nb >= 8) nb -= nb % 8;
+      const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&absorb_wave), WAVE_LDS);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(absorb_wave, dim3(nb, wave_cols, d.groups), dim3(256), WAVE_LDS, s, q,
+                         q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr,
+                         static_cast<uint16_t*>(q_tilde), alpha_q,
+                         static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,
+                         d.rank, d.rope_dim, d.eps, d.rope_theta);
+      return hipGetLastError();
+    }
     // about one block per CU: a block takes several row tiles when there are
     // more (the W^K_g tile is staged once per block when d <= 128)
     const int row_tiles = cdiv(rows_per_group, TM), col_blocks = cdiv(d.rank, TN);

@@ -169,7 +169,12 @@ def test_absorb_query(name):
 # forms alpha^q and the RoPE query of more than one batch of rows) and a head
 # dim spanning two staging steps
 ABSORB_SHAPES = [("dsv3", dict(rank=128)), ("dsv3", dict(rank=256, heads=64)),
-                 ("grouped", dict(rank=384)), ("dsv3", dict(head_dim=256, rank=64))]
+                 ("grouped", dict(rank=384)), ("dsv3", dict(head_dim=256, rank=64)),
+                 # from 16384 query rows (x 4 column blocks) the wave-tile kernel:
+                 # whole tiles, a ragged last tile with tiles spanning two query
+                 # tokens (100 heads), and four groups
+                 ("mtp", dict(batch=32)), ("mtp", dict(batch=41, heads=100)),
+                 ("grouped", dict(batch=130))]
 
 
 @pytest.mark.parametrize("name,kw", ABSORB_SHAPES)
@@ -202,8 +207,20 @@ def _verify_absorb(wl, inp, r):
         got = O.bf16_bits_to_f32(qt).astype(np.float64)
         assert row_err(got, exact["q_tilde"]) <= 2.0 ** -8 * 1.01
         assert np.mean(qt == ref["q_tilde"]) > 0.99
+        # The RoPE query word is x1 cos - x2 sin (and x2 cos + x1 sin) formed in
+        # float32 and rounded to bf16.  Its terms are as large as the row, so
+        # the float32 evaluation (the norm, the products, the sine and cosine
+        # of the angle rounded to float) is good to ~2^-21 of the row's
+        # largest entry, and a word near zero may be several bf16 steps off
+        # while still that close.  So each word is within one bf16 step of the
+        # oracle's word, or within 2^-20 of its row's largest entry of the
+        # exact float64 value.
         d = ulp_distance_bf16(qr, ref["qr_hat"])
-        assert d.max() <= 1
+        got_r = O.bf16_bits_to_f32(qr).astype(np.float64)
+        ex_r = exact["qr_hat"]
+        near = np.abs(got_r - ex_r) <= 2.0 ** -20 * np.max(np.abs(ex_r), axis=-1, keepdims=True)
+        assert np.all((d <= 1) | near), (int(d.max()), int(np.sum(d > 1)))
+        assert np.mean(d == 0) > 0.99
     else:
         assert row_err(qt, ref["q_tilde"]) < 1e-5
         assert row_err(qr, ref["qr_hat"]) < 1e-5
