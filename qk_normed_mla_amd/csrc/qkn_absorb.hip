@@ -415,8 +415,8 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
   }
 }
 
-// Wave-independent variant for d = 128, rank a multiple of 128 and d_R <= 128
-// (the workloads' shapes).  A block of 4 waves stages one 128-column block of
+// Wave-independent variant for d = 128, rank a multiple of 128 and d_R a
+// multiple of 32 up to 128 (the workloads' shapes).  A block of 4 waves stages one 128-column block of
 // W^K_g, times gamma_q gamma_k, as hi/lo bf16 words in LDS (69.6 KB, two
 // blocks per CU) and needs no barrier after that: each wave takes whole
 // 32-row tiles of q~ on its own.  The product is taken transposed,
@@ -424,13 +424,13 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
 // and the query rows the second one, loaded straight from HBM into the
 // operand layout (lane l: row l % 32, head-dim entries 16 s + 8 (l / 32) ..
 // + 7 of step s) and split in registers; the accumulator then holds, per lane,
-// runs of four consecutive q~ columns of one row, stored as 8-byte pieces.
-// The next tile's query loads go out step by step as the current tile's
-// operand words are formed.  alpha^q comes from the same registers (the two
-// lanes of a row hold its two halves); the RoPE query of a share of each
-// tile's rows (per column block) is formed one row per wave step with lanes
-// over the pairs (j, j + d_R / 2), its loads issued with the tile's first
-// products.
+// runs of four consecutive q~ columns of one row, and the two lanes of a row
+// trade halves to store 16-byte pieces.  The next tile's query loads go out
+// step by step as the current tile's operand words are formed.  alpha^q comes
+// from the same registers (the two lanes of a row hold its two halves); the
+// RoPE query of a share of each tile's rows (per column block) is formed four
+// rows per wave step, 16 lanes on a row, its loads issued with the tile's
+// first products.
 constexpr int WCB = 128;          // q~ columns per block
 constexpr int WLD = 128 + 8;      // LDS row of bf16 words (272 B: as SLD)
 constexpr int WAVE_LDS = 2 * WCB * WLD * 2;  // bytes: hi and lo words
@@ -504,50 +504,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();  // the only barrier: from here on the waves are independent
 
   // RoPE rows of each tile for this column block: rows rr_lo .. rr_hi - 1,
-  // lane j < d_R / 2 on the pair (j, j + d_R / 2)
+  // four per wave step.  Lane (rq, jj) = (lane / 16, lane % 16) takes row
+  // rq of the step and the pairs (j, j + d_R / 2), j = jj + 16 p, p < d_R / 32;
+  // the row's sum of squares is reduced over its 16 lanes.  A lane keeps the
+  // angles of the query token of its last row and forms them again when the
+  // token changes.
   const int share = cdiv(WROWS, (int)gridDim.y);
   const int rr_lo = min(WROWS, cb * share), rr_hi = min(WROWS, rr_lo + share);
   const int half = rope_dim / 2;
-  const bool jl = lane < half;
-  const int ja = jl ? lane : 0, jb = jl ? lane + half : 0;  // lanes past d_R / 2 read entry 0
-  const float ga = jl ? gamma_qr[ja] : 0.f, gb = jl ? gamma_qr[jb] : 0.f;
-  const double omega = (jl && theta != 0.f) ? rope_omega(lane, rope_dim, theta) : 0.0;
-  float cs = 1.f, sn = 0.f;
+  const int np_ = half / 16;  // pairs per lane, 1 .. 4 (d_R a multiple of 32, at most 128)
+  const int rq = lane >> 4, jj = lane & 15;
+  float ga[4], gb[4], cs[4], sn[4];
+  double om[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int j = jj + 16 * pp;
+    const bool ok = pp < np_;
+    ga[pp] = ok ? gamma_qr[j] : 0.f;
+    gb[pp] = ok ? gamma_qr[j + half] : 0.f;
+    om[pp] = (ok && theta != 0.f) ? rope_omega(j, rope_dim, theta) : 0.0;
+    cs[pp] = 1.f;
+    sn[pp] = 0.f;
+  }
   int angle_tok = -1;
-  float xa[RCH], xb[RCH];
+  constexpr int RST = RCH / 4;  // wave steps per chunk
+  float xa[RST][4], xb[RST][4];
   auto rope_load = [&](int n0, int c0) {
 #pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int lr = min(c0 + u, WROWS - 1);
-      const int gr = grow_of(n0 + lr);  // uniform
+    for (int u = 0; u < RST; ++u) {
+      const int lr = min(c0 + 4 * u + rq, WROWS - 1);
+      const int gr = lr < rr_hi ? grow_of(n0 + lr) : -1;
       const float* x = q_rope + (size_t)(gr >= 0 ? gr : 0) * rope_dim;
-      xa[u] = x[ja];
-      xb[u] = x[jb];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int j = pp < np_ ? jj + 16 * pp : 0;
+        xa[u][pp] = x[j];
+        xb[u][pp] = x[j + half];
+      }
     }
   };
   auto rope_finish = [&](int n0, int c0) {
 #pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int lr = c0 + u;
-      if (lr >= rr_hi) break;  // uniform
-      const int n = n0 + lr;
-      const int gr = grow_of(n);
-      if (gr < 0) break;  // uniform: rows past the end come last
-      const int tok = n / heads_per_group;
-      if (tok != angle_tok) {
-        cs = 1.f;
-        sn = 0.f;
-        if (jl && theta != 0.f) rope_cos_sin_at<false>(q_pos[tok], omega, &cs, &sn);
-        angle_tok = tok;
-      }
-      const float a = jl ? xa[u] : 0.f, b = jl ? xb[u] : 0.f;
-      const float sr = wave_sum(fmaf(a, a, b * b));
-      const float inv = 1.0f / sqrtf(sr / (float)rope_dim + eps);
-      if (jl) {
-        const float x1 = a * inv * ga, x2 = b * inv * gb;
+    for (int u = 0; u < RST; ++u) {
+      const int lr = c0 + 4 * u + rq;
+      const int gr = lr < rr_hi ? grow_of(n0 + lr) : -1;
+      float ss = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+        if (pp < np_) ss = fmaf(xa[u][pp], xa[u][pp], fmaf(xb[u][pp], xb[u][pp], ss));
+      // the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror
+      ss += dpp_partner<0xB1>(ss);
+      ss += dpp_partner<0x4E>(ss);
+      ss += dpp_partner<0x141>(ss);
+      ss += dpp_partner<0x140>(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)rope_dim + eps);
+      if (gr >= 0) {
+        const int tok = (n0 + lr) / heads_per_group;
+        if (tok != angle_tok) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+            if (pp < np_ && theta != 0.f) rope_cos_sin_at<false>(q_pos[tok], om[pp], &cs[pp], &sn[pp]);
+          angle_tok = tok;
+        }
         uint16_t* out = q_rope_out + (size_t)gr * rope_dim;
-        out[lane] = f32_to_bf16(x1 * cs - x2 * sn);
-        out[lane + half] = f32_to_bf16(x2 * cs + x1 * sn);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          if (pp < np_) {
+            const int j = jj + 16 * pp;
+            const float x1 = xa[u][pp] * inv * ga[pp], x2 = xb[u][pp] * inv * gb[pp];
+            out[j] = f32_to_bf16(x1 * cs[pp] - x2 * sn[pp]);
+            out[j + half] = f32_to_bf16(x2 * cs[pp] + x1 * sn[pp]);
+          }
+        }
       }
     }
   };
@@ -703,7 +731,7 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
     const int hpg = d.heads / d.groups;
     const int rows_per_group = d.batch * d.s_q * hpg;
     const int wave_cols = d.rank / WCB, n_tiles = cdiv(rows_per_group, WROWS);
-    if (d.head_dim == 128 && d.rank % WCB == 0 && d.rope_dim <= 128 &&
+    if (d.head_dim == 128 && d.rank % WCB == 0 && d.rope_dim % 32 == 0 && d.rope_dim <= 128 &&
         (long)rows_per_group * wave_cols * d.groups >= 65536) {
       // Enough 32-row tiles for every wave of two blocks per CU to take
       // about two (from 16384 query rows at r = 512); below that the 8-wave
