@@ -21,7 +21,9 @@ grouped, long); ``sparse`` the selected-token decode (2048 listed tokens per
 query out of 16384, its listed rows as the algorithmic bytes); ``prefill`` the
 chunked prefill on the explicit path (a 512-token chunk over 8192 tokens);
 ``qknorm_sweep`` the cost of the inverse-RMS factors over a
-batch-1 context sweep from 4k to 256k tokens; ``cpu_baseline`` the float64 CPU
+batch-1 context sweep from 4k to 256k tokens; ``hbm_read_stream`` the HBM read
+rate a plain read-only stream reaches on this GPU (each workload's decode rate
+is also given as a fraction of it); ``cpu_baseline`` the float64 CPU
 oracle timed on a bounded sample on the host's cores (and on one core).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp]
@@ -50,6 +52,40 @@ MIN_ROTATION_BYTES = 512 << 20
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def hbm_read_stream(Q, torch, timer, gib=2, launches=4):
+    """The achievable HBM read rate on this GPU: qkn_mla_stream_read (every
+    16-byte word of a 2 GiB buffer read once, non-temporal, as the decode reads
+    the cache) captured `launches` times in a graph and timed like the
+    kernels.  Also checks the XOR it returns against the buffer's."""
+    import ctypes
+    n = gib << 30
+    buf = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    buf.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda"))
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib = Q.library()
+
+    def call(_k=0):
+        st = lib.qkn_mla_stream_read(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"qkn_mla_stream_read failed: {st}")
+
+    call()
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32)))
+    got = int(sink.cpu().numpy().view(np.uint32)[0])
+    if got != want:
+        raise RuntimeError(f"qkn_mla_stream_read: XOR {got:#x}, expected {want:#x}")
+    g = timer.capture(call, launches)
+    timer.warm(g)
+    ms = timer.timed([g], reps=7)[0] / launches
+    gbs = n / (ms * 1e-3) / 1e9
+    log(f"HBM read stream: {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f})")
+    del buf
+    return {"kernel": "qkn_mla_stream_read", "bytes_per_launch": n, "gbs": round(gbs, 1),
+            "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def split_len(T, P):
@@ -904,6 +940,15 @@ def main():
         log("batch-1 QK-norm overhead sweep")
         sweep = qknorm_sweep(Q, W, torch, timer)
 
+    stream = None
+    if not args.only:
+        stream = hbm_read_stream(Q, torch, timer)
+        # each HBM-bound figure also against the measured read rate
+        for w in [head["summary"]] + others:
+            if w.get("decode_kernel_us"):
+                w["decode_frac_of_stream"] = round(
+                    w["cache_bytes"] / (w["decode_kernel_us"] * 1e-6) / 1e9 / stream["gbs"], 4)
+
     hs = head["summary"]
     roof = roofline_of(head["flops"], head["nbytes"], head["dec_ms"] * 1e-3, load_traffic(wl.name))
     cpu = None
@@ -941,6 +986,7 @@ def main():
         "prefill": prefill,
         "gqa_path": gqa or None,
         "qknorm_sweep": sweep,
+        "hbm_read_stream": stream,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -49,7 +49,7 @@ extern "C" {
 #define QKN_API
 #endif
 
-#define QKN_MLA_ABI_VERSION 8
+#define QKN_MLA_ABI_VERSION 9
 #define QKN_MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -515,6 +515,21 @@ QKN_API int qkn_mla_gqa_attend(const qkn_mla_dims* dims, const void* q_hat,
                        const int32_t* block_table, const int32_t* seq_lens,
                        int32_t num_splits, void* workspace, size_t workspace_bytes,
                        float* o, float* lse, int32_t* err_flag, void* stream);
+
+/*
+ * qkn_mla_stream_read -- a plain read-only stream over device memory (not a
+ *   step of the method): the achievable HBM read rate on this GPU, against
+ *   which the cache-reading kernels are measured besides the published peak.
+ *   Every 16-byte word of src is read once with non-temporal loads
+ *   (consecutive lanes on consecutive words, four loads in flight per
+ *   thread), and the XOR of all the 32-bit words read is XORed into *sink
+ *   (so the caller sets *sink beforehand; the result does not depend on
+ *   timing).
+ *   src (device) 16-byte aligned, bytes a positive multiple of 16;
+ *   sink (device) one 4-byte aligned uint32.  Nothing is written but *sink.
+ *   QKN_ERR_INVALID_ARG / QKN_ERR_ALIGNMENT before any launch.
+ */
+QKN_API int qkn_mla_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

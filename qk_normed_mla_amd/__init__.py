@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqknmla.so")
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 QKN_OK = 0
 QKN_ERR_SCRATCH = -5
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -122,6 +122,8 @@ def library() -> ctypes.CDLL:
         lib.qkn_mla_gqa_attend.restype = ctypes.c_int
         lib.qkn_mla_gqa_attend.argtypes = [D, P, P, P, P, P, _c_int32, P, ctypes.c_size_t, P, P, P,
                                            P]
+        lib.qkn_mla_stream_read.restype = ctypes.c_int
+        lib.qkn_mla_stream_read.argtypes = [P, ctypes.c_uint64, P, P]
         if lib.qkn_mla_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {lib.qkn_mla_abi_version()}, "
                                f"this binding needs {ABI_VERSION}: rebuild it")
@@ -138,6 +140,7 @@ EXPORTED_SYMBOLS = (
     "qkn_mla_combine", "qkn_mla_combine_project",
     "qkn_mla_prefill_query", "qkn_mla_prefill_expand", "qkn_mla_prefill_attend",
     "qkn_mla_gqa_append", "qkn_mla_gqa_workspace_bytes", "qkn_mla_gqa_attend",
+    "qkn_mla_stream_read",
 )
 
 

@@ -388,6 +388,13 @@ int qkn_mla_combine_project(const qkn_mla_dims* dims, int32_t num_splits, const 
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int qkn_mla_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return QKN_ERR_INVALID_ARG;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return QKN_ERR_ALIGNMENT;
+  return hip_status(qkn::launch_stream_read(src, static_cast<size_t>(bytes), sink,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t qkn_mla_gqa_workspace_bytes(const qkn_mla_dims* dims, int32_t num_splits) {
   if (check_dims(dims) != QKN_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
   return gqa_workspace_layout(*dims, num_splits).total;

@@ -214,6 +214,7 @@ hipError_t launch_gqa_attend(const qkn_mla_dims& d, const void* q_hat, const voi
                              int num_splits, void* o_part, float* lse_part, float* o, float* lse,
                              int32_t* err_flag, hipStream_t s);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_combine(const qkn_mla_dims& d, int num_splits, const void* o_part,
                           const float* lse_part, float* o_lat, float* lse, hipStream_t s);
 // The same merge for n_rows rows of row_len (a multiple of 8) entries, the

@@ -33,7 +33,7 @@ def good_dims(**kw):
 def test_library_exports_header_symbols():
     lib = Q.library()
     syms = declared_symbols()
-    assert len(syms) == 20, syms
+    assert len(syms) == 21, syms
     assert set(syms) == set(Q.EXPORTED_SYMBOLS)
     for s in syms:
         assert hasattr(lib, s), f"{s} not exported"
@@ -47,7 +47,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings():
     lib = Q.library()
-    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 8
+    assert lib.qkn_mla_abi_version() == Q.ABI_VERSION == 9
     for st in (0, -1, -2, -3, -4, -5):
         assert len(Q.status_string(st)) >= 2
     assert Q.status_string(123) == "unknown status"
@@ -312,3 +312,14 @@ def test_gqa_rejections():
     assert attend(3, P(0x1010), ws) == -3                    # not 256-byte aligned
     assert attend(1, None, 0, q=None) == -1
     assert attend(1, None, 0, q=P(0x1004)) == -3
+
+
+def test_stream_read_rejections():
+    lib = Q.library()
+    P = ctypes.c_void_p
+    assert lib.qkn_mla_stream_read(None, 64, P(0x1000), None) == -1        # no source
+    assert lib.qkn_mla_stream_read(P(0x1000), 64, None, None) == -1        # no sink
+    assert lib.qkn_mla_stream_read(P(0x1000), 0, P(0x1000), None) == -1    # nothing to read
+    assert lib.qkn_mla_stream_read(P(0x1000), 40, P(0x1000), None) == -1   # not whole 16-byte words
+    assert lib.qkn_mla_stream_read(P(0x1008), 64, P(0x1000), None) == -3   # misaligned source
+    assert lib.qkn_mla_stream_read(P(0x1000), 64, P(0x1002), None) == -3   # misaligned sink
