@@ -174,7 +174,10 @@ ABSORB_SHAPES = [("dsv3", dict(rank=128)), ("dsv3", dict(rank=256, heads=64)),
                  # whole tiles, a ragged last tile with tiles spanning two query
                  # tokens (100 heads), and four groups
                  ("mtp", dict(batch=32)), ("mtp", dict(batch=41, heads=100)),
-                 ("grouped", dict(batch=130))]
+                 ("grouped", dict(batch=130)),
+                 # every RoPE width it takes (1 to 4 pairs per lane), and no rotation
+                 ("mtp", dict(batch=32, rope_dim=32)), ("mtp", dict(batch=32, rope_dim=96)),
+                 ("mtp", dict(batch=32, rope_dim=128)), ("mtp", dict(batch=32, rope_theta=0.0))]
 
 
 @pytest.mark.parametrize("name,kw", ABSORB_SHAPES)
