@@ -61,8 +61,7 @@ def hbm_read_stream(Q, torch, timer, gib=2, launches=4):
     kernels.  Also checks the XOR it returns against the buffer's."""
     import ctypes
     n = gib << 30
-    buf = torch.empty(n // 4, dtype=torch.int32, device="cuda")
-    buf.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda"))
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     lib = Q.library()
 
