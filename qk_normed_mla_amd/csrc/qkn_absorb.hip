@@ -416,10 +416,10 @@ __global__ __launch_bounds__(64 * SW) void absorb_split(
 }
 
 // Wave-independent variant for d = 128, rank a multiple of 128 and d_R a
-// multiple of 32 up to 128 (the workloads' shapes).  A block of 4 waves stages one 128-column block of
-// W^K_g, times gamma_q gamma_k, as hi/lo bf16 words in LDS (69.6 KB, two
-// blocks per CU) and needs no barrier after that: each wave takes whole
-// 32-row tiles of q~ on its own.  The product is taken transposed,
+// multiple of 32 up to 128 (the workloads' shapes).  A block of 8 waves (one
+// block per CU) stages one 128-column block of W^K_g, times gamma_q gamma_k,
+// as hi/lo bf16 words in LDS (69.6 KB) and needs no barrier after that: each
+// wave takes whole 32-row tiles of q~ on its own.  The product is taken transposed,
 // q~^T = W . q^T, so that the W rows are the first operand (read from LDS)
 // and the query rows the second one, loaded straight from HBM into the
 // operand layout (lane l: row l % 32, head-dim entries 16 s + 8 (l / 32) ..
@@ -436,8 +436,9 @@ constexpr int WLD = 128 + 8;      // LDS row of bf16 words (272 B: as SLD)
 constexpr int WAVE_LDS = 2 * WCB * WLD * 2;  // bytes: hi and lo words
 constexpr int WROWS = 32;         // query rows per wave tile
 constexpr int RCH = 8;            // RoPE rows per chunk
+constexpr int WW = 8;             // waves per block (one block per CU)
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void absorb_wave(
+__global__ __launch_bounds__(64 * WW) __attribute__((amdgpu_waves_per_eu(2, 2))) void absorb_wave(
     const float* __restrict__ q, const float* __restrict__ q_rope,
     const int32_t* __restrict__ q_pos, const float* __restrict__ w_k,
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
@@ -454,8 +455,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int r = lane & 31, h = lane >> 5;
   const int m0 = cb * WCB;
   const int n_tiles = cdiv(rows_per_group, WROWS);
-  const int t_step = gridDim.x * 4;
-  const int t0 = blockIdx.x * 4 + wave;
+  const int t_step = gridDim.x * WW;
+  const int t0 = blockIdx.x * WW + wave;
 
   auto grow_of = [&](int n) {  // global query row of group row n, -1 past the end
     const int bi = n / heads_per_group, hl = n - bi * heads_per_group;
@@ -483,12 +484,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int k4 = 4 * (tid & 31);
     const float4 f = make_float4(gamma_q[k4] * gk[k4], gamma_q[k4 + 1] * gk[k4 + 1],
                                  gamma_q[k4 + 2] * gk[k4 + 2], gamma_q[k4 + 3] * gk[k4 + 3]);
-    float4 wv[16];
+    constexpr int NW = WCB * D / 4 / (64 * WW);  // float4 of the block's W rows per thread
+    float4 wv[NW];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)((tid >> 5) + 8 * u) * D + k4);
+    for (int u = 0; u < NW; ++u)
+      wv[u] = *reinterpret_cast<const float4*>(wg + (size_t)((tid >> 5) + 2 * WW * u) * D + k4);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < NW; ++u) {
       float4 v = wv[u];
       v.x *= f.x;
       v.y *= f.y;
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       v.w *= f.w;
       bf16x4 hi, lo;
       split4(v, hi, lo);
-      const int o = ((tid >> 5) + 8 * u) * WLD + k4;
+      const int o = ((tid >> 5) + 2 * WW * u) * WLD + k4;
       *reinterpret_cast<bf16x4*>(&Wh[o]) = hi;
       *reinterpret_cast<bf16x4*>(&Wl[o]) = lo;
     }
@@ -733,16 +735,16 @@ hipError_t launch_absorb_query(const qkn_mla_dims& d, const float* q, const floa
     const int wave_cols = d.rank / WCB, n_tiles = cdiv(rows_per_group, WROWS);
     if (d.head_dim == 128 && d.rank % WCB == 0 && d.rope_dim % 32 == 0 && d.rope_dim <= 128 &&
         (long)rows_per_group * wave_cols * d.groups >= 65536) {
-      // Enough 32-row tiles for every wave of two blocks per CU to take
+      // Enough 32-row tiles for every wave (one 8-wave block per CU) to take
       // about two (from 16384 query rows at r = 512); below that the 8-wave
       // 64-row tiles keep more waves busy.  The column blocks of one row range
       // sit on one XCD (block ids that differ by a multiple of 8) and share
       // its L2.
-      int nb = std::max(1, std::min(cdiv(n_tiles, 4), 512 / (wave_cols * d.groups)));
+      int nb = std::max(1, std::min(cdiv(n_tiles, WW), (2048 / WW) / (wave_cols * d.groups)));
       if (nb >= 8) nb -= nb % 8;
       const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&absorb_wave), WAVE_LDS);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(absorb_wave, dim3(nb, wave_cols, d.groups), dim3(256), WAVE_LDS, s, q,
+      hipLaunchKernelGGL(absorb_wave, dim3(nb, wave_cols, d.groups), dim3(64 * WW), WAVE_LDS, s, q,
                          q_rope, q_pos, w_k, gamma_q, gamma_k, gamma_qr,
                          static_cast<uint16_t*>(q_tilde), alpha_q,
                          static_cast<uint16_t*>(q_rope_normed), rows_per_group, d.heads, hpg,
