@@ -177,7 +177,10 @@ ABSORB_SHAPES = [("dsv3", dict(rank=128)), ("dsv3", dict(rank=256, heads=64)),
                  ("grouped", dict(batch=130)),
                  # every RoPE width it takes (1 to 4 pairs per lane), and no rotation
                  ("mtp", dict(batch=32, rope_dim=32)), ("mtp", dict(batch=32, rope_dim=96)),
-                 ("mtp", dict(batch=32, rope_dim=128)), ("mtp", dict(batch=32, rope_theta=0.0))]
+                 ("mtp", dict(batch=32, rope_dim=128)), ("mtp", dict(batch=32, rope_theta=0.0)),
+                 # two column blocks (16 RoPE rows each, in two chunks) and G = 8 (16 heads
+                 # per group: two query tokens per tile)
+                 ("grouped", dict(batch=260, groups=8, rank=256))]
 
 
 @pytest.mark.parametrize("name,kw", ABSORB_SHAPES)
